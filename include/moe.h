@@ -1,0 +1,162 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) mixture-of-experts layer library.
+ *
+ * One MoE layer shaped like Kimi K3.1 (top-16 of 896 routed experts plus 2
+ * always-on shared experts, MXFP4 SwiGLU experts) and the Q8_0 multi-row
+ * spine matmul.  Source: "Run Kimi 3.1 locally on one GPU" (argonautlabs.ai)
+ * and its sections named per function below.
+ *
+ * Conventions (all functions):
+ *  - Every array pointer is DEVICE memory allocated and owned by the caller.
+ *    The library never allocates, frees or retains caller memory.  Structs
+ *    passed by pointer (moe_experts) are HOST memory, read during the call.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is
+ *    enqueued on it; no function synchronises the device or the stream, and
+ *    each returns as soon as its kernels are enqueued.
+ *  - Return value: MOE_OK (0) or a negative moe_status.  Argument errors are
+ *    detected on the host before anything is enqueued; then nothing is
+ *    enqueued and no output is touched.
+ *  - Arrays are row-major and densely packed.  Floating outputs are fp32.
+ *  - M = 0 rows is valid and enqueues nothing.
+ *  - Rows of one call never influence each other's results: the result of a
+ *    row is bit-identical whether it is alone (M = 1) or inside a block of
+ *    any M, for every function here ("A drafter that leaves the answer
+ *    unchanged": a block's rows run the same arithmetic as plain steps).
+ *
+ * MXFP4 storage (OCP MX v1.0 elements; the byte layout is this library's
+ * data contract, the pages give only the format name and the 17,547,264-byte
+ * expert size, "One GPU, three storage tiers"):
+ *  - a matrix [rows x K] (K a multiple of 32) is a codes plane of rows*K/2
+ *    bytes, element 2i in the LOW nibble of byte i and element 2i+1 in the
+ *    high nibble (E2M1: sign, 2-bit exponent with bias 1, 1-bit mantissa),
+ *    followed by a scales plane of rows*K/32 E8M0 bytes (2^(b-127)), scale j
+ *    of a row covering its elements 32j..32j+31;
+ *  - an expert record is W_gate [f x d], W_up [f x d], W_down [d x f], each
+ *    as codes plane then scales plane, back to back: 3*d*f*17/32 bytes
+ *    (17,547,264 at d=7168, f=1536);
+ *  - a layer is n_routed + n_shared records at a fixed stride; shared expert
+ *    s has id n_routed + s.
+ * E8M0 byte 255 (NaN) and bytes that would make a weight overflow fp32 are
+ * outside the supported input range.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,       /* bad argument: NULL pointer, negative size, k > E, d % 32, ... */
+  MOE_EUNSUPPORTED = -2, /* valid but outside what this build implements (see per function) */
+  MOE_EHIP = -3          /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* One layer's experts, resident in device memory. */
+typedef struct {
+  const uint8_t *base; /* device: (n_routed + n_shared) * stride bytes, 16-byte aligned */
+  int64_t stride;      /* bytes between records, >= 3*d*f*17/32, multiple of 16 */
+  int32_t d;           /* model width (reduction dim of gate/up), multiple of 32 */
+  int32_t f;           /* expert FFN width, multiple of 32 */
+  int32_t n_routed;    /* E */
+  int32_t n_shared;    /* S, applied to every row with weight 1 */
+} moe_experts;
+
+/* Router ("Read the experts the router needs": the router picks 16 of 896
+ * experts per token).  The router function is softmax over the E logits,
+ * the k largest are kept and their probabilities renormalised to sum to 1.
+ *
+ *   x         [M x d] fp32 or bf16 (x_dtype), the layer input rows.
+ *   w_router  [E x d] fp32.  If non-NULL, logits[m,e] = sum_c w_router[e,c]*x[m,c]
+ *             is computed and written to `logits`.  If NULL, `logits` is an
+ *             INPUT (x is then not read and may be NULL).
+ *   logits    [M x E] fp32, output or input as above.
+ *   topk_ids  [M x k] int32 out: expert ids in rank order (larger logit first,
+ *             equal logits to the lower index, NaN ranks below every number).
+ *   topk_w    [M x k] fp32 out: w[m,j] = exp(l_j - l_0) / sum_{i<k} exp(l_i - l_0)
+ *             with l_0 the top logit (the renormalised softmax; summed in rank
+ *             order).  Undefined (NaN) when the top logit is not finite.
+ * Requires 1 <= k <= min(E, 64), E <= 4096, d % 32 == 0 (when w_router != NULL).
+ */
+int moe_route(const void *x, moe_dtype x_dtype, const float *w_router, float *logits, int32_t M, int32_t d,
+              int32_t E, int32_t k, int32_t *topk_ids, float *topk_w, void *stream);
+
+/* Bucketing: group the M*(k+S) slots by expert so each expert's rows are
+ * found together and its weights are read once for all of them ("A drafter
+ * that leaves the answer unchanged": a block reads each expert once for all
+ * its rows).  Slot t = m*(k+S)+j is routed expert topk_ids[m,j] for j < k and
+ * shared expert E+(j-k) for j >= k.
+ *
+ *   offsets   [E+S+1] int32 out: exclusive prefix sum of per-expert slot
+ *             counts; offsets[E+S] = M*(k+S).
+ *   perm      [M*(k+S)] int32 out: slots sorted by (expert, slot), i.e. expert
+ *             e's slots in ascending order at perm[offsets[e] .. offsets[e+1]).
+ *   active    [E+S] int32 out: the experts with at least one slot, ascending,
+ *             in active[0 .. *n_active).  Entries beyond are unspecified.
+ *   n_active  [1] int32 out.
+ *   dev_error [1] int32 out: set to 0, or to 1 if some topk_ids entry is
+ *             outside [0,E) or a row repeats an expert.  Such slots are
+ *             dropped; every write stays in bounds and the other outputs
+ *             are unspecified.  Read after synchronising the stream.
+ * Requires 1 <= k, E + S <= 4096.  All outputs are exact (integer).
+ */
+int moe_bucket(const int32_t *topk_ids, int32_t M, int32_t k, int32_t E, int32_t n_shared, int32_t *offsets,
+               int32_t *perm, int32_t *active, int32_t *n_active, int32_t *dev_error, void *stream);
+
+/* Expert FFN over the bucketed slots ("A drafter that leaves the answer
+ * unchanged": each expert's weights are read once for all rows of the block;
+ * experts are SwiGLU: y = W_down (silu(W_gate x) * (W_up x)), silu(z) = z/(1+e^-z)).
+ *
+ *   x         [M x d] fp32 or bf16 (x_dtype).
+ *   M, k      as given to moe_bucket; S = W->n_shared.
+ *   W         host pointer to the layer's expert table (device records).
+ *   offsets, perm, active, n_active: moe_bucket's outputs for these M, k.
+ *   y_slots   [M*(k+S) x d] fp32 out: row t holds slot t's expert output for
+ *             row m = t/(k+S).  Every slot row is written.
+ *   workspace device scratch of at least moe_workspace_bytes(M, k, W) bytes,
+ *             owned by the caller; contents on entry do not matter.
+ * The result of a slot does not depend on M, on the other rows, or on the
+ * order of the active list.  Requires W->d % 128 == 0 or d % 32 == 0 (any
+ * multiple of 32 works), W->f % 32 == 0.
+ */
+int moe_expert_ffn_mxfp4(const void *x, moe_dtype x_dtype, int32_t M, int32_t k, const moe_experts *W,
+                         const int32_t *offsets, const int32_t *perm, const int32_t *active,
+                         const int32_t *n_active, float *y_slots, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/* Bytes of workspace moe_expert_ffn_mxfp4 needs for M rows (host-only query;
+ * returns 0 for invalid arguments). */
+size_t moe_workspace_bytes(int32_t M, int32_t k, const moe_experts *W);
+
+/* Weighted combine: out[m,r] = sum_{j<k} topk_w[m,j] * y_slots[m*(k+S)+j, r]
+ *                              + sum_{s<S} y_slots[m*(k+S)+k+s, r],
+ * accumulated in fp32 in slot order (routed experts by the router's weights,
+ * shared experts with weight 1).
+ *   y_slots [M*(k+S) x d] fp32, topk_w [M x k] fp32, out [M x d] fp32.
+ * Requires k >= 1, S >= 0, d % 4 == 0. */
+int moe_combine(const float *y_slots, const float *topk_w, int32_t M, int32_t k, int32_t n_shared, int32_t d,
+                float *out, void *stream);
+
+/* Q8_0 spine matmul ("A drafter that leaves the answer unchanged": the
+ * spine's matrix multiplies load each weight once for up to eight rows;
+ * "One GPU, three storage tiers": the spine's matrices are Q8_0):
+ *   Y[m,n] = sum_c X[m,c] * Wq[n,c] * Ws[n, c/32]
+ *   X  [M x K] fp32;  Wq [N x K] int8;  Ws [N x K/32] fp16 bit patterns;
+ *   Y  [M x N] fp32 out.
+ * Requires 1 <= M <= 8 (M = 0 enqueues nothing), K % 32 == 0, N >= 1. */
+int q8_0_matmul(const float *X, int32_t M, int32_t K, const int8_t *Wq, const uint16_t *Ws, int32_t N, float *Y,
+                void *stream);
+
+/* Human-readable name of a status code (static string). */
+const char *moe_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

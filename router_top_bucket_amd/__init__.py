@@ -1,0 +1,250 @@
+"""Python binding of libmoe, the MI355X (gfx950) mixture-of-experts layer library.
+
+Thin ctypes marshalling over the C ABI declared in ``include/moe.h``: every
+function takes torch tensors that already live on the GPU, checks their shape
+and dtype, and passes raw device pointers plus the current HIP stream.  All of
+the computation runs in the library's HIP kernels; torch only owns memory and
+streams.  There is no fallback: if ``libmoe.so`` is missing or fails to load,
+importing this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+from .build import LIB_PATH
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP = 0, -1, -2, -3
+MOE_F32, MOE_BF16 = 0, 1
+
+# names exported by include/moe.h
+ABI_FUNCTIONS = ("moe_route", "moe_bucket", "moe_expert_ffn_mxfp4", "moe_workspace_bytes", "moe_combine",
+                 "q8_0_matmul", "moe_status_str")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, rc: int):
+        super().__init__(f"{fn} failed: {_lib.moe_status_str(rc).decode()} (rc={rc})")
+        self.rc = rc
+
+
+class _Experts(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("stride", ctypes.c_int64), ("d", ctypes.c_int32),
+                ("f", ctypes.c_int32), ("n_routed", ctypes.c_int32), ("n_shared", ctypes.c_int32)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run router_top_bucket_amd/build.py (or __graft_entry__.build())")
+    # torch is imported first, so the HIP runtime torch uses is the one this
+    # library binds to (same soname), and torch's streams are valid here
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    EP = ctypes.POINTER(_Experts)
+    sigs = {
+        "moe_route": (ctypes.c_int, [P, ctypes.c_int, P, P, i32, i32, i32, i32, P, P, P]),
+        "moe_bucket": (ctypes.c_int, [P, i32, i32, i32, i32, P, P, P, P, P, P]),
+        "moe_expert_ffn_mxfp4": (ctypes.c_int, [P, ctypes.c_int, i32, i32, EP, P, P, P, P, P, P, sz, P]),
+        "moe_workspace_bytes": (sz, [i32, i32, EP]),
+        "moe_combine": (ctypes.c_int, [P, P, i32, i32, i32, i32, P, P]),
+        "q8_0_matmul": (ctypes.c_int, [P, i32, i32, P, P, i32, P, P]),
+        "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def raw_library() -> ctypes.CDLL:
+    return _lib
+
+
+# ----------------------------------------------------------------------------- helpers
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _check(fn: str, rc: int):
+    if rc != MOE_OK:
+        raise MoeError(fn, rc)
+
+
+def _x_dtype(x: torch.Tensor) -> int:
+    if x.dtype == torch.float32:
+        return MOE_F32
+    if x.dtype in (torch.bfloat16, torch.uint16, torch.int16):
+        return MOE_BF16
+    raise ValueError(f"x must be float32 or bfloat16 (got {x.dtype})")
+
+
+@dataclass
+class Experts:
+    """One layer's expert records in device memory (see include/moe.h)."""
+    base: torch.Tensor  # uint8, (n_routed + n_shared) * stride bytes
+    stride: int
+    d: int
+    f: int
+    n_routed: int
+    n_shared: int
+
+    def c_struct(self) -> _Experts:
+        if self.base.dtype != torch.uint8:
+            raise ValueError("expert base must be a uint8 tensor")
+        if self.base.numel() < (self.n_routed + self.n_shared) * self.stride:
+            raise ValueError("expert base tensor is too small")
+        return _Experts(_ptr(self.base), self.stride, self.d, self.f, self.n_routed, self.n_shared)
+
+
+# ----------------------------------------------------------------------------- ABI
+def moe_route(x, w_router, logits, k, topk_ids, topk_w, stream=None):
+    """Router logits (when w_router is given) then top-k ids and renormalised
+    softmax weights.  With w_router None, ``logits`` [M x E] is the input."""
+    M, E = logits.shape
+    if logits.dtype != torch.float32 or topk_ids.dtype != torch.int32 or topk_w.dtype != torch.float32:
+        raise ValueError("logits/topk_w must be float32 and topk_ids int32")
+    if tuple(topk_ids.shape) != (M, k) or tuple(topk_w.shape) != (M, k):
+        raise ValueError("topk outputs must be [M x k]")
+    if w_router is not None:
+        if w_router.dtype != torch.float32 or w_router.shape[0] != E or x.shape != (M, w_router.shape[1]):
+            raise ValueError("w_router must be float32 [E x d] and x [M x d]")
+        d, xdt = w_router.shape[1], _x_dtype(x)
+    else:
+        d, xdt = 0, (_x_dtype(x) if x is not None else MOE_F32)
+    rc = _lib.moe_route(_ptr(x) if w_router is not None else None, xdt, _ptr(w_router), _ptr(logits), M, d, E, k,
+                        _ptr(topk_ids), _ptr(topk_w), _stream(stream))
+    _check("moe_route", rc)
+
+
+def moe_bucket(topk_ids, E, n_shared, offsets, perm, active, n_active, dev_error, stream=None):
+    """Stable grouping of the M*(k+S) slots by expert."""
+    M, k = topk_ids.shape
+    for t in (topk_ids, offsets, perm, active, n_active, dev_error):
+        if t.dtype != torch.int32:
+            raise ValueError("bucket tensors are int32")
+    if offsets.numel() < E + n_shared + 1 or perm.numel() < M * (k + n_shared) or active.numel() < E + n_shared:
+        raise ValueError("bucket outputs too small")
+    rc = _lib.moe_bucket(_ptr(topk_ids), M, k, E, n_shared, _ptr(offsets), _ptr(perm), _ptr(active), _ptr(n_active),
+                         _ptr(dev_error), _stream(stream))
+    _check("moe_bucket", rc)
+
+
+def moe_workspace_bytes(M, k, experts: Experts) -> int:
+    s = experts.c_struct()
+    return int(_lib.moe_workspace_bytes(M, k, ctypes.byref(s)))
+
+
+def moe_expert_ffn_mxfp4(x, k, experts: Experts, offsets, perm, active, n_active, y_slots, workspace, stream=None):
+    """Every slot's SwiGLU expert output, each expert's weights read once."""
+    M = x.shape[0]
+    S = experts.n_shared
+    if x.shape[1] != experts.d:
+        raise ValueError("x must be [M x d]")
+    if y_slots.dtype != torch.float32 or tuple(y_slots.shape) != (M * (k + S), experts.d):
+        raise ValueError("y_slots must be float32 [M*(k+S) x d]")
+    if workspace.dtype != torch.uint8:
+        raise ValueError("workspace must be a uint8 tensor")
+    s = experts.c_struct()
+    rc = _lib.moe_expert_ffn_mxfp4(_ptr(x), _x_dtype(x), M, k, ctypes.byref(s), _ptr(offsets), _ptr(perm),
+                                   _ptr(active), _ptr(n_active), _ptr(y_slots), _ptr(workspace), workspace.numel(),
+                                   _stream(stream))
+    _check("moe_expert_ffn_mxfp4", rc)
+
+
+def moe_combine(y_slots, topk_w, k, n_shared, out, stream=None):
+    """out[m] = sum_j w[m,j] y[m,j] + sum_s y_shared[m,s], fp32 in slot order."""
+    M, d = out.shape
+    if tuple(topk_w.shape) != (M, k) or tuple(y_slots.shape) != (M * (k + n_shared), d):
+        raise ValueError("combine shapes")
+    rc = _lib.moe_combine(_ptr(y_slots), _ptr(topk_w), M, k, n_shared, d, _ptr(out), _stream(stream))
+    _check("moe_combine", rc)
+
+
+def q8_0_matmul(X, Wq, Ws, Y, stream=None):
+    """Y[M x N] = X[M x K] . W^T with W in Q8_0 (int8 [N x K], fp16 bits [N x K/32])."""
+    M, K = X.shape
+    N = Wq.shape[0]
+    if X.dtype != torch.float32 or Wq.dtype != torch.int8 or Ws.dtype not in (torch.int16, torch.uint16,
+                                                                                torch.float16):
+        raise ValueError("q8_0 dtypes: X float32, Wq int8, Ws fp16 bits")
+    if tuple(Wq.shape) != (N, K) or tuple(Ws.shape) != (N, K // 32) or tuple(Y.shape) != (M, N):
+        raise ValueError("q8_0 shapes")
+    rc = _lib.q8_0_matmul(_ptr(X), M, K, _ptr(Wq), _ptr(Ws), N, _ptr(Y), _stream(stream))
+    _check("q8_0_matmul", rc)
+
+
+# ----------------------------------------------------------------------------- one layer
+class MoELayer:
+    """Buffers for one MoE layer pass over up to ``max_rows`` rows, and the pass
+    itself as the four ABI calls in order (route, bucket, expert FFN, combine)."""
+
+    def __init__(self, experts: Experts, k: int, max_rows: int, w_router: torch.Tensor | None = None,
+                 device="cuda"):
+        self.experts, self.k, self.max_rows, self.w_router = experts, k, max_rows, w_router
+        E, S, d = experts.n_routed, experts.n_shared, experts.d
+        T = max_rows * (k + S)
+        i32 = dict(dtype=torch.int32, device=device)
+        f32 = dict(dtype=torch.float32, device=device)
+        self.logits = torch.empty((max_rows, E), **f32)
+        self.topk_ids = torch.empty((max_rows, k), **i32)
+        self.topk_w = torch.empty((max_rows, k), **f32)
+        self.offsets = torch.empty(E + S + 1, **i32)
+        self.perm = torch.empty(max(T, 1), **i32)
+        self.active = torch.empty(E + S, **i32)
+        self.n_active = torch.empty(1, **i32)
+        self.dev_error = torch.empty(1, **i32)
+        self.y_slots = torch.empty((T, d), **f32)
+        self.out = torch.empty((max_rows, d), **f32)
+        self.workspace = torch.empty(max(moe_workspace_bytes(max_rows, k, experts), 256), dtype=torch.uint8,
+                                     device=device)
+
+    def views(self, M: int):
+        S = self.experts.n_shared
+        return dict(logits=self.logits[:M], topk_ids=self.topk_ids[:M], topk_w=self.topk_w[:M],
+                    offsets=self.offsets, perm=self.perm[:M * (self.k + S)], active=self.active,
+                    n_active=self.n_active, dev_error=self.dev_error, y_slots=self.y_slots[:M * (self.k + S)],
+                    out=self.out[:M])
+
+    def forward(self, x: torch.Tensor, logits: torch.Tensor | None = None, stream=None):
+        """One layer pass over x [M x d].  With ``logits`` given the router
+        GEMV is skipped and those logits are routed."""
+        M = x.shape[0]
+        if M > self.max_rows:
+            raise ValueError("more rows than the layer buffers hold")
+        v = self.views(M)
+        E, S = self.experts.n_routed, self.experts.n_shared
+        if logits is not None:
+            v["logits"] = logits
+            moe_route(None, None, logits, self.k, v["topk_ids"], v["topk_w"], stream)
+        else:
+            moe_route(x, self.w_router, v["logits"], self.k, v["topk_ids"], v["topk_w"], stream)
+        moe_bucket(v["topk_ids"], E, S, v["offsets"], v["perm"], v["active"], v["n_active"], v["dev_error"], stream)
+        moe_expert_ffn_mxfp4(x, self.k, self.experts, v["offsets"], v["perm"], v["active"], v["n_active"],
+                             v["y_slots"], self.workspace, stream)
+        moe_combine(v["y_slots"], v["topk_w"], self.k, S, v["out"], stream)
+        return v

@@ -1,0 +1,163 @@
+// Bucketing: stable counting sort of the M*(k+S) slots by expert, so each
+// expert's rows are found together and its weights are read once for all of
+// them ("A drafter that leaves the answer unchanged", "Run Kimi 3.1 locally on
+// one GPU").  One workgroup; every result is an integer and exact.
+//
+// Stable rank without sorting: within a row the k routed experts and the S
+// shared experts are distinct, so the rank of slot (m, j) inside expert e's
+// segment is the number of earlier rows that chose e.  Rows are taken 64 at a
+// time; mask[e] has bit (m mod 64) set for each row of the chunk that chose
+// e, and rank = base[e] + popcount(mask[e] & bits below m).
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+constexpr int BK_THREADS = 1024;
+
+// Expert of slot t, or -1 for a routed id outside [0, E).
+__device__ __forceinline__ int slot_expert(const int32_t *ids, int t, int k, int kps, int E) {
+  const int m = t / kps, j = t - m * kps;
+  if (j >= k) return E + (j - k);
+  const int e = ids[(int64_t)m * k + j];
+  return (e >= 0 && e < E) ? e : -1;
+}
+
+__global__ __launch_bounds__(BK_THREADS) void bucket_kernel(const int32_t *__restrict__ ids, int M, int k, int E,
+                                                            int S, int32_t *__restrict__ offsets,
+                                                            int32_t *__restrict__ perm, int32_t *__restrict__ active,
+                                                            int32_t *__restrict__ n_active,
+                                                            int32_t *__restrict__ dev_error) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int NE = E + S;
+  unsigned long long *mask = (unsigned long long *)smem;  // [NE]
+  int32_t *base = (int32_t *)(mask + NE);                 // [NE] counts, then running bases
+  __shared__ int32_t wave_sum[16][2];
+  __shared__ int32_t err;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int kps = k + S;
+  const int T = M * kps;
+
+  for (int e = tid; e < NE; e += BK_THREADS) base[e] = 0;
+  if (tid == 0) err = 0;
+  __syncthreads();
+  // ---- counts
+  for (int t = tid; t < T; t += BK_THREADS) {
+    const int e = slot_expert(ids, t, k, kps, E);
+    if (e < 0 || e >= NE) err = 1;
+    else atomicAdd(&base[e], 1);
+  }
+  __syncthreads();
+  // ---- exclusive scan of counts (offsets) and of nonempty flags (active)
+  const int per = (NE + BK_THREADS - 1) / BK_THREADS;
+  const int e_beg = tid * per;
+  int c_loc = 0, a_loc = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = e_beg + i;
+    if (e < NE) { c_loc += base[e]; a_loc += base[e] > 0; }
+  }
+  int cv = c_loc, av = a_loc;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int tc = __shfl_up(cv, o, 64), ta = __shfl_up(av, o, 64);
+    if (lane >= o) { cv += tc; av += ta; }
+  }
+  if (lane == 63) { wave_sum[wv][0] = cv; wave_sum[wv][1] = av; }
+  __syncthreads();
+  int c_ex = cv - c_loc, a_ex = av - a_loc, c_tot = 0, a_tot = 0;
+  for (int w2 = 0; w2 < BK_THREADS / 64; ++w2) {
+    if (w2 < wv) { c_ex += wave_sum[w2][0]; a_ex += wave_sum[w2][1]; }
+    c_tot += wave_sum[w2][0];
+    a_tot += wave_sum[w2][1];
+  }
+  __syncthreads();  // every thread has read its counts range before it is overwritten
+  for (int i = 0; i < per; ++i) {
+    const int e = e_beg + i;
+    if (e < NE) {
+      const int c = base[e];
+      offsets[e] = c_ex;
+      if (c > 0) active[a_ex++] = e;
+      base[e] = c_ex;
+      c_ex += c;
+    }
+  }
+  if (tid == 0) {
+    offsets[NE] = c_tot;
+    *n_active = a_tot;
+  }
+  __syncthreads();
+  // ---- stable placement, 64 rows at a time
+  for (int m0 = 0; m0 < M; m0 += 64) {
+    for (int e = tid; e < NE; e += BK_THREADS) mask[e] = 0ull;
+    __syncthreads();
+    const int mrows = (M - m0) < 64 ? (M - m0) : 64;
+    const int tc = mrows * kps;
+    for (int i = tid; i < tc; i += BK_THREADS) {
+      const int t = m0 * kps + i;
+      const int e = slot_expert(ids, t, k, kps, E);
+      if (e >= 0 && e < NE) {
+        const unsigned long long bit = 1ull << (t / kps - m0);
+        const unsigned long long old = atomicOr(&mask[e], bit);
+        if (old & bit) err = 1;  // a row names the same expert twice
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < tc; i += BK_THREADS) {
+      const int t = m0 * kps + i;
+      const int e = slot_expert(ids, t, k, kps, E);
+      if (e >= 0 && e < NE) {
+        const unsigned long long bit = 1ull << (t / kps - m0);
+        const int rank = base[e] + __popcll(mask[e] & (bit - 1ull));
+        if (rank < T) perm[rank] = t;
+      }
+    }
+    __syncthreads();
+    for (int e = tid; e < NE; e += BK_THREADS) base[e] += __popcll(mask[e]);
+    __syncthreads();
+  }
+  if (tid == 0) *dev_error = err;
+}
+
+int bucket_launch(const int32_t *ids, int M, int k, int E, int S, int32_t *offsets, int32_t *perm, int32_t *active,
+                  int32_t *n_active, int32_t *dev_error, hipStream_t stream) {
+  const int NE = E + S;
+  const size_t smem = (size_t)NE * (sizeof(unsigned long long) + sizeof(int32_t));
+  hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(BK_THREADS), smem, stream, ids, M, k, E, S, offsets, perm, active,
+                     n_active, dev_error);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+// ------------------------------------------------------------------ combine
+// out[m,r] = sum_{j<k} w[m,j] y[m*(k+S)+j, r] + sum_{s<S} y[m*(k+S)+k+s, r],
+// fp32, in slot order.  One thread per 4 consecutive r.
+__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y, const float *__restrict__ w, int M,
+                                                      int k, int S, int d, float *__restrict__ out) {
+  const int d4 = d >> 2;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)M * d4) return;
+  const int64_t m = idx / d4;
+  const int c = (int)(idx - m * d4) * 4;
+  const int kps = k + S;
+  const float *ym = y + m * kps * (int64_t)d + c;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) {
+    const float wj = w[m * k + j];
+    const f32x4 v = *(const f32x4 *)(ym + (int64_t)j * d);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(wj, v[i], acc[i]);
+  }
+  for (int s = 0; s < S; ++s) {
+    const f32x4 v = *(const f32x4 *)(ym + (int64_t)(k + s) * d);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += v[i];
+  }
+  *(f32x4 *)(out + m * (int64_t)d + c) = acc;
+}
+
+int combine_launch(const float *y, const float *w, int M, int k, int S, int d, float *out, hipStream_t stream) {
+  const int64_t n = (int64_t)M * (d / 4);
+  const int64_t grid = (n + 255) / 256;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)grid), dim3(256), 0, stream, y, w, M, k, S, d, out);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+}  // namespace moe

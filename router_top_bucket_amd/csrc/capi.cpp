@@ -1,0 +1,114 @@
+// extern "C" entry points of libmoe: host-side argument validation, then the
+// kernels are enqueued on the caller's stream.  Declarations and the contract
+// of each function are in include/moe.h.
+#include <hip/hip_runtime.h>
+
+#include "../../include/moe.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int kMaxExperts = 4096;  // E + S bound of the single-workgroup bucket and of top-k keys in LDS
+
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline int status_of(int rc) { return rc == 0 ? MOE_OK : MOE_EHIP; }
+
+inline bool experts_ok(const moe_experts *W) {
+  if (!W || !W->base) return false;
+  if (W->d <= 0 || W->f <= 0 || W->d % 32 || W->f % 32) return false;
+  if (W->n_routed <= 0 || W->n_shared < 0) return false;
+  const int64_t rec = (int64_t)3 * W->d * W->f * 17 / 32;
+  if (W->stride < rec || W->stride % 16) return false;
+  if (reinterpret_cast<uintptr_t>(W->base) % 16) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: valid but not supported by this build";
+    case MOE_EHIP: return "MOE_EHIP: HIP launch or runtime error";
+    default: return "unknown moe_status";
+  }
+}
+
+int moe_route(const void *x, moe_dtype x_dtype, const float *w_router, float *logits, int32_t M, int32_t d,
+              int32_t E, int32_t k, int32_t *topk_ids, float *topk_w, void *stream) {
+  if (M < 0 || E <= 0 || k < 1 || k > E) return MOE_EINVAL;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_EINVAL;
+  if (!logits || !topk_ids || !topk_w) return MOE_EINVAL;
+  if (w_router) {
+    if (!x || d <= 0 || d % 32) return MOE_EINVAL;
+    if (reinterpret_cast<uintptr_t>(w_router) % 16 || reinterpret_cast<uintptr_t>(x) % 16) return MOE_EINVAL;
+  }
+  if (E > kMaxExperts || k > 64) return MOE_EUNSUPPORTED;
+  if (M == 0) return MOE_OK;
+  return status_of(moe::route_launch(x, x_dtype == MOE_BF16, w_router, logits, M, d, E, k, topk_ids, topk_w,
+                                     as_stream(stream)));
+}
+
+int moe_bucket(const int32_t *topk_ids, int32_t M, int32_t k, int32_t E, int32_t n_shared, int32_t *offsets,
+               int32_t *perm, int32_t *active, int32_t *n_active, int32_t *dev_error, void *stream) {
+  if (M < 0 || k < 1 || E <= 0 || n_shared < 0) return MOE_EINVAL;
+  if (!topk_ids || !offsets || !perm || !active || !n_active || !dev_error) return MOE_EINVAL;
+  if (E + n_shared > kMaxExperts) return MOE_EUNSUPPORTED;
+  if ((int64_t)M * (k + n_shared) > INT32_MAX / 2) return MOE_EUNSUPPORTED;
+  if (M == 0) return MOE_OK;
+  return status_of(moe::bucket_launch(topk_ids, M, k, E, n_shared, offsets, perm, active, n_active, dev_error,
+                                      as_stream(stream)));
+}
+
+size_t moe_workspace_bytes(int32_t M, int32_t k, const moe_experts *W) {
+  if (M < 0 || k < 1 || !experts_ok(W)) return 0;
+  return moe::ffn_workspace_bytes(M, k, W->n_shared, W->d, W->f, W->n_routed + W->n_shared);
+}
+
+int moe_expert_ffn_mxfp4(const void *x, moe_dtype x_dtype, int32_t M, int32_t k, const moe_experts *W,
+                         const int32_t *offsets, const int32_t *perm, const int32_t *active,
+                         const int32_t *n_active, float *y_slots, void *workspace, size_t workspace_bytes,
+                         void *stream) {
+  if (M < 0 || k < 1 || !experts_ok(W)) return MOE_EINVAL;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_EINVAL;
+  if (!x || !offsets || !perm || !active || !n_active || !y_slots || !workspace) return MOE_EINVAL;
+  if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(y_slots) % 16 ||
+      reinterpret_cast<uintptr_t>(workspace) % 256)
+    return MOE_EINVAL;
+  if (k > W->n_routed) return MOE_EINVAL;
+  if (W->n_routed + W->n_shared > kMaxExperts) return MOE_EUNSUPPORTED;
+  if (!moe::ffn_smem_limit_ok(W->d, W->f)) return MOE_EUNSUPPORTED;
+  if ((int64_t)M * (k + W->n_shared) > INT32_MAX / 2) return MOE_EUNSUPPORTED;
+  if (M == 0) return MOE_OK;
+  if (workspace_bytes < moe::ffn_workspace_bytes(M, k, W->n_shared, W->d, W->f, W->n_routed + W->n_shared))
+    return MOE_EINVAL;
+  return status_of(moe::ffn_launch(x, x_dtype == MOE_BF16, M, k, W->base, W->stride, W->d, W->f, W->n_routed,
+                                   W->n_shared, offsets, perm, active, n_active, y_slots, workspace,
+                                   as_stream(stream)));
+}
+
+int moe_combine(const float *y_slots, const float *topk_w, int32_t M, int32_t k, int32_t n_shared, int32_t d,
+                float *out, void *stream) {
+  if (M < 0 || k < 1 || n_shared < 0 || d <= 0 || d % 4) return MOE_EINVAL;
+  if (!y_slots || !topk_w || !out) return MOE_EINVAL;
+  if (reinterpret_cast<uintptr_t>(y_slots) % 16 || reinterpret_cast<uintptr_t>(out) % 16) return MOE_EINVAL;
+  if (M == 0) return MOE_OK;
+  return status_of(moe::combine_launch(y_slots, topk_w, M, k, n_shared, d, out, as_stream(stream)));
+}
+
+int q8_0_matmul(const float *X, int32_t M, int32_t K, const int8_t *Wq, const uint16_t *Ws, int32_t N, float *Y,
+                void *stream) {
+  if (M < 0 || K <= 0 || K % 32 || N <= 0) return MOE_EINVAL;
+  if (!X || !Wq || !Ws || !Y) return MOE_EINVAL;
+  if (reinterpret_cast<uintptr_t>(X) % 16 || reinterpret_cast<uintptr_t>(Wq) % 16) return MOE_EINVAL;
+  if (M > 8) return MOE_EUNSUPPORTED;
+  if ((int64_t)(K / 32 + 2) * 64 * 2 > 65536) return MOE_EUNSUPPORTED;
+  if (M == 0) return MOE_OK;
+  return status_of(moe::q8_0_launch(X, M, K, Wq, Ws, N, Y, as_stream(stream)));
+}
+
+}  // extern "C"

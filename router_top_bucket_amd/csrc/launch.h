@@ -1,0 +1,28 @@
+// Internal launch interface between the C ABI (capi.cpp) and the kernels.
+// Arguments are validated by the caller; these functions only enqueue.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+int route_launch(const void *x, int x_bf16, const float *w_router, float *logits, int M, int d, int E, int k,
+                 int32_t *ids, float *w, hipStream_t stream);
+
+int bucket_launch(const int32_t *ids, int M, int k, int E, int S, int32_t *offsets, int32_t *perm, int32_t *active,
+                  int32_t *n_active, int32_t *dev_error, hipStream_t stream);
+
+int64_t ffn_max_groups(int64_t M, int k, int S, int n_experts);
+size_t ffn_workspace_bytes(int64_t M, int k, int S, int d, int f, int n_experts);
+size_t ffn_smem_limit_ok(int d, int f);
+int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *experts, int64_t stride, int d, int f,
+               int n_routed, int n_shared, const int32_t *offsets, const int32_t *perm, const int32_t *active,
+               const int32_t *n_active, float *y, void *workspace, hipStream_t stream);
+
+int combine_launch(const float *y, const float *w, int M, int k, int S, int d, float *out, hipStream_t stream);
+
+int q8_0_launch(const float *X, int M, int K, const int8_t *wq, const uint16_t *ws, int N, float *Y,
+                hipStream_t stream);
+
+}  // namespace moe

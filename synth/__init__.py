@@ -153,3 +153,16 @@ def q8_0_weight(seed: int, K: int, N: int):
 
 def q8_0_x(seed: int, M: int, K: int) -> np.ndarray:
     return rng(seed, _T_Q8, M, K, 1).standard_normal((M, K), dtype=np.float32)
+
+
+def device_experts(shape: LayerShape, seed: int, device="cuda", ids=None):
+    """All expert records of a layer (or only ``ids``, others left zero) in one
+    device uint8 tensor of n_experts * stride bytes; generated on the host one
+    record at a time and copied up."""
+    import torch
+
+    base = torch.zeros(shape.n_experts * shape.stride, dtype=torch.uint8, device=device)
+    todo = range(shape.n_experts) if ids is None else ids
+    for e, rec in expert_records(shape, seed, todo):
+        base[e * shape.stride:(e + 1) * shape.stride].copy_(torch.from_numpy(rec), non_blocking=False)
+    return base

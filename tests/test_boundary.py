@@ -1,0 +1,158 @@
+"""The C-ABI library: it loads, exports every function include/moe.h declares,
+and rejects invalid arguments on the host before anything is enqueued.  CPU
+only: no call here passes validation, so no kernel is ever launched."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char \*)\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for fn in ("moe_route", "moe_bucket", "moe_expert_ffn_mxfp4", "moe_combine", "q8_0_matmul"):
+        assert fn in names
+
+
+def test_library_exports_every_declared_symbol():
+    import router_top_bucket_amd as moe
+    lib = moe.raw_library()
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.library_path()], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in _declared_functions():
+        assert name in exported, f"{name} not exported"
+        assert hasattr(lib, name)
+    assert set(moe.ABI_FUNCTIONS) == set(_declared_functions())
+
+
+def test_header_compiles_as_c():
+    # the header is plain C: no HIP or torch types in the signatures
+    r = subprocess.run(["gcc", "-std=c99", "-fsyntax-only", "-Wall", "-Werror", "-x", "c", HEADER],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_status_strings():
+    import router_top_bucket_amd as moe
+    lib = moe.raw_library()
+    assert lib.moe_status_str(0) == b"MOE_OK"
+    assert lib.moe_status_str(-1).startswith(b"MOE_EINVAL")
+    assert lib.moe_status_str(-2).startswith(b"MOE_EUNSUPPORTED")
+    assert lib.moe_status_str(-3).startswith(b"MOE_EHIP")
+
+
+FAKE = 0x100000  # never dereferenced: every call below fails host validation
+
+
+def test_route_validation():
+    import router_top_bucket_amd as moe
+    lib = moe.raw_library()
+    EINVAL, EUNSUP = moe.MOE_EINVAL, moe.MOE_EUNSUPPORTED
+    assert lib.moe_route(None, 0, None, None, 1, 0, 16, 2, None, None, None) == EINVAL  # NULL outputs
+    assert lib.moe_route(None, 0, None, FAKE, -1, 0, 16, 2, FAKE, FAKE, None) == EINVAL  # M < 0
+    assert lib.moe_route(None, 0, None, FAKE, 1, 0, 16, 0, FAKE, FAKE, None) == EINVAL  # k < 1
+    assert lib.moe_route(None, 0, None, FAKE, 1, 0, 16, 17, FAKE, FAKE, None) == EINVAL  # k > E
+    assert lib.moe_route(None, 7, None, FAKE, 1, 0, 16, 2, FAKE, FAKE, None) == EINVAL  # dtype
+    assert lib.moe_route(FAKE, 0, FAKE, FAKE, 1, 100, 16, 2, FAKE, FAKE, None) == EINVAL  # d % 32
+    assert lib.moe_route(None, 0, FAKE, FAKE, 1, 256, 16, 2, FAKE, FAKE, None) == EINVAL  # x NULL with router
+    assert lib.moe_route(None, 0, None, FAKE, 1, 0, 5000, 2, FAKE, FAKE, None) == EUNSUP  # E too large
+    assert lib.moe_route(None, 0, None, FAKE, 0, 0, 16, 2, FAKE, FAKE, None) == moe.MOE_OK  # M = 0: no-op
+
+
+def test_bucket_validation():
+    import router_top_bucket_amd as moe
+    lib = moe.raw_library()
+    EINVAL = moe.MOE_EINVAL
+    assert lib.moe_bucket(None, 1, 2, 16, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == EINVAL
+    assert lib.moe_bucket(FAKE, 1, 0, 16, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == EINVAL
+    assert lib.moe_bucket(FAKE, 1, 2, 16, -1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == EINVAL
+    assert lib.moe_bucket(FAKE, 1, 2, 16, 0, FAKE, FAKE, FAKE, FAKE, None, None) == EINVAL
+    assert lib.moe_bucket(FAKE, 1, 2, 4095, 2, FAKE, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_EUNSUPPORTED
+    assert lib.moe_bucket(FAKE, 0, 2, 16, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_OK
+
+
+def _experts(**kw):
+    import router_top_bucket_amd as moe
+    v = dict(base=FAKE, stride=52224, d=256, f=128, n_routed=16, n_shared=0)
+    v.update(kw)
+    return moe._Experts(v["base"], v["stride"], v["d"], v["f"], v["n_routed"], v["n_shared"])
+
+
+def test_ffn_validation_and_workspace_query():
+    import router_top_bucket_amd as moe
+    lib = moe.raw_library()
+    EINVAL = moe.MOE_EINVAL
+    ok = _experts()
+    assert lib.moe_workspace_bytes(1, 2, ctypes.byref(ok)) > 0
+    for bad in (_experts(d=100), _experts(f=50), _experts(stride=1000), _experts(base=0), _experts(n_routed=0),
+                _experts(base=FAKE + 4)):
+        assert lib.moe_workspace_bytes(1, 2, ctypes.byref(bad)) == 0
+        assert lib.moe_expert_ffn_mxfp4(FAKE, 0, 1, 2, ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                        1 << 20, None) == EINVAL
+    # workspace too small
+    need = lib.moe_workspace_bytes(4, 2, ctypes.byref(ok))
+    assert lib.moe_expert_ffn_mxfp4(FAKE, 0, 4, 2, ctypes.byref(ok), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1,
+                                    None) == EINVAL
+    # k > E, NULL y, misaligned workspace
+    assert lib.moe_expert_ffn_mxfp4(FAKE, 0, 1, 17, ctypes.byref(ok), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                                    None) == EINVAL
+    assert lib.moe_expert_ffn_mxfp4(FAKE, 0, 1, 2, ctypes.byref(ok), FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30,
+                                    None) == EINVAL
+    assert lib.moe_expert_ffn_mxfp4(FAKE, 0, 1, 2, ctypes.byref(ok), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 16,
+                                    1 << 30, None) == EINVAL
+    assert lib.moe_expert_ffn_mxfp4(FAKE, 0, 0, 2, ctypes.byref(ok), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0,
+                                    None) == moe.MOE_OK
+
+
+def test_workspace_grows_with_rows():
+    import router_top_bucket_amd as moe
+    lib = moe.raw_library()
+    kimi = _experts(stride=17547264, d=7168, f=1536, n_routed=896, n_shared=2)
+    a = lib.moe_workspace_bytes(1, 16, ctypes.byref(kimi))
+    b = lib.moe_workspace_bytes(16, 16, ctypes.byref(kimi))
+    c = lib.moe_workspace_bytes(1533, 16, ctypes.byref(kimi))
+    assert 0 < a < b < c
+    # h for every slot in three bf16 parts, at least
+    assert c >= 1533 * 18 * 1536 * 6
+
+
+def test_combine_and_q8_0_validation():
+    import router_top_bucket_amd as moe
+    lib = moe.raw_library()
+    EINVAL = moe.MOE_EINVAL
+    assert lib.moe_combine(FAKE, FAKE, 1, 0, 0, 16, FAKE, None) == EINVAL
+    assert lib.moe_combine(FAKE, FAKE, 1, 2, 0, 18, FAKE, None) == EINVAL  # d % 4
+    assert lib.moe_combine(None, FAKE, 1, 2, 0, 16, FAKE, None) == EINVAL
+    assert lib.moe_combine(FAKE, FAKE, 0, 2, 0, 16, FAKE, None) == moe.MOE_OK
+    assert lib.q8_0_matmul(FAKE, 1, 100, FAKE, FAKE, 10, FAKE, None) == EINVAL  # K % 32
+    assert lib.q8_0_matmul(FAKE, 9, 128, FAKE, FAKE, 10, FAKE, None) == moe.MOE_EUNSUPPORTED  # M > 8
+    assert lib.q8_0_matmul(None, 1, 128, FAKE, FAKE, 10, FAKE, None) == EINVAL
+    assert lib.q8_0_matmul(FAKE, 0, 128, FAKE, FAKE, 10, FAKE, None) == moe.MOE_OK
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    # the product path has no fallback: a copy of the package without the
+    # built library raises on import instead of computing anything elsewhere
+    import shutil
+    pkg = os.path.join(ROOT, "router_top_bucket_amd")
+    dst = tmp_path / "router_top_bucket_amd"
+    shutil.copytree(pkg, dst, ignore=shutil.ignore_patterns("*.so", "_build", "__pycache__"))
+    code = ("import sys\n"
+            "try:\n"
+            "    import router_top_bucket_amd\n"
+            "except ImportError as e:\n"
+            "    print('RAISED', e)\n")
+    r = subprocess.run(["python", "-c", code], cwd=str(tmp_path), capture_output=True, text=True)
+    assert "RAISED" in r.stdout, r.stdout + r.stderr

@@ -1,0 +1,374 @@
+"""GPU parity: every C-ABI call against the CPU oracle on the same seeded
+inputs, plus the pages' invariants on the GPU path ("A drafter that leaves
+the answer unchanged": block rows equal plain steps bit for bit; outputs are
+unchanged by the order experts are computed in).  Needs an MI355X."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from conftest import assert_close
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _moe():
+    import router_top_bucket_amd as moe
+    return moe
+
+
+def _dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.cuda()
+
+
+def _host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+# ----------------------------------------------------------------------------- fixtures
+@pytest.fixture(scope="session")
+def kimi_layer():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe = _moe()
+    shp = synth.KIMI
+    seed = 0
+    print(f"\n[kimi_layer] generating {shp.n_experts} experts ({shp.n_experts * shp.stride / 1e9:.1f} GB)", flush=True)
+    base = synth.device_experts(shp, seed)
+    ex = moe.Experts(base, shp.stride, shp.d, shp.f, shp.n_routed, shp.n_shared)
+    wr = synth.router_weight(shp, seed)
+    cache = {}
+
+    def rec(e):
+        if e not in cache:
+            cache[e] = synth.expert_record(shp, seed, e)
+        return cache[e]
+
+    return dict(shape=shp, experts=ex, wr=wr, wr_dev=_dev(wr), rec=rec)
+
+
+def _small_layer(shape, seed):
+    moe = _moe()
+    base = synth.device_experts(shape, seed)
+    ex = moe.Experts(base, shape.stride, shape.d, shape.f, shape.n_routed, shape.n_shared)
+    recs = {e: synth.expert_record(shape, seed, e) for e in range(shape.n_experts)}
+    return ex, recs
+
+
+def _x_dev(shape, x):
+    return _dev(x, torch.bfloat16) if shape.x_dtype == "bf16" else _dev(x)
+
+
+def _compare_layer(res_gpu, ref, what, k, S, exact_ids=True):
+    assert_close(_host(res_gpu["logits"]), ref["logits"], what + " logits")
+    ids = _host(res_gpu["topk_ids"])
+    if exact_ids:
+        assert np.array_equal(ids, ref["ids"]), what + " ids"
+    assert_close(_host(res_gpu["topk_w"]), ref["w"], what + " w")
+    assert np.array_equal(_host(res_gpu["offsets"]), ref["offsets"]), what + " offsets"
+    assert np.array_equal(_host(res_gpu["perm"]), ref["perm"]), what + " perm"
+    na = int(_host(res_gpu["n_active"])[0])
+    assert na == ref["n_active"]
+    assert np.array_equal(_host(res_gpu["active"])[:na], ref["active"]), what + " active"
+    assert int(_host(res_gpu["dev_error"])[0]) == 0
+    assert_close(_host(res_gpu["y_slots"]), ref["y_slots"], what + " y_slots")
+    assert_close(_host(res_gpu["out"]), ref["out"], what + " out")
+
+
+# ----------------------------------------------------------------------------- tiny layer
+@pytest.mark.parametrize("seed", range(20))
+def test_tiny_layer_parity(seed):
+    moe = _moe()
+    shp = synth.TINY
+    ex, recs = _small_layer(shp, seed)
+    wr = synth.router_weight(shp, seed)
+    x = synth.rows_x(shp, seed, 1)
+    layer = moe.MoELayer(ex, shp.k, 1, w_router=_dev(wr))
+    res = layer.forward(_x_dev(shp, x))
+    ref = oracle.layer(x, shp.k, shp.n_routed, shp.n_shared, shp.d, shp.f, recs.__getitem__, w_r=wr)
+    _compare_layer(res, ref, f"tiny seed {seed}", shp.k, shp.n_shared)
+
+
+# ----------------------------------------------------------------------------- route
+@pytest.mark.parametrize("M,E,k", [(1, 896, 16), (16, 896, 16), (1533, 896, 16), (7, 16, 2), (3, 100, 1),
+                                   (5, 64, 64), (2, 4096, 16)])
+def test_route_given_logits_exact(M, E, k):
+    moe = _moe()
+    lg = synth.random_logits(M + E, M, E)
+    # ties and NaN: quantise some rows to a coarse grid, poison a few entries
+    lg[::3] = np.round(lg[::3] * 2) / 2
+    lg[1::5, ::7] = np.nan
+    if M > 1:
+        lg[-1] = 0.25  # an all-equal row
+    ids_ref, w_ref = oracle.topk(lg, k)
+    d_lg = _dev(lg)
+    ids = torch.empty((M, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((M, k), dtype=torch.float32, device="cuda")
+    moe.moe_route(None, None, d_lg, k, ids, w)
+    assert np.array_equal(_host(ids), ids_ref)
+    assert_close(_host(w), w_ref, "topk weights")
+
+
+def test_route_zipf_prefill_logits_exact():
+    moe = _moe()
+    for M in (270, 1533):
+        lg = synth.zipf_logits(synth.KIMI, 1, M)
+        ids_ref, w_ref = oracle.topk(lg, 16)
+        ids = torch.empty((M, 16), dtype=torch.int32, device="cuda")
+        w = torch.empty((M, 16), dtype=torch.float32, device="cuda")
+        moe.moe_route(None, None, _dev(lg), 16, ids, w)
+        assert np.array_equal(_host(ids), ids_ref)
+        assert_close(_host(w), w_ref, "zipf weights")
+
+
+# ----------------------------------------------------------------------------- bucket
+def _run_bucket(ids_np, E, S):
+    moe = _moe()
+    M, k = ids_np.shape
+    T = M * (k + S)
+    i32 = dict(dtype=torch.int32, device="cuda")
+    offsets = torch.full((E + S + 1,), -7, **i32)
+    perm = torch.full((max(T, 1),), -7, **i32)
+    active = torch.full((E + S,), -7, **i32)
+    na = torch.full((1,), -7, **i32)
+    err = torch.full((1,), -7, **i32)
+    moe.moe_bucket(_dev(ids_np), E, S, offsets, perm, active, na, err)
+    return _host(offsets), _host(perm)[:T], _host(active), int(_host(na)[0]), int(_host(err)[0])
+
+
+@pytest.mark.parametrize("M,E,k,S", [(1, 896, 16, 2), (3, 16, 2, 0), (16, 896, 16, 2), (64, 896, 16, 2),
+                                     (65, 896, 16, 2), (270, 896, 16, 2), (1533, 896, 16, 2), (5, 4, 4, 1),
+                                     (200, 4000, 16, 96)])
+def test_bucket_exact(M, E, k, S):
+    g = synth.rng(3, M, E)
+    ids = np.stack([g.permutation(E)[:k] for _ in range(M)]).astype(np.int32)
+    off, perm, act, na, err = _run_bucket(ids, E, S)
+    r_off, r_perm, r_act, r_na = oracle.bucket(ids, E, S)
+    assert err == 0
+    assert np.array_equal(off, r_off) and np.array_equal(perm, r_perm)
+    assert na == r_na and np.array_equal(act[:na], r_act)
+
+
+def test_bucket_zipf_exact():
+    lg = synth.zipf_logits(synth.KIMI, 2, 1533)
+    ids, _ = oracle.topk(lg, 16)
+    off, perm, act, na, err = _run_bucket(ids, 896, 2)
+    r_off, r_perm, r_act, r_na = oracle.bucket(ids, 896, 2)
+    assert err == 0 and np.array_equal(off, r_off) and np.array_equal(perm, r_perm)
+    assert na == r_na and np.array_equal(act[:na], r_act)
+
+
+def test_bucket_flags_bad_ids_in_bounds():
+    ids = np.array([[0, 5], [3, 16], [-1, 2], [4, 4]], dtype=np.int32)  # out of range and a repeat
+    off, perm, act, na, err = _run_bucket(ids, 16, 1)
+    assert err == 1
+    assert off[-1] <= 4 * 3  # only valid slots counted, all writes in bounds
+    valid = np.array([[0, 5], [3, 1], [6, 2], [7, 8]], dtype=np.int32)
+    off, perm, act, na, err = _run_bucket(valid, 16, 1)
+    assert err == 0  # the flag is cleared by a clean call
+
+
+# ----------------------------------------------------------------------------- combine
+@pytest.mark.parametrize("M,k,S,d", [(1, 16, 2, 7168), (16, 16, 2, 7168), (5, 2, 0, 256), (3, 4, 3, 8)])
+def test_combine_parity(M, k, S, d):
+    moe = _moe()
+    g = synth.rng(4, M, d)
+    y = g.standard_normal((M * (k + S), d)).astype(np.float32)
+    w = g.random((M, k)).astype(np.float32)
+    out = torch.empty((M, d), dtype=torch.float32, device="cuda")
+    moe.moe_combine(_dev(y), _dev(w), k, S, out)
+    assert_close(_host(out), oracle.combine(y, w, k, S), "combine")
+
+
+# ----------------------------------------------------------------------------- FFN, ragged shapes
+RAGGED = [
+    synth.LayerShape("r1", 160, 96, 5, 1, 3, -6, -2, 0.05, "f32"),
+    synth.LayerShape("r2", 160, 96, 5, 1, 3, -6, -2, 0.05, "bf16"),
+    synth.LayerShape("r3", 416, 224, 9, 2, 4, -7, -3, 0.05, "bf16"),
+    synth.LayerShape("r4", 96, 32, 3, 0, 1, -5, -1, 0.05, "f32"),
+]
+
+
+@pytest.mark.parametrize("shape", RAGGED, ids=lambda s: s.name)
+@pytest.mark.parametrize("M", [1, 7, 16, 17, 40])
+def test_ffn_ragged_parity(shape, M):
+    moe = _moe()
+    ex, recs = _small_layer(shape, 5)
+    wr = synth.router_weight(shape, 5)
+    x = synth.rows_x(shape, 6, M)
+    layer = moe.MoELayer(ex, shape.k, M, w_router=_dev(wr))
+    res = layer.forward(_x_dev(shape, x))
+    ref = oracle.layer(x, shape.k, shape.n_routed, shape.n_shared, shape.d, shape.f, recs.__getitem__, w_r=wr)
+    _compare_layer(res, ref, f"{shape.name} M={M}", shape.k, shape.n_shared)
+
+
+# ----------------------------------------------------------------------------- Kimi decode
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_kimi_one_row_parity(kimi_layer, seed):
+    moe = _moe()
+    L = kimi_layer
+    shp = L["shape"]
+    x = synth.rows_x(shp, 100 + seed, 1)
+    layer = moe.MoELayer(L["experts"], shp.k, 1, w_router=L["wr_dev"])
+    res = layer.forward(_x_dev(shp, x))
+    ref = oracle.layer(x, shp.k, shp.n_routed, shp.n_shared, shp.d, shp.f, L["rec"], w_r=L["wr"])
+    _compare_layer(res, ref, f"kimi 1 row seed {seed}", shp.k, shp.n_shared)
+
+
+def _row_outputs(res, m, k, S):
+    kps = k + S
+    return dict(logits=_host(res["logits"][m]), ids=_host(res["topk_ids"][m]), w=_host(res["topk_w"][m]),
+                y=_host(res["y_slots"][m * kps:(m + 1) * kps]), out=_host(res["out"][m]))
+
+
+@pytest.mark.parametrize("B", [2, 8, 16])
+def test_kimi_block_rows_equal_single_rows(kimi_layer, B):
+    """Block rows run the same arithmetic as plain steps: bit-identical."""
+    moe = _moe()
+    L = kimi_layer
+    shp = L["shape"]
+    blk = moe.MoELayer(L["experts"], shp.k, B, w_router=L["wr_dev"])
+    one = moe.MoELayer(L["experts"], shp.k, 1, w_router=L["wr_dev"])
+    for seed in range(20 if B == 16 else 6):
+        x = synth.block_x(shp, seed, B)
+        xd = _x_dev(shp, x)
+        rb = blk.forward(xd)
+        for m in range(B):
+            r1 = one.forward(xd[m:m + 1])
+            a = _row_outputs(rb, m, shp.k, shp.n_shared)
+            b = _row_outputs(r1, 0, shp.k, shp.n_shared)
+            for key in a:
+                assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), (B, seed, m, key)
+
+
+def test_kimi_block16_parity(kimi_layer):
+    moe = _moe()
+    L = kimi_layer
+    shp = L["shape"]
+    x = synth.block_x(shp, 0, 16)
+    layer = moe.MoELayer(L["experts"], shp.k, 16, w_router=L["wr_dev"])
+    res = layer.forward(_x_dev(shp, x))
+    ref = oracle.layer(x, shp.k, shp.n_routed, shp.n_shared, shp.d, shp.f, L["rec"], w_r=L["wr"])
+    print(f"block of 16: {ref['n_active'] - shp.n_shared} unique routed experts", flush=True)
+    _compare_layer(res, ref, "kimi block 16", shp.k, shp.n_shared)
+
+
+def test_kimi_expert_order_independence(kimi_layer):
+    """Outputs do not depend on the order experts are computed in."""
+    moe = _moe()
+    L = kimi_layer
+    shp = L["shape"]
+    x = _x_dev(shp, synth.block_x(shp, 3, 16))
+    layer = moe.MoELayer(L["experts"], shp.k, 16, w_router=L["wr_dev"])
+    res = layer.forward(x)
+    y_ref = _host(res["y_slots"]).copy()
+    na = int(_host(res["n_active"])[0])
+    act = res["active"]
+    g = torch.Generator().manual_seed(0)
+    for order in ("reverse", "shuffle"):
+        idx = torch.arange(na - 1, -1, -1) if order == "reverse" else torch.randperm(na, generator=g)
+        act[:na] = act[:na][idx.cuda()].clone()
+        res["y_slots"].zero_()
+        moe.moe_expert_ffn_mxfp4(x, shp.k, L["experts"], res["offsets"], res["perm"], act, res["n_active"],
+                                 res["y_slots"], layer.workspace)
+        assert np.array_equal(_host(res["y_slots"]).view(np.uint8), y_ref.view(np.uint8)), order
+
+
+# ----------------------------------------------------------------------------- prefill
+@pytest.mark.parametrize("M", [270, 1533])
+def test_kimi_prefill_parity_sampled(kimi_layer, M):
+    moe = _moe()
+    L = kimi_layer
+    shp = L["shape"]
+    kps = shp.k + shp.n_shared
+    x = synth.rows_x(shp, 7, M)
+    lg = synth.zipf_logits(shp, 7, M)
+    layer = moe.MoELayer(L["experts"], shp.k, M)
+    res = layer.forward(_x_dev(shp, x), logits=_dev(lg))
+    ids_ref, w_ref = oracle.topk(lg, shp.k)
+    assert np.array_equal(_host(res["topk_ids"]), ids_ref)
+    off_ref, perm_ref, act_ref, na_ref = oracle.bucket(ids_ref, shp.n_routed, shp.n_shared)
+    assert np.array_equal(_host(res["offsets"]), off_ref) and np.array_equal(_host(res["perm"]), perm_ref)
+    y = _host(res["y_slots"])
+    out = _host(res["out"])
+    xf = oracle.as_f32_rows(x)
+    # sampled rows: every slot of these rows, and their combined output
+    g = synth.rng(8, M)
+    rows = sorted(set([0, M - 1] + list(g.choice(M, 3, replace=False))))
+    for m in rows:
+        y_ref = np.zeros((kps, shp.d), np.float32)
+        for j in range(kps):
+            e = int(ids_ref[m, j]) if j < shp.k else shp.n_routed + j - shp.k
+            y_ref[j] = oracle.expert_ffn(xf[m:m + 1], L["rec"](e), shp.d, shp.f)[0]
+        assert_close(y[m * kps:(m + 1) * kps], y_ref, f"prefill M={M} row {m} y_slots")
+        o_ref = oracle.combine(y_ref, w_ref[m:m + 1], shp.k, shp.n_shared)
+        assert_close(out[m:m + 1], o_ref, f"prefill M={M} row {m} out")
+    # the most popular expert's segment spans many groups of 16: check its
+    # first and last slots
+    counts = np.diff(off_ref)[:shp.n_routed]
+    e_hot = int(np.argmax(counts))
+    seg = perm_ref[off_ref[e_hot]:off_ref[e_hot + 1]]
+    for t in (seg[0], seg[len(seg) // 2], seg[-1]):
+        m = t // kps
+        y_ref = oracle.expert_ffn(xf[m:m + 1], L["rec"](e_hot), shp.d, shp.f)[0]
+        assert_close(y[t], y_ref, f"prefill hot expert slot {t}")
+
+
+def test_kimi_prefill_rows_equal_decode_rows(kimi_layer):
+    """The >16-row path runs the same per-slot arithmetic as the decode path."""
+    moe = _moe()
+    L = kimi_layer
+    shp = L["shape"]
+    M = 270
+    x = _x_dev(shp, synth.rows_x(shp, 9, M))
+    lg = _dev(synth.zipf_logits(shp, 9, M))
+    big = moe.MoELayer(L["experts"], shp.k, M)
+    rb = big.forward(x, logits=lg)
+    one = moe.MoELayer(L["experts"], shp.k, 1)
+    for m in (0, 57, 269):
+        r1 = one.forward(x[m:m + 1], logits=lg[m:m + 1].contiguous())
+        a = _row_outputs(rb, m, shp.k, shp.n_shared)
+        b = _row_outputs(r1, 0, shp.k, shp.n_shared)
+        for key in ("ids", "w", "y", "out"):
+            assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), (m, key)
+
+
+# ----------------------------------------------------------------------------- Q8_0
+def _q8(seed, K, N, M):
+    wq, ws = synth.q8_0_weight(seed, K, N)
+    X = synth.q8_0_x(seed, M, K)
+    return X, wq, ws
+
+
+@pytest.mark.parametrize("K,N", [(7168, 7168), (256, 100), (96, 33), (7168, 18432)])
+@pytest.mark.parametrize("M", [1, 2, 4, 8])
+def test_q8_0_parity(K, N, M):
+    moe = _moe()
+    X, wq, ws = _q8(10, K, N, M)
+    Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    moe.q8_0_matmul(_dev(X), _dev(wq), _dev(ws, torch.int16), Y)
+    assert_close(_host(Y), oracle.q8_0_matmul(X, wq, ws), f"q8_0 K={K} N={N} M={M}")
+
+
+def test_q8_0_large_sampled_and_row_invariance():
+    moe = _moe()
+    K, N = 7168, 163840
+    wq, ws = synth.q8_0_weight(11, K, N)
+    X = synth.q8_0_x(11, 8, K)
+    dwq, dws = _dev(wq), _dev(ws, torch.int16)
+    Y8 = torch.empty((8, N), dtype=torch.float32, device="cuda")
+    moe.q8_0_matmul(_dev(X), dwq, dws, Y8)
+    y8 = _host(Y8)
+    cols = np.sort(synth.rng(12).choice(N, 512, replace=False))
+    ref = oracle.q8_0_matmul(X, wq[cols], ws[cols])
+    assert_close(y8[:, cols], ref, "q8_0 163840 sampled")
+    for M in (1, 2, 4):
+        YM = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        moe.q8_0_matmul(_dev(X[:M]), dwq, dws, YM)
+        assert np.array_equal(_host(YM).view(np.uint8), y8[:M].view(np.uint8)), M
