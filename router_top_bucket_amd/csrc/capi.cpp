@@ -81,7 +81,7 @@ int moe_expert_ffn_mxfp4(const void *x, moe_dtype x_dtype, int32_t M, int32_t k,
     return MOE_EINVAL;
   if (k > W->n_routed) return MOE_EINVAL;
   if (W->n_routed + W->n_shared > kMaxExperts) return MOE_EUNSUPPORTED;
-  if (!moe::ffn_smem_limit_ok(W->d, W->f)) return MOE_EUNSUPPORTED;
+  if (!moe::ffn_shape_ok(M, k, W->n_shared, W->d, W->f, W->stride)) return MOE_EUNSUPPORTED;
   if ((int64_t)M * (k + W->n_shared) > INT32_MAX / 2) return MOE_EUNSUPPORTED;
   if (M == 0) return MOE_OK;
   if (workspace_bytes < moe::ffn_workspace_bytes(M, k, W->n_shared, W->d, W->f, W->n_routed + W->n_shared))

@@ -64,6 +64,84 @@ __device__ __forceinline__ bf16x8 bits_to_bf16x8(u32x4 v) {
   return r;
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// ---- buffer loads: a 32-bit byte offset into a resource of `bytes` bytes.
+// An offset past the end reads as zero and never faults, so masked lanes and
+// ragged tails need no branch around the load.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// Every resource here is smaller than 2^30 bytes.  An invalid lane's base
+// offset is kOOB and a dead step adds kDead, so any sum involving either is
+// at least 2^30 (past the end) and at most ~3.3 * 2^30 (no 32-bit wrap).
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr uint32_t kDead = 0x40000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t buf_load1(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t sel_off(bool ok, uint32_t off) { return ok ? off : kOOB; }
+
+// ---- wave reductions without LDS: DPP inside each 16-lane row, then the four
+// row results read as scalars and combined in row order.  Every lane of a
+// row ends with bit-identical values (each step combines a lane with a fixed
+// partner; a + b == b + a and max is symmetric), so the result is uniform and
+// independent of which lane asks.
+#define MOE_DPP_QUAD_1032 0xB1  // quad_perm [1,0,3,2]
+#define MOE_DPP_QUAD_2301 0x4E  // quad_perm [2,3,0,1]
+#define MOE_DPP_ROW_HALF_MIRROR 0x141
+#define MOE_DPP_ROW_MIRROR 0x140
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Sum over the 64 lanes: ((row0 + row1) + row2) + row3 of fixed-tree row sums.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = v + dpp_f32<MOE_DPP_QUAD_1032>(v);
+  v = v + dpp_f32<MOE_DPP_QUAD_2301>(v);
+  v = v + dpp_f32<MOE_DPP_ROW_HALF_MIRROR>(v);
+  v = v + dpp_f32<MOE_DPP_ROW_MIRROR>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return ((r0 + r1) + r2) + r3;
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
+  const uint32_t lo = dpp_u32<CTRL>((uint32_t)v), hi = dpp_u32<CTRL>((uint32_t)(v >> 32));
+  return max_u64(v, ((uint64_t)hi << 32) | lo);
+}
+
+// Maximum over the 64 lanes (uniform result).
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = dpp_max_u64<MOE_DPP_QUAD_1032>(v);
+  v = dpp_max_u64<MOE_DPP_QUAD_2301>(v);
+  v = dpp_max_u64<MOE_DPP_ROW_HALF_MIRROR>(v);
+  v = dpp_max_u64<MOE_DPP_ROW_MIRROR>(v);
+  uint64_t r = 0;
+#pragma unroll
+  for (int row = 0; row < 4; ++row) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, row * 16);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), row * 16);
+    r = max_u64(r, ((uint64_t)hi << 32) | lo);
+  }
+  return r;
+}
 
 }  // namespace moe

@@ -15,7 +15,7 @@ int bucket_launch(const int32_t *ids, int M, int k, int E, int S, int32_t *offse
 
 int64_t ffn_max_groups(int64_t M, int k, int S, int n_experts);
 size_t ffn_workspace_bytes(int64_t M, int k, int S, int d, int f, int n_experts);
-size_t ffn_smem_limit_ok(int d, int f);
+bool ffn_shape_ok(int64_t M, int k, int S, int d, int f, int64_t stride);
 int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *experts, int64_t stride, int d, int f,
                int n_routed, int n_shared, const int32_t *offsets, const int32_t *perm, const int32_t *active,
                const int32_t *n_active, float *y, void *workspace, hipStream_t stream);

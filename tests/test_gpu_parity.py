@@ -196,7 +196,7 @@ RAGGED = [
 
 
 @pytest.mark.parametrize("shape", RAGGED, ids=lambda s: s.name)
-@pytest.mark.parametrize("M", [1, 7, 16, 17, 40])
+@pytest.mark.parametrize("M", [1, 3, 7, 16, 17, 40])
 def test_ffn_ragged_parity(shape, M):
     moe = _moe()
     ex, recs = _small_layer(shape, 5)
