@@ -122,13 +122,28 @@ int moe_bucket(const int32_t *topk_ids, int32_t M, int32_t k, int32_t E, int32_t
  *   workspace device scratch of at least moe_workspace_bytes(M, k, W) bytes,
  *             owned by the caller; contents on entry do not matter.
  * The result of a slot does not depend on M, on the other rows, or on the
- * order of the active list.  Requires W->d % 128 == 0 or d % 32 == 0 (any
- * multiple of 32 works), W->f % 32 == 0.
+ * order of the active list.  Requires W->d % 32 == 0 and W->f % 32 == 0;
+ * MOE_EUNSUPPORTED if a record, x or the workspace would exceed 2^30 bytes.
  */
 int moe_expert_ffn_mxfp4(const void *x, moe_dtype x_dtype, int32_t M, int32_t k, const moe_experts *W,
                          const int32_t *offsets, const int32_t *perm, const int32_t *active,
                          const int32_t *n_active, float *y_slots, void *workspace, size_t workspace_bytes,
                          void *stream);
+
+/* The two stages of moe_expert_ffn_mxfp4, for callers that time or schedule
+ * them apart.  moe_ffn_gateup_mxfp4 computes h = silu(W_gate x) * (W_up x) for
+ * every slot into the workspace; moe_ffn_down_mxfp4 then computes
+ * y_slots = W_down h from it.  The down stage must follow the gate/up stage on
+ * the same stream with the same M, k, W, bucketing arrays and workspace, with
+ * nothing writing that workspace in between.  Together they enqueue exactly
+ * what moe_expert_ffn_mxfp4 enqueues and give bit-identical y_slots.
+ * Arguments, requirements and errors are those of moe_expert_ffn_mxfp4. */
+int moe_ffn_gateup_mxfp4(const void *x, moe_dtype x_dtype, int32_t M, int32_t k, const moe_experts *W,
+                         const int32_t *offsets, const int32_t *perm, const int32_t *active,
+                         const int32_t *n_active, void *workspace, size_t workspace_bytes, void *stream);
+int moe_ffn_down_mxfp4(int32_t M, int32_t k, const moe_experts *W, const int32_t *offsets, const int32_t *perm,
+                       const int32_t *active, const int32_t *n_active, float *y_slots, void *workspace,
+                       size_t workspace_bytes, void *stream);
 
 /* Bytes of workspace moe_expert_ffn_mxfp4 needs for M rows (host-only query;
  * returns 0 for invalid arguments). */

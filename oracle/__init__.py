@@ -29,6 +29,7 @@ def _load():
         P = ctypes.c_void_p
         i32, i64 = ctypes.c_int32, ctypes.c_int64
         sig = {
+            "orc_max_threads": (ctypes.c_int, []),
             "orc_e2m1": (ctypes.c_double, [ctypes.c_int]),
             "orc_e8m0": (ctypes.c_double, [ctypes.c_int]),
             "orc_fp16": (ctypes.c_double, [ctypes.c_uint16]),
@@ -61,6 +62,11 @@ def _check(rc: int, what: str):
 
 
 # --------------------------------------------------------------------------- formats
+def max_threads() -> int:
+    """Threads the oracle's parallel loops run on."""
+    return int(_load().orc_max_threads())
+
+
 def e2m1(code: int) -> float:
     """E2M1 element value (OCP MX v1.0 FP4), as used for the MXFP4 experts."""
     return _load().orc_e2m1(int(code))

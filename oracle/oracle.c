@@ -36,8 +36,21 @@
 #include <stdlib.h>
 #include <string.h>
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
 #define ORC_OK 0
 #define ORC_EINVAL (-1)
+
+/* Threads a parallel region of this library uses (1 without OpenMP). */
+int orc_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
 
 /* ------------------------------------------------------------------------ */
 /* Element formats                                                          */

@@ -21,8 +21,8 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP = 0, -1, -2, -3
 MOE_F32, MOE_BF16 = 0, 1
 
 # names exported by include/moe.h
-ABI_FUNCTIONS = ("moe_route", "moe_bucket", "moe_expert_ffn_mxfp4", "moe_workspace_bytes", "moe_combine",
-                 "q8_0_matmul", "moe_status_str")
+ABI_FUNCTIONS = ("moe_route", "moe_bucket", "moe_expert_ffn_mxfp4", "moe_ffn_gateup_mxfp4", "moe_ffn_down_mxfp4",
+                 "moe_workspace_bytes", "moe_combine", "q8_0_matmul", "moe_status_str")
 
 
 class MoeError(RuntimeError):
@@ -48,6 +48,8 @@ def _load() -> ctypes.CDLL:
         "moe_route": (ctypes.c_int, [P, ctypes.c_int, P, P, i32, i32, i32, i32, P, P, P]),
         "moe_bucket": (ctypes.c_int, [P, i32, i32, i32, i32, P, P, P, P, P, P]),
         "moe_expert_ffn_mxfp4": (ctypes.c_int, [P, ctypes.c_int, i32, i32, EP, P, P, P, P, P, P, sz, P]),
+        "moe_ffn_gateup_mxfp4": (ctypes.c_int, [P, ctypes.c_int, i32, i32, EP, P, P, P, P, P, sz, P]),
+        "moe_ffn_down_mxfp4": (ctypes.c_int, [i32, i32, EP, P, P, P, P, P, P, sz, P]),
         "moe_workspace_bytes": (sz, [i32, i32, EP]),
         "moe_combine": (ctypes.c_int, [P, P, i32, i32, i32, i32, P, P]),
         "q8_0_matmul": (ctypes.c_int, [P, i32, i32, P, P, i32, P, P]),
@@ -174,6 +176,33 @@ def moe_expert_ffn_mxfp4(x, k, experts: Experts, offsets, perm, active, n_active
                                    _ptr(active), _ptr(n_active), _ptr(y_slots), _ptr(workspace), workspace.numel(),
                                    _stream(stream))
     _check("moe_expert_ffn_mxfp4", rc)
+
+
+def moe_ffn_gateup_mxfp4(x, k, experts: Experts, offsets, perm, active, n_active, workspace, stream=None):
+    """First FFN stage: h = silu(W_gate x) * (W_up x) per slot, into the workspace."""
+    M = x.shape[0]
+    if x.shape[1] != experts.d:
+        raise ValueError("x must be [M x d]")
+    if workspace.dtype != torch.uint8:
+        raise ValueError("workspace must be a uint8 tensor")
+    s = experts.c_struct()
+    rc = _lib.moe_ffn_gateup_mxfp4(_ptr(x), _x_dtype(x), M, k, ctypes.byref(s), _ptr(offsets), _ptr(perm),
+                                   _ptr(active), _ptr(n_active), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check("moe_ffn_gateup_mxfp4", rc)
+
+
+def moe_ffn_down_mxfp4(M, k, experts: Experts, offsets, perm, active, n_active, y_slots, workspace, stream=None):
+    """Second FFN stage: y_slots = W_down h, h read from the workspace the
+    gate/up stage filled for the same arguments."""
+    S = experts.n_shared
+    if y_slots.dtype != torch.float32 or tuple(y_slots.shape) != (M * (k + S), experts.d):
+        raise ValueError("y_slots must be float32 [M*(k+S) x d]")
+    if workspace.dtype != torch.uint8:
+        raise ValueError("workspace must be a uint8 tensor")
+    s = experts.c_struct()
+    rc = _lib.moe_ffn_down_mxfp4(M, k, ctypes.byref(s), _ptr(offsets), _ptr(perm), _ptr(active), _ptr(n_active),
+                                 _ptr(y_slots), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check("moe_ffn_down_mxfp4", rc)
 
 
 def moe_combine(y_slots, topk_w, k, n_shared, out, stream=None):

@@ -24,6 +24,38 @@ inline bool experts_ok(const moe_experts *W) {
   return true;
 }
 
+// Argument checks shared by the expert-FFN entry points (the full call and
+// its two stages).  need_x / need_y say whether that entry point takes x / y.
+int ffn_check(const void *x, moe_dtype x_dtype, bool need_x, int32_t M, int32_t k, const moe_experts *W,
+              const int32_t *offsets, const int32_t *perm, const int32_t *active, const int32_t *n_active,
+              const float *y_slots, bool need_y, const void *workspace, size_t workspace_bytes) {
+  if (M < 0 || k < 1 || !experts_ok(W)) return MOE_EINVAL;
+  if (need_x) {
+    if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_EINVAL;
+    if (!x || reinterpret_cast<uintptr_t>(x) % 16) return MOE_EINVAL;
+  }
+  if (need_y && (!y_slots || reinterpret_cast<uintptr_t>(y_slots) % 16)) return MOE_EINVAL;
+  if (!offsets || !perm || !active || !n_active || !workspace) return MOE_EINVAL;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return MOE_EINVAL;
+  if (k > W->n_routed) return MOE_EINVAL;
+  if (W->n_routed + W->n_shared > kMaxExperts) return MOE_EUNSUPPORTED;
+  if (!moe::ffn_shape_ok(M, k, W->n_shared, W->d, W->f, W->stride)) return MOE_EUNSUPPORTED;
+  if ((int64_t)M * (k + W->n_shared) > INT32_MAX / 2) return MOE_EUNSUPPORTED;
+  if (M == 0) return MOE_OK;
+  if (workspace_bytes < moe::ffn_workspace_bytes(M, k, W->n_shared, W->d, W->f, W->n_routed + W->n_shared))
+    return MOE_EINVAL;
+  return MOE_OK;
+}
+
+int run_ffn(const void *x, moe_dtype x_dtype, int32_t M, int32_t k, const moe_experts *W, const int32_t *offsets,
+            const int32_t *perm, const int32_t *active, const int32_t *n_active, float *y_slots, void *workspace,
+            int stages, void *stream) {
+  return moe::ffn_launch(x, x_dtype == MOE_BF16, M, k, W->base, W->stride, W->d, W->f, W->n_routed, W->n_shared,
+                         offsets, perm, active, n_active, y_slots, workspace, stages, as_stream(stream)) == 0
+             ? MOE_OK
+             : MOE_EHIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -73,22 +105,31 @@ int moe_expert_ffn_mxfp4(const void *x, moe_dtype x_dtype, int32_t M, int32_t k,
                          const int32_t *offsets, const int32_t *perm, const int32_t *active,
                          const int32_t *n_active, float *y_slots, void *workspace, size_t workspace_bytes,
                          void *stream) {
-  if (M < 0 || k < 1 || !experts_ok(W)) return MOE_EINVAL;
-  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_EINVAL;
-  if (!x || !offsets || !perm || !active || !n_active || !y_slots || !workspace) return MOE_EINVAL;
-  if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(y_slots) % 16 ||
-      reinterpret_cast<uintptr_t>(workspace) % 256)
-    return MOE_EINVAL;
-  if (k > W->n_routed) return MOE_EINVAL;
-  if (W->n_routed + W->n_shared > kMaxExperts) return MOE_EUNSUPPORTED;
-  if (!moe::ffn_shape_ok(M, k, W->n_shared, W->d, W->f, W->stride)) return MOE_EUNSUPPORTED;
-  if ((int64_t)M * (k + W->n_shared) > INT32_MAX / 2) return MOE_EUNSUPPORTED;
-  if (M == 0) return MOE_OK;
-  if (workspace_bytes < moe::ffn_workspace_bytes(M, k, W->n_shared, W->d, W->f, W->n_routed + W->n_shared))
-    return MOE_EINVAL;
-  return status_of(moe::ffn_launch(x, x_dtype == MOE_BF16, M, k, W->base, W->stride, W->d, W->f, W->n_routed,
-                                   W->n_shared, offsets, perm, active, n_active, y_slots, workspace,
-                                   as_stream(stream)));
+  const int rc = ffn_check(x, x_dtype, true, M, k, W, offsets, perm, active, n_active, y_slots, true, workspace,
+                           workspace_bytes);
+  if (rc != MOE_OK || M == 0) return rc;
+  return run_ffn(x, x_dtype, M, k, W, offsets, perm, active, n_active, y_slots, workspace,
+                 moe::kStageGateUp | moe::kStageDown, stream);
+}
+
+int moe_ffn_gateup_mxfp4(const void *x, moe_dtype x_dtype, int32_t M, int32_t k, const moe_experts *W,
+                         const int32_t *offsets, const int32_t *perm, const int32_t *active,
+                         const int32_t *n_active, void *workspace, size_t workspace_bytes, void *stream) {
+  const int rc = ffn_check(x, x_dtype, true, M, k, W, offsets, perm, active, n_active, nullptr, false, workspace,
+                           workspace_bytes);
+  if (rc != MOE_OK || M == 0) return rc;
+  return run_ffn(x, x_dtype, M, k, W, offsets, perm, active, n_active, nullptr, workspace, moe::kStageGateUp,
+                 stream);
+}
+
+int moe_ffn_down_mxfp4(int32_t M, int32_t k, const moe_experts *W, const int32_t *offsets, const int32_t *perm,
+                       const int32_t *active, const int32_t *n_active, float *y_slots, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+  const int rc = ffn_check(nullptr, MOE_BF16, false, M, k, W, offsets, perm, active, n_active, y_slots, true,
+                           workspace, workspace_bytes);
+  if (rc != MOE_OK || M == 0) return rc;
+  return run_ffn(nullptr, MOE_BF16, M, k, W, offsets, perm, active, n_active, y_slots, workspace, moe::kStageDown,
+                 stream);
 }
 
 int moe_combine(const float *y_slots, const float *topk_w, int32_t M, int32_t k, int32_t n_shared, int32_t d,

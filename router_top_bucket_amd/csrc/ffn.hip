@@ -607,33 +607,35 @@ bool ffn_shape_ok(int64_t M, int k, int S, int d, int f, int64_t stride) {
 }
 
 template <int XBF16, int TPW, int GW, int PF, int MAXC, bool SX4, bool BRES>
-static void launch_gateup(const void *x, int d, int f, int kps, int T, const uint8_t *experts, int64_t stride,
-                          const GroupSrc &src, const int32_t *perm, int64_t maxg, uint16_t *h_ws, hipStream_t stream) {
+static int launch_gateup(const void *x, int d, int f, int kps, int T, const uint8_t *experts, int64_t stride,
+                         const GroupSrc &src, const int32_t *perm, int64_t maxg, uint16_t *h_ws, hipStream_t stream) {
   constexpr int ROWS = GW * TPW * 16;
   const int n_ftiles = (f + ROWS - 1) / ROWS;
   const size_t smem = gateup_smem(d, PF, XBF16 ? 1 : 3, MAXC, BRES);
   static const bool lds_ok =
       allow_lds(reinterpret_cast<const void *>(&ffn_gateup_kernel<XBF16, TPW, GW, PF, MAXC, SX4, BRES>));
-  if (!lds_ok) return;
+  if (!lds_ok) return -3;
   hipLaunchKernelGGL((ffn_gateup_kernel<XBF16, TPW, GW, PF, MAXC, SX4, BRES>), dim3((unsigned)(maxg * n_ftiles)), dim3(GW * 64),
                      smem, stream, x, d, f, kps, T, experts, stride, src, perm, n_ftiles, h_ws);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
 template <int TPW, int DW, int PF, int MAXC, bool SX4, bool BRES>
-static void launch_down(int d, int f, int T, const uint8_t *experts, int64_t stride, const GroupSrc &src,
-                        const int32_t *perm, int64_t maxg, const uint16_t *h_ws, float *y, hipStream_t stream) {
+static int launch_down(int d, int f, int T, const uint8_t *experts, int64_t stride, const GroupSrc &src,
+                       const int32_t *perm, int64_t maxg, const uint16_t *h_ws, float *y, hipStream_t stream) {
   constexpr int ROWS = DW * TPW * 16;
   const int n_dtiles = (d + ROWS - 1) / ROWS;
   const size_t smem = down_smem(f, PF, MAXC, BRES);
   static const bool lds_ok = allow_lds(reinterpret_cast<const void *>(&ffn_down_kernel<TPW, DW, PF, MAXC, SX4, BRES>));
-  if (!lds_ok) return;
+  if (!lds_ok) return -3;
   hipLaunchKernelGGL((ffn_down_kernel<TPW, DW, PF, MAXC, SX4, BRES>), dim3((unsigned)(maxg * n_dtiles)), dim3(DW * 64), smem,
                      stream, d, f, T, experts, stride, src, perm, n_dtiles, h_ws, y);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
 int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *experts, int64_t stride, int d, int f,
                int n_routed, int n_shared, const int32_t *offsets, const int32_t *perm, const int32_t *active,
-               const int32_t *n_active, float *y, void *workspace, hipStream_t stream) {
+               const int32_t *n_active, float *y, void *workspace, int stages, hipStream_t stream) {
   const int S = n_shared;
   const int kps = k + S;
   const int64_t T = M * kps;
@@ -648,8 +650,12 @@ int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *exper
 
   GroupSrc src{offsets, active, n_active, nullptr, nullptr};
   if (M > kGroupCols) {
-    hipLaunchKernelGGL(plan_groups_kernel, dim3(1), dim3(1024), 0, stream, offsets, active, n_active, groups,
-                       n_groups);
+    // the group plan lives in the workspace and serves both stages
+    if (stages & kStageGateUp) {
+      hipLaunchKernelGGL(plan_groups_kernel, dim3(1), dim3(1024), 0, stream, offsets, active, n_active, groups,
+                         n_groups);
+      if (hipGetLastError() != hipSuccess) return -3;
+    }
     src.groups = groups;
     src.n_groups = n_groups;
   }
@@ -657,35 +663,39 @@ int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *exper
   // many B columns are staged (a group never has more slots than M), never
   // the order of any reduction: every choice gives bit-identical results.
   const bool gsx4 = (d / 32) % 16 == 0, dsx4 = (f / 32) % 16 == 0;
+  const int T_ = (int)T;
 #define MOE_GU(XB, T, G, P, C, R)                                                                                  \
-  (gsx4 ? launch_gateup<XB, T, G, P, C, true, R>(x, d, f, kps, (int)T_, experts, stride, src, perm, maxg, h_ws, stream) \
-        : launch_gateup<XB, T, G, P, C, false, R>(x, d, f, kps, (int)T_, experts, stride, src, perm, maxg, h_ws, stream))
+  (gsx4 ? launch_gateup<XB, T, G, P, C, true, R>(x, d, f, kps, T_, experts, stride, src, perm, maxg, h_ws, stream) \
+        : launch_gateup<XB, T, G, P, C, false, R>(x, d, f, kps, T_, experts, stride, src, perm, maxg, h_ws, stream))
 #define MOE_DN(T, D, P, C, R)                                                                                   \
-  (dsx4 ? launch_down<T, D, P, C, true, R>(d, f, (int)T_, experts, stride, src, perm, maxg, h_ws, y, stream) \
-        : launch_down<T, D, P, C, false, R>(d, f, (int)T_, experts, stride, src, perm, maxg, h_ws, y, stream))
-  const int64_t T_ = T;
+  (dsx4 ? launch_down<T, D, P, C, true, R>(d, f, T_, experts, stride, src, perm, maxg, h_ws, y, stream) \
+        : launch_down<T, D, P, C, false, R>(d, f, T_, experts, stride, src, perm, maxg, h_ws, y, stream))
   // few rows: each group's B operand (x or h) stays resident in LDS for the
   // whole reduction; more rows: B is staged step by step through a ring
-  const bool bres_fits = gateup_smem(d, 4, x_bf16 ? 1 : 3, 4, true) <= (size_t)kMaxLds &&
-                         down_smem(f, 4, 4, true) <= (size_t)kMaxLds;
-  if (x_bf16) {
-    if (M == 1 && bres_fits) MOE_GU(1, 1, 2, 4, 1, true);
-    else if (M <= 4 && bres_fits) MOE_GU(1, 1, 2, 4, 4, true);
-    else if (M <= 4) MOE_GU(1, 1, 4, 4, 4, false);
-    else MOE_GU(1, 1, 4, 4, 16, false);
-  } else {
-    if (M <= 4 && bres_fits) MOE_GU(0, 1, 2, 4, 4, true);
-    else MOE_GU(0, 1, 4, 4, 16, false);
+  int rc = 0;
+  if (stages & kStageGateUp) {
+    const bool gres = gateup_smem(d, 4, x_bf16 ? 1 : 3, 4, true) <= (size_t)kMaxLds;
+    if (x_bf16) {
+      if (M == 1 && gres) rc = MOE_GU(1, 1, 2, 4, 1, true);
+      else if (M <= 4 && gres) rc = MOE_GU(1, 1, 2, 4, 4, true);
+      else if (M <= 4) rc = MOE_GU(1, 1, 4, 4, 4, false);
+      else rc = MOE_GU(1, 1, 4, 4, 16, false);
+    } else {
+      if (M <= 4 && gres) rc = MOE_GU(0, 1, 2, 4, 4, true);
+      else rc = MOE_GU(0, 1, 4, 4, 16, false);
+    }
+    if (rc) return rc;
   }
-  if (hipGetLastError() != hipSuccess) return -3;
-  if (M == 1 && bres_fits) MOE_DN(2, 8, 4, 1, true);
-  else if (M <= 4 && bres_fits) MOE_DN(2, 8, 4, 4, true);
-  else if (M <= 4) MOE_DN(2, 8, 4, 4, false);
-  else MOE_DN(2, 8, 4, 16, false);
+  if (stages & kStageDown) {
+    const bool dres = down_smem(f, 4, 4, true) <= (size_t)kMaxLds;
+    if (M == 1 && dres) rc = MOE_DN(2, 8, 4, 1, true);
+    else if (M <= 4 && dres) rc = MOE_DN(2, 8, 4, 4, true);
+    else if (M <= 4) rc = MOE_DN(2, 8, 4, 4, false);
+    else rc = MOE_DN(2, 8, 4, 16, false);
+  }
 #undef MOE_GU
 #undef MOE_DN
-  if (hipGetLastError() != hipSuccess) return -3;
-  return 0;
+  return rc;
 }
 
 }  // namespace moe

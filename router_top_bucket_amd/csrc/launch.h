@@ -16,9 +16,12 @@ int bucket_launch(const int32_t *ids, int M, int k, int E, int S, int32_t *offse
 int64_t ffn_max_groups(int64_t M, int k, int S, int n_experts);
 size_t ffn_workspace_bytes(int64_t M, int k, int S, int d, int f, int n_experts);
 bool ffn_shape_ok(int64_t M, int k, int S, int d, int f, int64_t stride);
+// stages: kStageGateUp (group plan + gate/up + SwiGLU into the workspace),
+// kStageDown (down projection from the workspace into y), or both.
+constexpr int kStageGateUp = 1, kStageDown = 2;
 int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *experts, int64_t stride, int d, int f,
                int n_routed, int n_shared, const int32_t *offsets, const int32_t *perm, const int32_t *active,
-               const int32_t *n_active, float *y, void *workspace, hipStream_t stream);
+               const int32_t *n_active, float *y, void *workspace, int stages, hipStream_t stream);
 
 int combine_launch(const float *y, const float *w, int M, int k, int S, int d, float *out, hipStream_t stream);
 

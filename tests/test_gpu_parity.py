@@ -208,6 +208,28 @@ def test_ffn_ragged_parity(shape, M):
     _compare_layer(res, ref, f"{shape.name} M={M}", shape.k, shape.n_shared)
 
 
+def _stages_equal_full(moe, ex, k, xd, layer, res):
+    """moe_ffn_gateup_mxfp4 + moe_ffn_down_mxfp4 == moe_expert_ffn_mxfp4, bit for bit."""
+    y_full = _host(res["y_slots"]).copy()
+    res["y_slots"].fill_(float("nan"))
+    M = xd.shape[0]
+    moe.moe_ffn_gateup_mxfp4(xd, k, ex, res["offsets"], res["perm"], res["active"], res["n_active"], layer.workspace)
+    moe.moe_ffn_down_mxfp4(M, k, ex, res["offsets"], res["perm"], res["active"], res["n_active"], res["y_slots"],
+                           layer.workspace)
+    assert np.array_equal(_host(res["y_slots"]).view(np.uint8), y_full.view(np.uint8))
+
+
+@pytest.mark.parametrize("shape", RAGGED[1:3], ids=lambda s: s.name)
+@pytest.mark.parametrize("M", [1, 4, 16, 40])
+def test_ffn_stages_equal_full_call(shape, M):
+    moe = _moe()
+    ex, _ = _small_layer(shape, 11)
+    wr = synth.router_weight(shape, 11)
+    xd = _x_dev(shape, synth.rows_x(shape, 12, M))
+    layer = moe.MoELayer(ex, shape.k, M, w_router=_dev(wr))
+    _stages_equal_full(moe, ex, shape.k, xd, layer, layer.forward(xd))
+
+
 # ----------------------------------------------------------------------------- Kimi decode
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_kimi_one_row_parity(kimi_layer, seed):
@@ -278,6 +300,52 @@ def test_kimi_expert_order_independence(kimi_layer):
         moe.moe_expert_ffn_mxfp4(x, shp.k, L["experts"], res["offsets"], res["perm"], act, res["n_active"],
                                  res["y_slots"], layer.workspace)
         assert np.array_equal(_host(res["y_slots"]).view(np.uint8), y_ref.view(np.uint8)), order
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_kimi_stages_equal_full_call(kimi_layer, M):
+    moe = _moe()
+    L = kimi_layer
+    shp = L["shape"]
+    xd = _x_dev(shp, synth.block_x(shp, 4, M))
+    layer = moe.MoELayer(L["experts"], shp.k, M, w_router=L["wr_dev"])
+    _stages_equal_full(moe, L["experts"], shp.k, xd, layer, layer.forward(xd))
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_kimi_layer_graph_replay(kimi_layer, M):
+    """The whole layer pass captured in a HIP graph: every replay, with eager
+    work and synchronisation in between, equals the eager pass bit for bit."""
+    moe = _moe()
+    L = kimi_layer
+    shp = L["shape"]
+    xs = [_x_dev(shp, synth.block_x(shp, 20 + i, M)) for i in range(2)]
+    layer = moe.MoELayer(L["experts"], shp.k, M, w_router=L["wr_dev"])
+    eager = []
+    for x in xs:
+        r = layer.forward(x)
+        eager.append((_host(r["out"]).copy(), _host(r["y_slots"]).copy(), _host(r["topk_ids"]).copy()))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    for x in xs:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            layer.forward(x)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for i, g in enumerate(graphs):
+            layer.out.fill_(float("nan"))
+            layer.y_slots.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            out, y, ids = eager[i]
+            assert np.array_equal(_host(layer.out[:M]).view(np.uint8), out.view(np.uint8)), (rep, i, "out")
+            assert np.array_equal(_host(layer.y_slots[:len(y)]).view(np.uint8), y.view(np.uint8)), (rep, i, "y")
+            assert np.array_equal(_host(layer.topk_ids[:M]), ids), (rep, i, "ids")
+            layer.forward(xs[1 - i])  # eager work between replays
+            torch.cuda.synchronize()
 
 
 # ----------------------------------------------------------------------------- prefill
