@@ -117,46 +117,143 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(const int32_t *__res
   if (tid == 0) *dev_error = err;
 }
 
+// Small batches (T <= 1024 slots, M <= 64 rows): one thread per slot keeps
+// its expert in a register, so the ids are read once; the counts and the
+// 64-row occupancy masks are built in the same pass, and the arithmetic of
+// every output is the general kernel's.
+__global__ __launch_bounds__(BK_THREADS) void bucket_small_kernel(const int32_t *__restrict__ ids, int M, int k, int E,
+                                                                  int S, int32_t *__restrict__ offsets,
+                                                                  int32_t *__restrict__ perm,
+                                                                  int32_t *__restrict__ active,
+                                                                  int32_t *__restrict__ n_active,
+                                                                  int32_t *__restrict__ dev_error) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int NE = E + S;
+  unsigned long long *mask = (unsigned long long *)smem;  // [NE]
+  int32_t *base = (int32_t *)(mask + NE);                 // [NE] counts, then bases
+  __shared__ int32_t wave_sum[16][2];
+  __shared__ int32_t err;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int kps = k + S;
+  const int T = M * kps;
+  const int e_mine = tid < T ? slot_expert(ids, tid, k, kps, E) : -2;
+  for (int e = tid; e < NE; e += BK_THREADS) {
+    base[e] = 0;
+    mask[e] = 0ull;
+  }
+  if (tid == 0) err = 0;
+  __syncthreads();
+  const unsigned long long bit = 1ull << (tid < T ? tid / kps : 0);
+  if (e_mine == -1) err = 1;
+  if (e_mine >= 0) {
+    atomicAdd(&base[e_mine], 1);
+    const unsigned long long old = atomicOr(&mask[e_mine], bit);
+    if (old & bit) err = 1;  // a row names the same expert twice
+  }
+  __syncthreads();
+  // exclusive scans of the counts (offsets) and of the nonempty flags (active)
+  const int per = (NE + BK_THREADS - 1) / BK_THREADS;
+  const int e_beg = tid * per;
+  int c_loc = 0, a_loc = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = e_beg + i;
+    if (e < NE) { c_loc += base[e]; a_loc += base[e] > 0; }
+  }
+  int cv = c_loc, av = a_loc;
+  for (int o = 1; o < 64; o <<= 1) {
+    const int tc = __shfl_up(cv, o, 64), ta = __shfl_up(av, o, 64);
+    if (lane >= o) { cv += tc; av += ta; }
+  }
+  if (lane == 63) { wave_sum[wv][0] = cv; wave_sum[wv][1] = av; }
+  __syncthreads();
+  int c_ex = cv - c_loc, a_ex = av - a_loc, c_tot = 0, a_tot = 0;
+  for (int w2 = 0; w2 < BK_THREADS / 64; ++w2) {
+    if (w2 < wv) { c_ex += wave_sum[w2][0]; a_ex += wave_sum[w2][1]; }
+    c_tot += wave_sum[w2][0];
+    a_tot += wave_sum[w2][1];
+  }
+  __syncthreads();  // every count is read before it becomes a base
+  for (int i = 0; i < per; ++i) {
+    const int e = e_beg + i;
+    if (e < NE) {
+      const int c = base[e];
+      offsets[e] = c_ex;
+      if (c > 0) active[a_ex++] = e;
+      base[e] = c_ex;
+      c_ex += c;
+    }
+  }
+  if (tid == 0) {
+    offsets[NE] = c_tot;
+    *n_active = a_tot;
+  }
+  __syncthreads();
+  if (e_mine >= 0) {
+    const int rank = base[e_mine] + __popcll(mask[e_mine] & (bit - 1ull));
+    if (rank < T) perm[rank] = tid;
+  }
+  __syncthreads();
+  if (tid == 0) *dev_error = err;
+}
+
 int bucket_launch(const int32_t *ids, int M, int k, int E, int S, int32_t *offsets, int32_t *perm, int32_t *active,
                   int32_t *n_active, int32_t *dev_error, hipStream_t stream) {
   const int NE = E + S;
   const size_t smem = (size_t)NE * (sizeof(unsigned long long) + sizeof(int32_t));
-  hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(BK_THREADS), smem, stream, ids, M, k, E, S, offsets, perm, active,
-                     n_active, dev_error);
+  if ((int64_t)M * (k + S) <= BK_THREADS && M <= 64)
+    hipLaunchKernelGGL(bucket_small_kernel, dim3(1), dim3(BK_THREADS), smem, stream, ids, M, k, E, S, offsets, perm,
+                       active, n_active, dev_error);
+  else
+    hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(BK_THREADS), smem, stream, ids, M, k, E, S, offsets, perm, active,
+                       n_active, dev_error);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
 // ------------------------------------------------------------------ combine
 // out[m,r] = sum_{j<k} w[m,j] y[m*(k+S)+j, r] + sum_{s<S} y[m*(k+S)+k+s, r],
-// fp32, in slot order.  One thread per 4 consecutive r.
-__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y, const float *__restrict__ w, int M,
-                                                      int k, int S, int d, float *__restrict__ out) {
+// fp32, in slot order.  One thread per 4 consecutive r; the slot rows are
+// loaded CH at a time before their (ordered) accumulation.
+constexpr int CB_THREADS = 64;
+__global__ __launch_bounds__(CB_THREADS) void combine_kernel(const float *__restrict__ y, const float *__restrict__ w,
+                                                             int M, int k, int S, int d, float *__restrict__ out) {
+  constexpr int CH = 9;
   const int d4 = d >> 2;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t idx = (int64_t)blockIdx.x * CB_THREADS + threadIdx.x;
   if (idx >= (int64_t)M * d4) return;
   const int64_t m = idx / d4;
   const int c = (int)(idx - m * d4) * 4;
   const int kps = k + S;
   const float *ym = y + m * kps * (int64_t)d + c;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const float wj = w[m * k + j];
-    const f32x4 v = *(const f32x4 *)(ym + (int64_t)j * d);
+  for (int j0 = 0; j0 < kps; j0 += CH) {
+    f32x4 v[CH];
+    float wj[CH];
+    // clamped (always valid) indices: every load is issued, none waits on another
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(wj, v[i], acc[i]);
-  }
-  for (int s = 0; s < S; ++s) {
-    const f32x4 v = *(const f32x4 *)(ym + (int64_t)(k + s) * d);
+    for (int u = 0; u < CH; ++u) {
+      const int j = j0 + u;
+      v[u] = *(const f32x4 *)(ym + (int64_t)(j < kps ? j : kps - 1) * d);
+      wj[u] = w[m * k + (j < k ? j : k - 1)];
+    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] += v[i];
+    for (int u = 0; u < CH; ++u) {
+      const int j = j0 + u;
+      if (j < k) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(wj[u], v[u][i], acc[i]);
+      } else if (j < kps) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += v[u][i];
+      }
+    }
   }
   *(f32x4 *)(out + m * (int64_t)d + c) = acc;
 }
 
 int combine_launch(const float *y, const float *w, int M, int k, int S, int d, float *out, hipStream_t stream) {
   const int64_t n = (int64_t)M * (d / 4);
-  const int64_t grid = (n + 255) / 256;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)grid), dim3(256), 0, stream, y, w, M, k, S, d, out);
+  const int64_t grid = (n + CB_THREADS - 1) / CB_THREADS;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)grid), dim3(CB_THREADS), 0, stream, y, w, M, k, S, d, out);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

@@ -80,6 +80,8 @@ int moe_route(const void *x, moe_dtype x_dtype, const float *w_router, float *lo
     if (reinterpret_cast<uintptr_t>(w_router) % 16 || reinterpret_cast<uintptr_t>(x) % 16) return MOE_EINVAL;
   }
   if (E > kMaxExperts || k > 64) return MOE_EUNSUPPORTED;
+  // router operands are addressed with 32-bit buffer offsets below 2^30
+  if (w_router && ((int64_t)E * d * 4 >= (1 << 30) || (int64_t)M * d * 4 >= (1 << 30))) return MOE_EUNSUPPORTED;
   if (M == 0) return MOE_OK;
   return status_of(moe::route_launch(x, x_dtype == MOE_BF16, w_router, logits, M, d, E, k, topk_ids, topk_w,
                                      as_stream(stream)));

@@ -80,6 +80,9 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+__device__ __forceinline__ u32x2 buf_load8(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
 __device__ __forceinline__ uint32_t buf_load1(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
 }
@@ -87,6 +90,20 @@ __device__ __forceinline__ uint32_t buf_load4(rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 __device__ __forceinline__ uint32_t sel_off(bool ok, uint32_t off) { return ok ? off : kOOB; }
+
+// s_waitcnt operand (gfx9 encoding) that waits for every vector-memory load
+// of the wave and nothing else: vmcnt 0, expcnt 7, lgkmcnt 15.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Workgroup barrier for handing LDS data between waves: waits for this wave's
+// LDS operations only.  __syncthreads() is a full workgroup fence and would
+// also wait for every global load the wave has in flight, draining any
+// prefetch ring at each barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // ---- wave reductions without LDS: DPP inside each 16-lane row, then the four
 // row results read as scalars and combined in row order.  Every lane of a

@@ -99,112 +99,178 @@ __global__ __launch_bounds__(1024) void plan_groups_kernel(const int32_t *offset
 
 
 // ------------------------------------------------------------------ B staging
-// The B operand of a step (16 columns x 128 K, in NP bf16 parts) is loaded
-// once per workgroup into an LDS ring slot and read by every wave from
-// there, instead of every wave loading all of it.  Only the first MAXC
-// columns are staged (no group has more slots than rows in the launch); the
-// other rows of every slot are zeroed once.  A slot row is 256 bytes of data
-// padded to 272 so the 16-byte fragment reads of 16 columns hit distinct
-// banks.
+// Ring mode: the B operand of a step (a 128-element segment of every B row)
+// is loaded once per workgroup into an LDS ring slot and read by every wave
+// from there.  A slot row is 256 bytes of data padded to 272, so the 16-byte
+// fragment reads of 16 rows hit distinct banks.
 constexpr int kBRow = 272;
 
-template <int NP>
-__device__ __forceinline__ uint32_t bslot_off(int slot, int part, int col) {
-  return (uint32_t)(((slot * NP + part) * 16 + col) * kBRow);
+__device__ __forceinline__ bf16x8 lds_b_fragment(const uint8_t *lds, uint32_t off) {
+  return bits_to_bf16x8(*(const u32x4 *)(lds + off));
 }
 
-__device__ __forceinline__ bf16x8 lds_b_fragment(const uint8_t *bring, uint32_t off) {
-  return bits_to_bf16x8(*(const u32x4 *)(bring + off));
-}
-
-template <int NP, int PF>
-__device__ __forceinline__ void zero_b_rows(uint8_t *bring, int maxc, int tid, int nthreads) {
-  const int rows = PF * NP * (16 - maxc);
-  for (int idx = tid; idx < rows * (kBRow / 16); idx += nthreads) {
-    const int rr = idx / (kBRow / 16), cc = idx - rr * (kBRow / 16);
-    const int slot_part = rr / (16 - maxc), col = maxc + rr % (16 - maxc);
-    *(u32x4 *)(bring + (slot_part * 16 + col) * kBRow + cc * 16) = u32x4{0u, 0u, 0u, 0u};
-  }
-}
-
-// Resident B (few columns): the group's whole B operand, MAXC columns of K
-// elements in NP parts, staged once before the main loop.  Row MAXC of each
-// part is zero and serves every lane whose column is past MAXC.  Each row is
-// K*2 bytes followed by an 80-byte zero tail: lanes whose block lies past K
-// read their fragments from the tail, and the row stride spreads the
-// 16-byte reads of 8 rows over distinct banks.
+// Resident mode (few rows): every B row for the whole reduction, staged once
+// before the main loop.  Each row is K*2 bytes followed by an 80-byte zero
+// tail: lanes whose 32-element block lies past K read their fragments from
+// the tail, and the stride spreads the 16-byte reads of 8 rows over distinct
+// banks.
 constexpr int kBresTail = 80;
 __host__ __device__ __forceinline__ uint32_t bres_row_bytes(int K) { return (uint32_t)(K * 2 + kBresTail); }
-__host__ __device__ __forceinline__ size_t bres_bytes(int K, int maxc, int np) {
-  return (size_t)np * (maxc + 1) * bres_row_bytes(K);
+
+// Epilogue exchange areas follow the B area in LDS, 16-byte aligned, then a
+// small dummy area: a staging load whose piece lies past the data is still
+// stored, there, so that every load is consumed on every path.  (A load left
+// unconsumed on some path makes the compiler assume it may still be pending
+// when the main loop starts, and wait for all loads in flight at every
+// iteration, which drains the prefetch ring.)
+__host__ __device__ __forceinline__ size_t lds_align16(size_t v) { return (v + 15) & ~(size_t)15; }
+
+// Scale rows staged in LDS: a row's K/32 E8M0 bytes followed by a zero tail
+// that the steps past K read (lanes of blocks past the end, padded steps).
+constexpr int kScTail = 48;
+__host__ __device__ __forceinline__ int sc_pitch(int K) { return (int)lds_align16((size_t)(K / 32 + kScTail)); }
+
+// Gate/up LDS: the scale rows of both matrices (2*ROWS), B (resident: NP*MAXC
+// rows; ring: PF slots of NP*16 rows), the W_up tiles (ROWS x 17 floats),
+// then the dummy area.
+__host__ __device__ __forceinline__ size_t gateup_b_off(int d, int rows) { return lds_align16((size_t)2 * rows * sc_pitch(d)); }
+__host__ __device__ __forceinline__ size_t gateup_b_bytes(int d, int pf, int np, int maxc, bool bres) {
+  return bres ? (size_t)np * maxc * bres_row_bytes(d) : (size_t)pf * np * 16 * kBRow;
+}
+__host__ __device__ __forceinline__ size_t gateup_e_off(int d, int pf, int np, int maxc, bool bres, int rows) {
+  return lds_align16(gateup_b_off(d, rows) + gateup_b_bytes(d, pf, np, maxc, bres));
+}
+__host__ __device__ __forceinline__ size_t gateup_dummy_off(int d, int pf, int np, int maxc, bool bres, int rows) {
+  return lds_align16(gateup_e_off(d, pf, np, maxc, bres, rows) + (size_t)rows * 17 * sizeof(float));
+}
+__host__ __device__ __forceinline__ size_t gateup_lds_bytes(int d, int pf, int np, int maxc, bool bres, int rows) {
+  return gateup_dummy_off(d, pf, np, maxc, bres, rows) + 16 * 3;
+}
+// Down LDS: the scale rows (ROWS), then B (resident: 3*MAXC rows; ring: PF
+// slots of 3*MAXC rows), whose space the per-(row, column) part sums (ROWS x
+// (3*MAXC + 1) floats) reuse once the main loop is done, then the dummy area.
+__host__ __device__ __forceinline__ size_t down_b_off(int f, int rows) { return lds_align16((size_t)rows * sc_pitch(f)); }
+__host__ __device__ __forceinline__ size_t down_b_bytes(int f, int pf, int maxc, bool bres) {
+  return bres ? (size_t)3 * maxc * bres_row_bytes(f) : (size_t)pf * 3 * maxc * kBRow;
+}
+__host__ __device__ __forceinline__ size_t down_y_off(int f, int pf, int maxc, bool bres, int rows) {
+  return down_b_off(f, rows);
+}
+__host__ __device__ __forceinline__ size_t down_dummy_off(int f, int pf, int maxc, bool bres, int rows) {
+  const size_t b = down_b_bytes(f, pf, maxc, bres), y = (size_t)rows * (3 * maxc + 1) * sizeof(float);
+  return lds_align16(down_b_off(f, rows) + (b > y ? b : y));
+}
+__host__ __device__ __forceinline__ size_t down_lds_bytes(int f, int pf, int maxc, bool bres, int rows) {
+  return down_dummy_off(f, pf, maxc, bres, rows) + 16;
 }
 
 // ------------------------------------------------------------------ scales
-// The E8M0 scale of a lane's 32-element block rides in the load ring with
-// the codes.  With SX4 (rows of scale bytes a multiple of 16 long) one
-// 16-byte load at step s = 4u brings the bytes of steps 4u..4u+3: byte
-// 4*(s%4) + q of it is the scale of lane (r, q) at step s.  Otherwise one byte
-// is loaded per step.  A dead step's scale is forced to 1.0: its codes read
-// as zero, and the bytes past a row may be anything (0xFF would be NaN).
-template <bool SX4, int NT, int PF>
-struct ScaleRing {
-  static_assert(!SX4 || PF % 4 == 0, "16-byte scale loads need a ring of a multiple of 4 steps");
-  uint32_t soff[NT];
-  u32x4 q4[SX4 ? PF / 4 : 1][NT];
-  uint32_t b1[SX4 ? 1 : PF][NT];
-  u32x4 cur[NT];
-
-  // loads for step s into ring slot p (call in step order)
-  __device__ __forceinline__ void issue(rsrc_t r, int s, int p, int nsteps, int smax, int q) {
-    if (SX4) {
-      if ((p & 3) == 0) {
-        const uint32_t ks = s < nsteps ? (uint32_t)(4 * s) : kDead;
+// Every scale byte a workgroup needs is copied into LDS once, before the main
+// loop: the scales of a run of consecutive weight rows are one contiguous span
+// of the scales plane, so the copy is a handful of wide coalesced loads.
+// (Loading them through the ring instead adds a small request per row every
+// few steps, and the streaming loop is bound by the number of requests.)
+// At step s lane (r, q) reads byte 4s + q of its row: the scale of its block.
+//
+// stage_scales: rows [0, nrows) of `lds_sc` (pitch sc_pitch(K)) get the nb =
+// K/32 scale bytes of global weight rows row0.. (scales plane at `plane`);
+// rows at or past `rows_valid` and every tail get zeros.  Loads are issued
+// before stores, and every load is stored (to `dummy` when out of range).
+template <bool W16>
+__device__ __forceinline__ void stage_scales(rsrc_t wr, uint32_t plane, int row0, int rows_valid, int nrows, int K,
+                                             uint8_t *lds_sc, uint32_t dummy_off, uint8_t *lds, int tid, int nth) {
+  const int nb = K >> 5, sp = sc_pitch(K);
+  if (W16) {
+    // nb is a multiple of 16: 16-byte pieces
+    const int per_row = nb >> 4, npieces = nrows * per_row;
+    constexpr int CH = 4;
+    for (int base = 0; base < npieces; base += CH * nth) {
+      u32x4 v[CH];
+      int pr[CH], pc[CH];
 #pragma unroll
-        for (int t = 0; t < NT; ++t) q4[p >> 2][t] = buf_load16(r, soff[t] + ks);
+      for (int c = 0; c < CH; ++c) {
+        const int piece = base + c * nth + tid;
+        pr[c] = piece / per_row;
+        pc[c] = piece - pr[c] * per_row;
+        const bool ok = piece < npieces && pr[c] < rows_valid;
+        v[c] = buf_load16(wr, ok ? plane + (uint32_t)(row0 + pr[c]) * (uint32_t)nb + 16u * pc[c] : kOOB);
       }
-    } else {
-      const uint32_t ks = s < smax ? (uint32_t)(4 * s + q) : kDead;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) b1[p][t] = buf_load1(r, soff[t] + ks);
+      for (int c = 0; c < CH; ++c) {
+        const bool live = base + c * nth + tid < npieces;
+        *(u32x4 *)(live ? lds_sc + pr[c] * sp + 16 * pc[c] : lds + dummy_off) = v[c];
+      }
+    }
+  } else {
+    const int npieces = nrows * nb;
+    constexpr int CH = 8;
+    for (int base = 0; base < npieces; base += CH * nth) {
+      uint32_t v[CH];
+      int pr[CH], pc[CH];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int piece = base + c * nth + tid;
+        pr[c] = piece / nb;
+        pc[c] = piece - pr[c] * nb;
+        const bool ok = piece < npieces && pr[c] < rows_valid;
+        v[c] = buf_load1(wr, ok ? plane + (uint32_t)(row0 + pr[c]) * (uint32_t)nb + (uint32_t)pc[c] : kOOB);
+      }
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const bool live = base + c * nth + tid < npieces;
+        *(live ? lds_sc + pr[c] * sp + pc[c] : lds + dummy_off) = (uint8_t)v[c];
+      }
     }
   }
-  // scale of tile t at step s (slot p); call for every t before issue() refills slot p
-  __device__ __forceinline__ float get(int s, int p, int t, int smax, int q) {
-    uint32_t b;
-    if (SX4) {
-      if ((p & 3) == 0) cur[t] = q4[p >> 2][t];
-      b = (cur[t][p & 3] >> (8 * q)) & 0xFFu;
+  // zero tails: bytes [nb, sp) of every row
+  const int tail16 = (sp - (nb & ~15)) >> 4;  // 16-byte pieces from the last aligned offset
+  for (int idx = tid; idx < nrows * tail16; idx += nth) {
+    const int row = idx / tail16, c = idx - row * tail16;
+    uint8_t *pt = lds_sc + row * sp + (nb & ~15) + 16 * c;
+    if (c == 0 && (nb & 15)) {
+      for (int k = nb & 15; k < 16; ++k) pt[k] = 0;
     } else {
-      b = b1[p][t] & 0xFFu;
+      *(u32x4 *)pt = u32x4{0u, 0u, 0u, 0u};
     }
-    return e8m0_to_f32(s < smax ? b : 127u);
   }
-};
+}
+
+// Scale of lane (r, q)'s block at step s, from its LDS row.
+__device__ __forceinline__ float lds_scale(const uint8_t *row, int s, int q) {
+  return __builtin_ldexpf(1.0f, (int)row[4 * s + q] - 127);
+}
 
 // ------------------------------------------------------------------ gate/up
-// Workgroup = (group, GW*TPW*16 rows of f).  Wave w owns TPW 16-row tiles of
-// W_gate and the same rows of W_up over the whole d reduction.  Lane l =
-// (r = l%16, q = l/16): per step and tile it loads 16 bytes of codes = one
-// 32-element MXFP4 block (row r, block q of the step).  MFMA j (0..3) of a
-// step consumes elements 8j..8j+7 of each lane's block and the B fragment
-// x[column r][128 s + 32 q + 8 j ..+8].
+// Workgroup = (group, ROWS = GW/2 * TPW * 16 rows of f).  The first GW/2
+// waves own TPW 16-row tiles of W_gate, the other GW/2 waves the same rows of
+// W_up, each over the whole d reduction.  Lane l = (r = l%16, q = l/16): per
+// step and tile it loads 16 bytes of codes = one 32-element MXFP4 block (row
+// r, block q of the step).  MFMA j (0..3) of a step consumes elements
+// 8j..8j+7 of each lane's block and the B fragment x[column r][128 s + 32 q +
+// 8 j ..+8].  Column r is slot r of the group.  In resident mode the lanes of
+// columns past the group's slots read column 0: an MFMA output column
+// depends only on its own B column, and those columns are never stored.
 //
-// x staging: piece i of a step (i < MAXC*16) is column i/16, elements
-// 8*(i%16)..+8 of the step; thread t stages pieces t, t+GW*64, ...  fp32 x
-// is split exactly into three bf16 parts as it is staged.
+// Epilogue: the W_up waves leave their tiles in LDS and the W_gate waves form
+// h = silu(g) * u for every slot, split exactly into three bf16 parts.
+//
+// x staging (ring mode): piece i of a step (i < MAXC*16) is column i/16,
+// elements 8*(i%16)..+8 of the step; thread t stages pieces t, t+GW*64, ...
+// fp32 x is split exactly into three bf16 parts as it is staged.
 template <int XBF16, int TPW, int GW, int PF, int MAXC, bool SX4, bool BRES>
 __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
     const void *__restrict__ x, int d, int f, int kps, int n_slots, const uint8_t *__restrict__ experts,
     int64_t stride, GroupSrc src, const int32_t *__restrict__ perm, int n_ftiles, uint16_t *__restrict__ h_ws) {
-  constexpr int ROWS = GW * TPW * 16;
-  constexpr int NT = 2 * TPW;  // tiles per wave: TPW gate then TPW up
+  static_assert(GW % 2 == 0, "gate and up waves come in pairs");
+  constexpr int HW = GW / 2;  // waves per matrix
+  constexpr int ROWS = HW * TPW * 16;
   constexpr int NP = XBF16 ? 1 : 3;
   constexpr int EL = XBF16 ? 2 : 4;  // bytes per x element
   constexpr int NTH = GW * 64;
   // pieces staged per thread per step (ring mode; none in resident mode)
   constexpr int SPT = BRES ? 0 : (MAXC * 16 + NTH - 1) / NTH;
   constexpr int SPTA = SPT > 0 ? SPT : 1;  // array extent
-  extern __shared__ __align__(16) uint8_t bring[];
+  extern __shared__ __align__(16) uint8_t lds[];
   const int g = blockIdx.x / n_ftiles;
   const int ft = blockIdx.x - g * n_ftiles;
   int expert, start, count;
@@ -212,68 +278,18 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = lane & 15, q = lane >> 4;
+  const int mat = wv >= HW ? 1 : 0;  // 0: W_gate, 1: W_up
+  const int rw = wv - mat * HW;      // row-tile group of this wave
   const int i0 = ft * ROWS;
-  const int nb = d >> 5;
   const uint32_t plane_c = (uint32_t)((int64_t)f * d / 2), plane_s = (uint32_t)((int64_t)f * d / 32);
-  const uint32_t up_c = plane_c + plane_s, up_s = up_c + plane_c;
+  const uint32_t mat_c = mat ? plane_c + plane_s : 0u;
   const rsrc_t wr = make_rsrc(experts + (int64_t)expert * stride, (uint32_t)stride);
   const int M = n_slots / kps;
   const rsrc_t xr = make_rsrc(x, (uint32_t)((int64_t)M * d * EL));
   const uint32_t brow = bres_row_bytes(d);
-  if constexpr (BRES) {
-    // stage x of the group's columns for the whole d once: 8 elements per
-    // piece, MAXC columns plus the zero row, all loads issued first
-    constexpr int CH = 8;  // pieces per thread per round
-    const int per_col = d / 8;
-    const int npieces = (MAXC + 1) * per_col;
-    for (int base = 0; base < npieces; base += CH * NTH) {
-      u32x4 v[CH][EL / 2];
-      int pc[CH], pe[CH];
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const int piece = base + c * NTH + tid;
-        pc[c] = piece / per_col;
-        pe[c] = (piece - pc[c] * per_col) * 8;
-        uint32_t off = kOOB;
-        if (piece < npieces && pc[c] < count) {
-          const int t = perm[start + pc[c]];
-          if (t >= 0 && t < n_slots) off = (uint32_t)(t / kps) * (uint32_t)(d * EL) + (uint32_t)(pe[c] * EL);
-        }
-#pragma unroll
-        for (int h = 0; h < EL / 2; ++h) v[c][h] = buf_load16(xr, off + 16 * h);
-      }
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        if (base + c * NTH + tid < npieces) {
-          if (XBF16) {
-            *(u32x4 *)(bring + pc[c] * brow + pe[c] * 2) = v[c][0];
-          } else {
-            uint32_t hi[8], mi[8], lo[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) split3_bf16(__uint_as_float(v[c][e >> 2][e & 3]), hi[e], mi[e], lo[e]);
-            u32x4 ph, pm, pl;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              ph[e] = hi[2 * e] | (hi[2 * e + 1] << 16);
-              pm[e] = mi[2 * e] | (mi[2 * e + 1] << 16);
-              pl[e] = lo[2 * e] | (lo[2 * e + 1] << 16);
-            }
-            *(u32x4 *)(bring + (0 * (MAXC + 1) + pc[c]) * brow + pe[c] * 2) = ph;
-            *(u32x4 *)(bring + (1 * (MAXC + 1) + pc[c]) * brow + pe[c] * 2) = pm;
-            *(u32x4 *)(bring + (2 * (MAXC + 1) + pc[c]) * brow + pe[c] * 2) = pl;
-          }
-        }
-      }
-    }
-    for (int idx = tid; idx < NP * (MAXC + 1) * (kBresTail / 16); idx += NTH) {
-      const int row = idx / (kBresTail / 16), c = idx - row * (kBresTail / 16);
-      *(u32x4 *)(bring + row * brow + d * 2 + 16 * c) = u32x4{0u, 0u, 0u, 0u};
-    }
-    __syncthreads();
-  } else {
-    zero_b_rows<NP, PF>(bring, MAXC, tid, NTH);
-  }
-  const int bres_r = r < MAXC ? r : MAXC;  // resident-B row of this lane's column
+  const uint32_t dummy = (uint32_t)gateup_dummy_off(d, PF, NP, MAXC, BRES, ROWS);
+  uint8_t *const bmem = lds + gateup_b_off(d, ROWS);  // B area (after the scale rows)
+  const int bcol = r < count ? r : 0;  // resident-B column read by this lane
 
   // staging pieces of this thread: x row base offset (kOOB when empty) and
   // element offset within the step
@@ -284,27 +300,26 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
     const int piece = tid + i * NTH;
     pcol[i] = piece >> 4;
     pel[i] = (piece & 15) * 8;
-    pbase[i] = kOOB;
-    if (piece < MAXC * 16 && pcol[i] < count) {
-      const int t = perm[start + pcol[i]];
-      if (t >= 0 && t < n_slots) pbase[i] = (uint32_t)(t / kps) * (uint32_t)(d * EL);
-    }
+    const int t = perm[start + (pcol[i] < count ? pcol[i] : count - 1)];
+    pbase[i] = (piece < MAXC * 16 && pcol[i] < count && t >= 0 && t < n_slots) ? (uint32_t)(t / kps) * (uint32_t)(d * EL)
+                                                                                 : kOOB;
   }
-  uint32_t aoff[NT];
-  ScaleRing<SX4, NT, PF> sr;
+  uint32_t aoff[TPW];
+  const uint8_t *srow[TPW];  // this lane's LDS scale row per tile
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int row = i0 + (wv * TPW + (t % TPW)) * 16 + r;
-    aoff[t] = sel_off(row < f, (t < TPW ? 0u : up_c) + (uint32_t)row * (uint32_t)(d / 2));
-    sr.soff[t] = sel_off(row < f, (t < TPW ? plane_c : up_s) + (uint32_t)row * (uint32_t)nb);
+  for (int t = 0; t < TPW; ++t) {
+    const int lrow = (rw * TPW + t) * 16 + r;
+    const int row = i0 + lrow;
+    aoff[t] = sel_off(row < f, mat_c + (uint32_t)row * (uint32_t)(d / 2));
+    srow[t] = lds + (mat * ROWS + lrow) * sc_pitch(d);
   }
-  f32x4 acc[NT];
+  f32x4 acc[TPW];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < TPW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nsteps = (d + 127) >> 7;
   const int smax = (d - (q << 5) + 127) >> 7;  // live steps of this lane's weight block
-  u32x4 ring[PF][NT];
+  u32x4 ring[PF][TPW];
   u32x4 xst[PF][SPTA][EL / 2];
   // Loads are consumed in the order they are issued (the vector-memory
   // counter retires in order): the codes, scales and x of step s are issued
@@ -314,8 +329,7 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
     const int kq = (s << 7) + (q << 5);
     const uint32_t ka = s < smax ? (uint32_t)(kq >> 1) : kDead;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) ring[p][t] = buf_load16(wr, aoff[t] + ka);
-    sr.issue(wr, s, p, nsteps, smax, q);
+    for (int t = 0; t < TPW; ++t) ring[p][t] = buf_load16(wr, aoff[t] + ka);
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
       const int k = (s << 7) + pel[i];
@@ -326,6 +340,82 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
   };
 #pragma unroll
   for (int p = 0; p < PF; ++p) issue(p, p);
+  // ring mode: the first loads arrive together; waiting for all of them here
+  // lets the compiler see the same loads in flight at every loop iteration
+  // (otherwise it keeps the prefill's issue order in mind at the loop head
+  // and waits far deeper than the ring needs, every iteration)
+  if constexpr (!BRES) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+  // scale and B staging run while the first ring loads are in flight
+  {
+    const int rv = f - i0 < ROWS ? f - i0 : ROWS;
+    stage_scales<SX4>(wr, plane_c, i0, rv, ROWS, d, lds, dummy, lds, tid, NTH);
+    stage_scales<SX4>(wr, 2 * plane_c + plane_s, i0, rv, ROWS, d, lds + ROWS * sc_pitch(d), dummy, lds, tid, NTH);
+  }
+  if constexpr (BRES) {
+    // x of the group's columns for the whole d, 8 elements per piece, all
+    // loads of a round issued before its LDS writes.  The x row of each
+    // column is read from perm once, up front.
+    uint32_t xb[MAXC];
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      const int t = perm[start + (c < count ? c : count - 1)];
+      xb[c] = (c < count && t >= 0 && t < n_slots) ? (uint32_t)(t / kps) * (uint32_t)(d * EL) : kOOB;
+    }
+    constexpr int CH = 8;  // pieces per thread per round
+    const int per_col = d / 8;
+    const int npieces = count * per_col;
+    for (int base = 0; base < npieces; base += CH * NTH) {
+      u32x4 v[CH][EL / 2];
+      int pc[CH], pe[CH];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int piece = base + c * NTH + tid;
+        pc[c] = piece / per_col;
+        pe[c] = (piece - pc[c] * per_col) * 8;
+        uint32_t xrow = xb[0];
+#pragma unroll
+        for (int cc = 1; cc < MAXC; ++cc) xrow = pc[c] == cc ? xb[cc] : xrow;
+        const uint32_t off = piece < npieces ? xrow + (uint32_t)(pe[c] * EL) : kOOB;
+#pragma unroll
+        for (int h = 0; h < EL / 2; ++h) v[c][h] = buf_load16(xr, off + 16 * h);
+      }
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const bool live = base + c * NTH + tid < npieces;
+        if (XBF16) {
+          *(u32x4 *)(live ? bmem + pc[c] * brow + pe[c] * 2 : lds + dummy) = v[c][0];
+        } else {
+          uint32_t hi[8], mi[8], lo[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) split3_bf16(__uint_as_float(v[c][e >> 2][e & 3]), hi[e], mi[e], lo[e]);
+          u32x4 ph, pm, pl;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            ph[e] = hi[2 * e] | (hi[2 * e + 1] << 16);
+            pm[e] = mi[2 * e] | (mi[2 * e + 1] << 16);
+            pl[e] = lo[2 * e] | (lo[2 * e + 1] << 16);
+          }
+          *(u32x4 *)(live ? bmem + (0 * MAXC + pc[c]) * brow + pe[c] * 2 : lds + dummy) = ph;
+          *(u32x4 *)(live ? bmem + (1 * MAXC + pc[c]) * brow + pe[c] * 2 : lds + dummy + 16) = pm;
+          *(u32x4 *)(live ? bmem + (2 * MAXC + pc[c]) * brow + pe[c] * 2 : lds + dummy + 32) = pl;
+        }
+      }
+    }
+    for (int idx = tid; idx < NP * MAXC * (kBresTail / 16); idx += NTH) {
+      const int row = idx / (kBresTail / 16), c = idx - row * (kBresTail / 16);
+      *(u32x4 *)(bmem + row * brow + d * 2 + 16 * c) = u32x4{0u, 0u, 0u, 0u};
+    }
+    lds_barrier();
+  } else if constexpr (MAXC < 16) {
+    // rows of columns >= MAXC are never staged: zero them once
+    const int zrows = PF * NP * (16 - MAXC);
+    for (int idx = tid; idx < zrows * (kBRow / 16); idx += NTH) {
+      const int rr = idx / (kBRow / 16), cc = idx - rr * (kBRow / 16);
+      const int slot_part = rr / (16 - MAXC), col = MAXC + rr % (16 - MAXC);
+      *(u32x4 *)(bmem + (slot_part * 16 + col) * kBRow + cc * 16) = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
 
   // The loop runs a whole number of rings: steps past the end load zeros
   // and add exact zeros, and nothing in the loop branches, so every wait on
@@ -339,9 +429,12 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
       // previous barrier; PF >= 2)
 #pragma unroll
       for (int i = 0; i < SPT; ++i) {
-        if (tid + i * NTH < MAXC * 16) {
+        {
+          const bool live = tid + i * NTH < MAXC * 16;
+          uint8_t *dst = live ? bmem + ((p * NP) * 16 + pcol[i]) * kBRow + pel[i] * 2 : lds + dummy;
+          const uint32_t pstep = live ? 16 * kBRow : 16;
           if (XBF16) {
-            *(u32x4 *)(bring + bslot_off<NP>(p, 0, pcol[i]) + pel[i] * 2) = xst[p][i][0];
+            *(u32x4 *)dst = xst[p][i][0];
           } else {
             uint32_t hi[8], mi[8], lo[8];
 #pragma unroll
@@ -354,48 +447,60 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
               pm[e] = mi[2 * e] | (mi[2 * e + 1] << 16);
               pl[e] = lo[2 * e] | (lo[2 * e + 1] << 16);
             }
-            *(u32x4 *)(bring + bslot_off<NP>(p, 0, pcol[i]) + pel[i] * 2) = ph;
-            *(u32x4 *)(bring + bslot_off<NP>(p, 1, pcol[i]) + pel[i] * 2) = pm;
-            *(u32x4 *)(bring + bslot_off<NP>(p, 2, pcol[i]) + pel[i] * 2) = pl;
+            *(u32x4 *)dst = ph;
+            *(u32x4 *)(dst + pstep) = pm;
+            *(u32x4 *)(dst + 2 * pstep) = pl;
           }
         }
       }
-      if constexpr (!BRES) __syncthreads();
-      float sc[NT];
+      if constexpr (!BRES) lds_barrier();
+      float sc[TPW];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) sc[t] = sr.get(s, p, t, smax, q);
+      for (int t = 0; t < TPW; ++t) sc[t] = lds_scale(srow[t], s, q);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         bf16x8 b[NP];
 #pragma unroll
         for (int pp = 0; pp < NP; ++pp) {
           if constexpr (BRES)
-            b[pp] = lds_b_fragment(bring, (pp * (MAXC + 1) + bres_r) * brow +
-                                              (s < smax ? ((s << 7) + (q << 5) + 8 * j) * 2 : d * 2 + 16 * j));
+            b[pp] = lds_b_fragment(bmem, (pp * MAXC + bcol) * brow +
+                                            (s < smax ? ((s << 7) + (q << 5) + 8 * j) * 2 : d * 2 + 16 * j));
           else
-            b[pp] = lds_b_fragment(bring, bslot_off<NP>(p, pp, r) + ((q << 5) + 8 * j) * 2);
+            b[pp] = lds_b_fragment(bmem, ((p * NP + pp) * 16 + r) * kBRow + ((q << 5) + 8 * j) * 2);
         }
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
+        for (int t = 0; t < TPW; ++t) {
           const bf16x8 a = fp4x8_to_bf16(ring[p][t][j], sc[t]);
 #pragma unroll
           for (int pp = 0; pp < NP; ++pp) acc[t] = mfma16x16x32(a, b[pp], acc[t]);
         }
       }
       issue(s + PF, p);
+      // keep the refill here: the scheduler would otherwise sink it past the
+      // next steps' waits and drain the ring once per unrolled window
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  // SwiGLU and the exact three-part split of h, written per slot
-  if (r < count) {
+  // SwiGLU: the W_up waves hand their tiles to the W_gate waves through LDS
+  float *ut = (float *)(lds + gateup_e_off(d, PF, NP, MAXC, BRES, ROWS));
+  if (mat) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ut[((rw * TPW + t) * 16 + 4 * q + i) * 17 + r] = acc[t][i];
+  }
+  lds_barrier();
+  if (!mat && r < count) {
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-      const int row = i0 + (wv * TPW + t) * 16 + 4 * q;
+      const int lrow = (rw * TPW + t) * 16 + 4 * q;
+      const int row = i0 + lrow;
       if (row < f) {
         uint32_t hi[4], mi[4], lo[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float gv = acc[t][i], uv = acc[t + TPW][i];
+          const float gv = acc[t][i], uv = ut[(lrow + i) * 17 + r];
           split3_bf16((gv / (1.0f + expf(-gv))) * uv, hi[i], mi[i], lo[i]);
         }
         uint16_t *hp = h_ws + (int64_t)(start + r) * 3 * f + row;
@@ -409,20 +514,28 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
 
 // ------------------------------------------------------------------ down
 // Workgroup = (group, DW*TPW*16 rows of d); each wave owns TPW row tiles and
-// the whole f reduction, B = the group's h in three exact bf16 parts, staged
-// per step in LDS as for gate/up (piece i: part i/(MAXC*16), column
-// (i/16)%MAXC, elements 8*(i%16)..+8).  Each slot's y row is written by its
-// column's lanes.
+// the whole f reduction.  B = the group's h in three exact bf16 parts, three
+// MFMA columns per slot: B row (global column) 3*j + p holds part p of slot j.
+// Those are rows start*3 + 3*j + p of the workspace's h, one contiguous
+// block for the group.  Columns come in blocks of 16, so a group of c slots
+// takes ceil(3c/16) MFMAs per 32-element slice (one for up to 5 slots).
+// Every column accumulates one (slot, part) over the whole reduction in a
+// fixed order, independent of the column's position; the epilogue adds a
+// slot's three part sums, hi + mid, then + lo.  Lanes of columns past the
+// group's read B row 0 (those columns are never used).
 template <int TPW, int DW, int PF, int MAXC, bool SX4, bool BRES>
 __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
     int d, int f, int n_slots, const uint8_t *__restrict__ experts, int64_t stride, GroupSrc src,
     const int32_t *__restrict__ perm, int n_dtiles, const uint16_t *__restrict__ h_ws, float *__restrict__ y) {
   constexpr int ROWS = DW * TPW * 16;
   constexpr int NTH = DW * 64;
-  constexpr int NPIECE = 3 * MAXC * 16;
+  constexpr int NC = 3 * MAXC;        // B rows at most
+  constexpr int NCB = (NC + 15) / 16;  // column blocks at most
+  constexpr int NPIECE = NC * 16;     // ring staging pieces per step (8 elements each)
   constexpr int SPT = BRES ? 0 : (NPIECE + NTH - 1) / NTH;
   constexpr int SPTA = SPT > 0 ? SPT : 1;
-  extern __shared__ __align__(16) uint8_t bring[];
+  constexpr int YP = NC + 1;  // epilogue row pitch (floats)
+  extern __shared__ __align__(16) uint8_t lds[];
   const int g = blockIdx.x / n_dtiles;
   const int dt = blockIdx.x - g * n_dtiles;
   int expert, start, count;
@@ -430,70 +543,44 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = lane & 15, q = lane >> 4;
-  const int nb = f >> 5;
+  const int nc = 3 * count, ncb = (nc + 15) >> 4;
   const uint32_t plane = (uint32_t)((int64_t)f * d / 2 + (int64_t)f * d / 32);
   const uint32_t dn_c = 2 * plane, dn_s = dn_c + (uint32_t)((int64_t)d * f / 2);
   const rsrc_t wr = make_rsrc(experts + (int64_t)expert * stride, (uint32_t)stride);
   const rsrc_t hr = make_rsrc(h_ws, (uint32_t)((int64_t)n_slots * 3 * f * 2));
+  const uint32_t hbase = (uint32_t)start * (uint32_t)(3 * f * 2);  // the group's first h row
   const int r0 = dt * ROWS;
   const uint32_t brow = bres_row_bytes(f);
-  if constexpr (BRES) {
-    // stage the group's h (3 parts x MAXC columns + the zero row) for the
-    // whole f once, all loads of a round issued first
-    constexpr int CH = 8;
-    const int per_row = f / 8;
-    const int npieces = 3 * (MAXC + 1) * per_row;
-    for (int base = 0; base < npieces; base += CH * NTH) {
-      u32x4 v[CH];
-      int prow[CH], pe[CH];
+  const uint32_t dummy = (uint32_t)down_dummy_off(f, PF, MAXC, BRES, ROWS);
+  uint8_t *const bmem = lds + down_b_off(f, ROWS);  // B area (after the scale rows)
+  int bsel[NCB];  // B row read by this lane in each column block
 #pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const int piece = base + c * NTH + tid;
-        prow[c] = piece / per_row;  // part * (MAXC + 1) + column
-        pe[c] = (piece - prow[c] * per_row) * 8;
-        const int part = prow[c] / (MAXC + 1), col = prow[c] - part * (MAXC + 1);
-        const uint32_t off = (piece < npieces && col < count)
-                                 ? (uint32_t)(start + col) * (uint32_t)(3 * f * 2) + (uint32_t)((part * f + pe[c]) * 2)
-                                 : kOOB;
-        v[c] = buf_load16(hr, off);
-      }
-#pragma unroll
-      for (int c = 0; c < CH; ++c)
-        if (base + c * NTH + tid < npieces) *(u32x4 *)(bring + prow[c] * brow + pe[c] * 2) = v[c];
-    }
-    for (int idx = tid; idx < 3 * (MAXC + 1) * (kBresTail / 16); idx += NTH) {
-      const int row = idx / (kBresTail / 16), c = idx - row * (kBresTail / 16);
-      *(u32x4 *)(bring + row * brow + f * 2 + 16 * c) = u32x4{0u, 0u, 0u, 0u};
-    }
-    __syncthreads();
-  } else {
-    zero_b_rows<3, PF>(bring, MAXC, tid, NTH);
-  }
-  const int bres_r = r < MAXC ? r : MAXC;
+  for (int cb = 0; cb < NCB; ++cb) bsel[cb] = cb * 16 + r < nc ? cb * 16 + r : 0;
 
+  // ring staging pieces: piece i is B row i/16, elements 8*(i%16)..+8 of the step
   uint32_t pbase[SPTA];
-  int ppart[SPTA], pcol[SPTA], pel[SPTA];
+  int prow[SPTA], pel[SPTA];
 #pragma unroll
   for (int i = 0; i < SPT; ++i) {
     const int piece = tid + i * NTH;
-    ppart[i] = piece / (MAXC * 16);
-    pcol[i] = (piece >> 4) % MAXC;
+    prow[i] = piece >> 4;
     pel[i] = (piece & 15) * 8;
-    pbase[i] = (piece < NPIECE && pcol[i] < count)
-                   ? (uint32_t)(start + pcol[i]) * (uint32_t)(3 * f * 2) + (uint32_t)(ppart[i] * f * 2)
-                   : kOOB;
+    pbase[i] = (piece < NPIECE && prow[i] < nc) ? hbase + (uint32_t)prow[i] * (uint32_t)(f * 2) : kOOB;
   }
   uint32_t aoff[TPW];
-  ScaleRing<SX4, TPW, PF> sr;
+  const uint8_t *srow[TPW];  // this lane's LDS scale row per tile
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
-    const int row = r0 + (wv * TPW + t) * 16 + r;
+    const int lrow = (wv * TPW + t) * 16 + r;
+    const int row = r0 + lrow;
     aoff[t] = sel_off(row < d, dn_c + (uint32_t)row * (uint32_t)(f / 2));
-    sr.soff[t] = sel_off(row < d, dn_s + (uint32_t)row * (uint32_t)nb);
+    srow[t] = lds + lrow * sc_pitch(f);
   }
-  f32x4 acc[TPW];
+  f32x4 acc[TPW][NCB];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc[t][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nsteps = (f + 127) >> 7;
   const int smax = (f - (q << 5) + 127) >> 7;
@@ -504,7 +591,6 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
     const uint32_t ka = s < smax ? (uint32_t)(kq >> 1) : kDead;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) ring[p][t] = buf_load16(wr, aoff[t] + ka);
-    sr.issue(wr, s, p, nsteps, smax, q);
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
       const int k = (s << 7) + pel[i];
@@ -513,6 +599,39 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
   };
 #pragma unroll
   for (int p = 0; p < PF; ++p) issue(p, p);
+  // ring mode: the first loads arrive together; waiting for all of them here
+  // lets the compiler see the same loads in flight at every loop iteration
+  // (otherwise it keeps the prefill's issue order in mind at the loop head
+  // and waits far deeper than the ring needs, every iteration)
+  if constexpr (!BRES) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+  // scale and B staging run while the first ring loads are in flight
+  stage_scales<SX4>(wr, dn_s, r0, d - r0 < ROWS ? d - r0 : ROWS, ROWS, f, lds, dummy, lds, tid, NTH);
+  if constexpr (BRES) {
+    // the group's nc h rows for the whole f, all loads of a round issued first
+    constexpr int CH = 8;
+    const int per_row = f / 8;
+    const int npieces = nc * per_row;
+    for (int base = 0; base < npieces; base += CH * NTH) {
+      u32x4 v[CH];
+      int pr[CH], pe[CH];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int piece = base + c * NTH + tid;
+        pr[c] = piece / per_row;
+        pe[c] = (piece - pr[c] * per_row) * 8;
+        v[c] = buf_load16(hr, piece < npieces ? hbase + (uint32_t)(pr[c] * f + pe[c]) * 2u : kOOB);
+      }
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        *(u32x4 *)(base + c * NTH + tid < npieces ? bmem + pr[c] * brow + pe[c] * 2 : lds + dummy) = v[c];
+    }
+    for (int idx = tid; idx < nc * (kBresTail / 16); idx += NTH) {
+      const int row = idx / (kBresTail / 16), c = idx - row * (kBresTail / 16);
+      *(u32x4 *)(bmem + row * brow + f * 2 + 16 * c) = u32x4{0u, 0u, 0u, 0u};
+    }
+    lds_barrier();
+  }
 
   const int nsteps_pad = (nsteps + PF - 1) / PF * PF;  // see the gate/up kernel
   for (int s0 = 0; s0 < nsteps_pad; s0 += PF) {
@@ -521,43 +640,61 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
       const int s = s0 + p;
 #pragma unroll
       for (int i = 0; i < SPT; ++i)
-        if (tid + i * NTH < NPIECE) *(u32x4 *)(bring + bslot_off<3>(p, ppart[i], pcol[i]) + pel[i] * 2) = hst[p][i];
-      if constexpr (!BRES) __syncthreads();
+        *(u32x4 *)(tid + i * NTH < NPIECE ? bmem + (p * NC + prow[i]) * kBRow + pel[i] * 2 : lds + dummy) = hst[p][i];
+      if constexpr (!BRES) lds_barrier();
       float sc[TPW];
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) sc[t] = sr.get(s, p, t, smax, q);
+      for (int t = 0; t < TPW; ++t) sc[t] = lds_scale(srow[t], s, q);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        bf16x8 b[3];
+        bf16x8 a[TPW];
 #pragma unroll
-        for (int pp = 0; pp < 3; ++pp) {
-          if constexpr (BRES)
-            b[pp] = lds_b_fragment(bring, (pp * (MAXC + 1) + bres_r) * brow +
-                                              (s < smax ? ((s << 7) + (q << 5) + 8 * j) * 2 : f * 2 + 16 * j));
-          else
-            b[pp] = lds_b_fragment(bring, bslot_off<3>(p, pp, r) + ((q << 5) + 8 * j) * 2);
-        }
+        for (int t = 0; t < TPW; ++t) a[t] = fp4x8_to_bf16(ring[p][t][j], sc[t]);
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-          const bf16x8 a = fp4x8_to_bf16(ring[p][t][j], sc[t]);
-          acc[t] = mfma16x16x32(a, b[0], acc[t]);
-          acc[t] = mfma16x16x32(a, b[1], acc[t]);
-          acc[t] = mfma16x16x32(a, b[2], acc[t]);
+        for (int cb = 0; cb < NCB; ++cb) {
+          if (cb < ncb) {
+            bf16x8 b;
+            if constexpr (BRES)
+              b = lds_b_fragment(bmem, bsel[cb] * brow + (s < smax ? ((s << 7) + (q << 5) + 8 * j) * 2 : f * 2 + 16 * j));
+            else
+              b = lds_b_fragment(bmem, (p * NC + bsel[cb]) * kBRow + ((q << 5) + 8 * j) * 2);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) acc[t][cb] = mfma16x16x32(a[t], b, acc[t][cb]);
+          }
         }
       }
       issue(s + PF, p);
+      // keep the refill here: the scheduler would otherwise sink it past the
+      // next steps' waits and drain the ring once per unrolled window
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  if (r < count) {
-    const int t_slot = perm[start + r];
-    if (t_slot >= 0 && t_slot < n_slots) {
-      float *yp = y + (int64_t)t_slot * d;
+  // every (row, column) sum goes through LDS (in the B area: all waves are
+  // past their last B read at the barrier); each slot's three part sums are
+  // added in a fixed order and its rows written as float4
+  float *ys = (float *)(lds + down_y_off(f, PF, MAXC, BRES, ROWS));
+  lds_barrier();
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) {
-        const int row = r0 + (wv * TPW + t) * 16 + 4 * q;
-        if (row < d) *(f32x4 *)(yp + row) = acc[t];
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+      if (cb * 16 + r < nc)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ys[((wv * TPW + t) * 16 + 4 * q + i) * YP + cb * 16 + r] = acc[t][cb][i];
+  lds_barrier();
+  for (int idx = tid; idx < count * (ROWS / 4); idx += NTH) {
+    const int j = idx / (ROWS / 4), lrow = (idx - j * (ROWS / 4)) * 4;
+    const int row = r0 + lrow;
+    const int t_slot = perm[start + j];
+    if (row < d && t_slot >= 0 && t_slot < n_slots) {
+      f32x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float *yr = ys + (lrow + i) * YP + 3 * j;
+        v[i] = (yr[0] + yr[1]) + yr[2];
       }
+      *(f32x4 *)(y + (int64_t)t_slot * d + row) = v;
     }
   }
 }
@@ -588,15 +725,7 @@ static bool allow_lds(const void *kernel) {
   return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds) == hipSuccess;
 }
 
-// LDS of a launch: scale rows plus the B ring.  Every buffer resource must
-// stay below 2^30 bytes (see kOOB / kDead).
-static size_t gateup_smem(int d, int pf, int np, int maxc, bool bres) {
-  return bres ? bres_bytes(d, maxc, np) : (size_t)pf * np * 16 * kBRow;
-}
-static size_t down_smem(int f, int pf, int maxc, bool bres) {
-  return bres ? bres_bytes(f, maxc, 3) : (size_t)pf * 3 * 16 * kBRow;
-}
-
+// Every buffer resource must stay below 2^30 bytes (see kOOB / kDead).
 bool ffn_shape_ok(int64_t M, int k, int S, int d, int f, int64_t stride) {
   const int64_t T = M * (k + S);
   const int64_t lim = (int64_t)kDead;
@@ -609,9 +738,10 @@ bool ffn_shape_ok(int64_t M, int k, int S, int d, int f, int64_t stride) {
 template <int XBF16, int TPW, int GW, int PF, int MAXC, bool SX4, bool BRES>
 static int launch_gateup(const void *x, int d, int f, int kps, int T, const uint8_t *experts, int64_t stride,
                          const GroupSrc &src, const int32_t *perm, int64_t maxg, uint16_t *h_ws, hipStream_t stream) {
-  constexpr int ROWS = GW * TPW * 16;
+  constexpr int ROWS = GW / 2 * TPW * 16;
   const int n_ftiles = (f + ROWS - 1) / ROWS;
-  const size_t smem = gateup_smem(d, PF, XBF16 ? 1 : 3, MAXC, BRES);
+  const size_t smem = gateup_lds_bytes(d, PF, XBF16 ? 1 : 3, MAXC, BRES, ROWS);
+  if (smem > (size_t)kMaxLds) return -3;
   static const bool lds_ok =
       allow_lds(reinterpret_cast<const void *>(&ffn_gateup_kernel<XBF16, TPW, GW, PF, MAXC, SX4, BRES>));
   if (!lds_ok) return -3;
@@ -625,7 +755,8 @@ static int launch_down(int d, int f, int T, const uint8_t *experts, int64_t stri
                        const int32_t *perm, int64_t maxg, const uint16_t *h_ws, float *y, hipStream_t stream) {
   constexpr int ROWS = DW * TPW * 16;
   const int n_dtiles = (d + ROWS - 1) / ROWS;
-  const size_t smem = down_smem(f, PF, MAXC, BRES);
+  const size_t smem = down_lds_bytes(f, PF, MAXC, BRES, ROWS);
+  if (smem > (size_t)kMaxLds) return -3;
   static const bool lds_ok = allow_lds(reinterpret_cast<const void *>(&ffn_down_kernel<TPW, DW, PF, MAXC, SX4, BRES>));
   if (!lds_ok) return -3;
   hipLaunchKernelGGL((ffn_down_kernel<TPW, DW, PF, MAXC, SX4, BRES>), dim3((unsigned)(maxg * n_dtiles)), dim3(DW * 64), smem,
@@ -671,27 +802,31 @@ int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *exper
   (dsx4 ? launch_down<T, D, P, C, true, R>(d, f, T_, experts, stride, src, perm, maxg, h_ws, y, stream) \
         : launch_down<T, D, P, C, false, R>(d, f, T_, experts, stride, src, perm, maxg, h_ws, y, stream))
   // few rows: each group's B operand (x or h) stays resident in LDS for the
-  // whole reduction; more rows: B is staged step by step through a ring
+  // whole reduction; more rows: B is staged step by step through a ring.
+  // Launch shapes (measured at the Kimi shape): gate/up 4 waves (2 W_gate +
+  // 2 W_up, 32 rows of f) with an 8-step ring at 1-2 rows, 8 waves with a
+  // 4-step ring beyond; down 4 waves x 1 tile (64 rows of d) at up to 4
+  // rows, 4 waves x 2 tiles beyond.  A resident B is used only where the
+  // LDS it takes still lets two or more workgroups share a CU.
   int rc = 0;
   if (stages & kStageGateUp) {
-    const bool gres = gateup_smem(d, 4, x_bf16 ? 1 : 3, 4, true) <= (size_t)kMaxLds;
+    const int np = x_bf16 ? 1 : 3;
+    const size_t half = (size_t)kMaxLds / 2;
     if (x_bf16) {
-      if (M == 1 && gres) rc = MOE_GU(1, 1, 2, 4, 1, true);
-      else if (M <= 4 && gres) rc = MOE_GU(1, 1, 2, 4, 4, true);
-      else if (M <= 4) rc = MOE_GU(1, 1, 4, 4, 4, false);
-      else rc = MOE_GU(1, 1, 4, 4, 16, false);
+      if (M == 1 && gateup_lds_bytes(d, 8, np, 1, true, 32) <= half) rc = MOE_GU(1, 1, 4, 8, 1, true);
+      else if (M == 2 && gateup_lds_bytes(d, 8, np, 2, true, 32) <= half) rc = MOE_GU(1, 1, 4, 8, 2, true);
+      else rc = MOE_GU(1, 1, 8, 4, 16, false);
     } else {
-      if (M <= 4 && gres) rc = MOE_GU(0, 1, 2, 4, 4, true);
-      else rc = MOE_GU(0, 1, 4, 4, 16, false);
+      if (M <= 4 && gateup_lds_bytes(d, 8, np, 4, true, 32) <= half) rc = MOE_GU(0, 1, 4, 8, 4, true);
+      else rc = MOE_GU(0, 1, 8, 4, 16, false);
     }
     if (rc) return rc;
   }
   if (stages & kStageDown) {
-    const bool dres = down_smem(f, 4, 4, true) <= (size_t)kMaxLds;
-    if (M == 1 && dres) rc = MOE_DN(2, 8, 4, 1, true);
-    else if (M <= 4 && dres) rc = MOE_DN(2, 8, 4, 4, true);
-    else if (M <= 4) rc = MOE_DN(2, 8, 4, 4, false);
-    else rc = MOE_DN(2, 8, 4, 16, false);
+    const size_t half = (size_t)kMaxLds / 2;
+    if (M == 1 && down_lds_bytes(f, 4, 1, true, 64) <= half) rc = MOE_DN(1, 4, 4, 1, true);
+    else if (M <= 4 && down_lds_bytes(f, 4, 4, true, 64) <= half) rc = MOE_DN(1, 4, 4, 4, true);
+    else rc = MOE_DN(2, 4, 4, 16, false);
   }
 #undef MOE_GU
 #undef MOE_DN
