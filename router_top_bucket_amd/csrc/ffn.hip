@@ -241,9 +241,12 @@ __device__ __forceinline__ float lds_scale(const uint8_t *row, int s, int q) {
 }
 
 // ------------------------------------------------------------------ gate/up
-// Workgroup = (group, ROWS = GW/2 * TPW * 16 rows of f).  The first GW/2
-// waves own TPW 16-row tiles of W_gate, the other GW/2 waves the same rows of
-// W_up, each over the whole d reduction.  Lane l = (r = l%16, q = l/16): per
+// Workgroup = (group, ROWS rows of f).  PAIR: each of the GW waves owns TPW
+// 16-row tiles of W_gate and the same rows of W_up (ROWS = GW * TPW * 16),
+// and forms SwiGLU itself.  Otherwise the first GW/2 waves own TPW tiles of
+// W_gate and the other GW/2 the same rows of W_up (ROWS = GW/2 * TPW * 16),
+// and the W_up waves hand their tiles over through LDS.  Each tile covers the
+// whole d reduction.  Lane l = (r = l%16, q = l/16): per
 // step and tile it loads 16 bytes of codes = one 32-element MXFP4 block (row
 // r, block q of the step).  MFMA j (0..3) of a step consumes elements
 // 8j..8j+7 of each lane's block and the B fragment x[column r][128 s + 32 q +
@@ -251,19 +254,20 @@ __device__ __forceinline__ float lds_scale(const uint8_t *row, int s, int q) {
 // columns past the group's slots read column 0: an MFMA output column
 // depends only on its own B column, and those columns are never stored.
 //
-// Epilogue: the W_up waves leave their tiles in LDS and the W_gate waves form
-// h = silu(g) * u for every slot, split exactly into three bf16 parts.
+// Epilogue: h = silu(g) * u for every slot, split exactly into three bf16
+// parts.
 //
 // x staging (ring mode): piece i of a step (i < MAXC*16) is column i/16,
 // elements 8*(i%16)..+8 of the step; thread t stages pieces t, t+GW*64, ...
 // fp32 x is split exactly into three bf16 parts as it is staged.
-template <int XBF16, int TPW, int GW, int PF, int MAXC, bool SX4, bool BRES>
+template <int XBF16, int TPW, int GW, int PF, int MAXC, bool SX4, bool BRES, bool PAIR>
 __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
     const void *__restrict__ x, int d, int f, int kps, int n_slots, const uint8_t *__restrict__ experts,
     int64_t stride, GroupSrc src, const int32_t *__restrict__ perm, int n_ftiles, uint16_t *__restrict__ h_ws) {
-  static_assert(GW % 2 == 0, "gate and up waves come in pairs");
-  constexpr int HW = GW / 2;  // waves per matrix
+  static_assert(PAIR || GW % 2 == 0, "gate and up waves come in pairs");
+  constexpr int HW = PAIR ? GW : GW / 2;  // waves per row group
   constexpr int ROWS = HW * TPW * 16;
+  constexpr int NT = PAIR ? 2 * TPW : TPW;  // tiles per wave
   constexpr int NP = XBF16 ? 1 : 3;
   constexpr int EL = XBF16 ? 2 : 4;  // bytes per x element
   constexpr int NTH = GW * 64;
@@ -278,11 +282,10 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = lane & 15, q = lane >> 4;
-  const int mat = wv >= HW ? 1 : 0;  // 0: W_gate, 1: W_up
-  const int rw = wv - mat * HW;      // row-tile group of this wave
+  const int mat = PAIR ? 0 : (wv >= HW ? 1 : 0);  // 0: W_gate, 1: W_up (split layout)
+  const int rw = wv - mat * HW;                    // row-tile group of this wave
   const int i0 = ft * ROWS;
   const uint32_t plane_c = (uint32_t)((int64_t)f * d / 2), plane_s = (uint32_t)((int64_t)f * d / 32);
-  const uint32_t mat_c = mat ? plane_c + plane_s : 0u;
   const rsrc_t wr = make_rsrc(experts + (int64_t)expert * stride, (uint32_t)stride);
   const int M = n_slots / kps;
   const rsrc_t xr = make_rsrc(x, (uint32_t)((int64_t)M * d * EL));
@@ -304,22 +307,23 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
     pbase[i] = (piece < MAXC * 16 && pcol[i] < count && t >= 0 && t < n_slots) ? (uint32_t)(t / kps) * (uint32_t)(d * EL)
                                                                                  : kOOB;
   }
-  uint32_t aoff[TPW];
-  const uint8_t *srow[TPW];  // this lane's LDS scale row per tile
+  uint32_t aoff[NT];
+  const uint8_t *srow[NT];  // this lane's LDS scale row per tile
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int lrow = (rw * TPW + t) * 16 + r;
+  for (int t = 0; t < NT; ++t) {
+    const int tm = PAIR ? t / TPW : mat;  // matrix of tile t
+    const int lrow = (rw * TPW + t % TPW) * 16 + r;
     const int row = i0 + lrow;
-    aoff[t] = sel_off(row < f, mat_c + (uint32_t)row * (uint32_t)(d / 2));
-    srow[t] = lds + (mat * ROWS + lrow) * sc_pitch(d);
+    aoff[t] = sel_off(row < f, (tm ? plane_c + plane_s : 0u) + (uint32_t)row * (uint32_t)(d / 2));
+    srow[t] = lds + (tm * ROWS + lrow) * sc_pitch(d);
   }
-  f32x4 acc[TPW];
+  f32x4 acc[NT];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nsteps = (d + 127) >> 7;
   const int smax = (d - (q << 5) + 127) >> 7;  // live steps of this lane's weight block
-  u32x4 ring[PF][TPW];
+  u32x4 ring[PF][NT];
   u32x4 xst[PF][SPTA][EL / 2];
   // Loads are consumed in the order they are issued (the vector-memory
   // counter retires in order): the codes, scales and x of step s are issued
@@ -329,7 +333,7 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
     const int kq = (s << 7) + (q << 5);
     const uint32_t ka = s < smax ? (uint32_t)(kq >> 1) : kDead;
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) ring[p][t] = buf_load16(wr, aoff[t] + ka);
+    for (int t = 0; t < NT; ++t) ring[p][t] = buf_load16(wr, aoff[t] + ka);
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
       const int k = (s << 7) + pel[i];
@@ -454,9 +458,9 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
         }
       }
       if constexpr (!BRES) lds_barrier();
-      float sc[TPW];
+      float sc[NT];
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) sc[t] = lds_scale(srow[t], s, q);
+      for (int t = 0; t < NT; ++t) sc[t] = lds_scale(srow[t], s, q);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         bf16x8 b[NP];
@@ -469,7 +473,7 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
             b[pp] = lds_b_fragment(bmem, ((p * NP + pp) * 16 + r) * kBRow + ((q << 5) + 8 * j) * 2);
         }
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) {
+        for (int t = 0; t < NT; ++t) {
           const bf16x8 a = fp4x8_to_bf16(ring[p][t][j], sc[t]);
 #pragma unroll
           for (int pp = 0; pp < NP; ++pp) acc[t] = mfma16x16x32(a, b[pp], acc[t]);
@@ -482,15 +486,18 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
     }
   }
 
-  // SwiGLU: the W_up waves hand their tiles to the W_gate waves through LDS
+  // SwiGLU: split layout: the W_up waves hand their tiles to the W_gate
+  // waves through LDS; paired layout: both are in the wave already
   float *ut = (float *)(lds + gateup_e_off(d, PF, NP, MAXC, BRES, ROWS));
-  if (mat) {
+  if (!PAIR) {
+    if (mat) {
 #pragma unroll
-    for (int t = 0; t < TPW; ++t)
+      for (int t = 0; t < TPW; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ut[((rw * TPW + t) * 16 + 4 * q + i) * 17 + r] = acc[t][i];
+        for (int i = 0; i < 4; ++i) ut[((rw * TPW + t) * 16 + 4 * q + i) * 17 + r] = acc[t][i];
+    }
+    lds_barrier();
   }
-  lds_barrier();
   if (!mat && r < count) {
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
@@ -500,7 +507,7 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
         uint32_t hi[4], mi[4], lo[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float gv = acc[t][i], uv = ut[(lrow + i) * 17 + r];
+          const float gv = acc[t][i], uv = PAIR ? acc[(t + TPW) % NT][i] : ut[(lrow + i) * 17 + r];
           split3_bf16((gv / (1.0f + expf(-gv))) * uv, hi[i], mi[i], lo[i]);
         }
         uint16_t *hp = h_ws + (int64_t)(start + r) * 3 * f + row;
@@ -735,17 +742,17 @@ bool ffn_shape_ok(int64_t M, int k, int S, int d, int f, int64_t stride) {
          M * (int64_t)d * 4 < lim && T * 3 * f * 2 < lim;
 }
 
-template <int XBF16, int TPW, int GW, int PF, int MAXC, bool SX4, bool BRES>
+template <int XBF16, int TPW, int GW, int PF, int MAXC, bool SX4, bool BRES, bool PAIR>
 static int launch_gateup(const void *x, int d, int f, int kps, int T, const uint8_t *experts, int64_t stride,
                          const GroupSrc &src, const int32_t *perm, int64_t maxg, uint16_t *h_ws, hipStream_t stream) {
-  constexpr int ROWS = GW / 2 * TPW * 16;
+  constexpr int ROWS = (PAIR ? GW : GW / 2) * TPW * 16;
   const int n_ftiles = (f + ROWS - 1) / ROWS;
   const size_t smem = gateup_lds_bytes(d, PF, XBF16 ? 1 : 3, MAXC, BRES, ROWS);
   if (smem > (size_t)kMaxLds) return -3;
   static const bool lds_ok =
-      allow_lds(reinterpret_cast<const void *>(&ffn_gateup_kernel<XBF16, TPW, GW, PF, MAXC, SX4, BRES>));
+      allow_lds(reinterpret_cast<const void *>(&ffn_gateup_kernel<XBF16, TPW, GW, PF, MAXC, SX4, BRES, PAIR>));
   if (!lds_ok) return -3;
-  hipLaunchKernelGGL((ffn_gateup_kernel<XBF16, TPW, GW, PF, MAXC, SX4, BRES>), dim3((unsigned)(maxg * n_ftiles)), dim3(GW * 64),
+  hipLaunchKernelGGL((ffn_gateup_kernel<XBF16, TPW, GW, PF, MAXC, SX4, BRES, PAIR>), dim3((unsigned)(maxg * n_ftiles)), dim3(GW * 64),
                      smem, stream, x, d, f, kps, T, experts, stride, src, perm, n_ftiles, h_ws);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
@@ -795,30 +802,31 @@ int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *exper
   // the order of any reduction: every choice gives bit-identical results.
   const bool gsx4 = (d / 32) % 16 == 0, dsx4 = (f / 32) % 16 == 0;
   const int T_ = (int)T;
-#define MOE_GU(XB, T, G, P, C, R)                                                                                  \
-  (gsx4 ? launch_gateup<XB, T, G, P, C, true, R>(x, d, f, kps, T_, experts, stride, src, perm, maxg, h_ws, stream) \
-        : launch_gateup<XB, T, G, P, C, false, R>(x, d, f, kps, T_, experts, stride, src, perm, maxg, h_ws, stream))
+#define MOE_GU(XB, T, G, P, C, R, PR)                                                                          \
+  (gsx4 ? launch_gateup<XB, T, G, P, C, true, R, PR>(x, d, f, kps, T_, experts, stride, src, perm, maxg, h_ws, stream) \
+        : launch_gateup<XB, T, G, P, C, false, R, PR>(x, d, f, kps, T_, experts, stride, src, perm, maxg, h_ws, stream))
 #define MOE_DN(T, D, P, C, R)                                                                                   \
   (dsx4 ? launch_down<T, D, P, C, true, R>(d, f, T_, experts, stride, src, perm, maxg, h_ws, y, stream) \
         : launch_down<T, D, P, C, false, R>(d, f, T_, experts, stride, src, perm, maxg, h_ws, y, stream))
   // few rows: each group's B operand (x or h) stays resident in LDS for the
   // whole reduction; more rows: B is staged step by step through a ring.
-  // Launch shapes (measured at the Kimi shape): gate/up 4 waves (2 W_gate +
-  // 2 W_up, 32 rows of f) with an 8-step ring at 1-2 rows, 8 waves with a
-  // 4-step ring beyond; down 4 waves x 1 tile (64 rows of d) at up to 4
-  // rows, 4 waves x 2 tiles beyond.  A resident B is used only where the
+  // Launch shapes (measured at the Kimi shape): gate/up 2 waves each with
+  // the W_gate and W_up tiles of 16 rows (32 rows of f) and a 4-step ring at
+  // 1-2 rows, 8 waves (4 W_gate + 4 W_up) with a 4-step ring beyond; down 4 waves x 1 tile (64 rows of d) at up to 4
+  // rows, 8 waves x 2 tiles beyond (fewer workgroups per group re-stage its
+  // h).  A resident B is used only where the
   // LDS it takes still lets two or more workgroups share a CU.
   int rc = 0;
   if (stages & kStageGateUp) {
     const int np = x_bf16 ? 1 : 3;
     const size_t half = (size_t)kMaxLds / 2;
     if (x_bf16) {
-      if (M == 1 && gateup_lds_bytes(d, 8, np, 1, true, 32) <= half) rc = MOE_GU(1, 1, 4, 8, 1, true);
-      else if (M == 2 && gateup_lds_bytes(d, 8, np, 2, true, 32) <= half) rc = MOE_GU(1, 1, 4, 8, 2, true);
-      else rc = MOE_GU(1, 1, 8, 4, 16, false);
+      if (M == 1 && gateup_lds_bytes(d, 4, np, 1, true, 32) <= half) rc = MOE_GU(1, 1, 2, 4, 1, true, true);
+      else if (M == 2 && gateup_lds_bytes(d, 4, np, 2, true, 32) <= half) rc = MOE_GU(1, 1, 2, 4, 2, true, true);
+      else rc = MOE_GU(1, 1, 8, 4, 16, false, false);
     } else {
-      if (M <= 4 && gateup_lds_bytes(d, 8, np, 4, true, 32) <= half) rc = MOE_GU(0, 1, 4, 8, 4, true);
-      else rc = MOE_GU(0, 1, 8, 4, 16, false);
+      if (M <= 4 && gateup_lds_bytes(d, 4, np, 4, true, 32) <= half) rc = MOE_GU(0, 1, 2, 4, 4, true, true);
+      else rc = MOE_GU(0, 1, 8, 4, 16, false, false);
     }
     if (rc) return rc;
   }
@@ -826,7 +834,7 @@ int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *exper
     const size_t half = (size_t)kMaxLds / 2;
     if (M == 1 && down_lds_bytes(f, 4, 1, true, 64) <= half) rc = MOE_DN(1, 4, 4, 1, true);
     else if (M <= 4 && down_lds_bytes(f, 4, 4, true, 64) <= half) rc = MOE_DN(1, 4, 4, 4, true);
-    else rc = MOE_DN(2, 4, 4, 16, false);
+    else rc = MOE_DN(2, 8, 4, 16, false);
   }
 #undef MOE_GU
 #undef MOE_DN

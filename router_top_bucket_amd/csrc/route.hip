@@ -238,7 +238,10 @@ template <int XBF16>
 static void launch_logits(const void *x, const float *w_router, float *logits, int M, int d, int E,
                           hipStream_t stream) {
   // pass shapes by row count; the arithmetic of a logit does not change
-  if (M <= 4)
+  if (M == 1)
+    hipLaunchKernelGGL((router_logits_kernel<XBF16, 1, 1, 8>), dim3(E), dim3(LG_THREADS), 0, stream, x, w_router, M,
+                       d, E, logits);
+  else if (M <= 4)
     hipLaunchKernelGGL((router_logits_kernel<XBF16, 1, 4, 8>), dim3(E), dim3(LG_THREADS), 0, stream, x, w_router, M,
                        d, E, logits);
   else if (M <= 16)
