@@ -3,180 +3,386 @@
 // unchanged", "Run Kimi 3.1 locally on one GPU": the spine's matrix multiplies
 // load each weight once for up to eight rows).
 //
-// Every weight is read once per launch for all M (<= 8) rows: the rows are
-// the 16 columns of an MFMA B operand (columns >= M are zero).  int8 values are
-// exact in bf16; X is split exactly into three bf16 parts (truncation: hi takes
-// the top 8 significant bits, mid the next 8 of the remainder, lo the rest), so
-// each block's MFMA products are exact.  Per 32-block: P = A.(hi+mid+lo) with a
-// fresh accumulator, then acc += P * scale.  Workgroup = 4 waves, each a fixed
-// quarter of K's blocks, summed in wave order; nothing depends on M.
+// Arithmetic (fixed for a given K and N, independent of M and of the launch
+// shape below): for output row n and X row m, each 32-block b contributes
+//   P_p = sum_{c in b} q[n,c] * x_p[m,c]        (one MFMA column, fresh C = 0)
+// for the three parts x = x_0 + x_1 + x_2 of an exact bf16 truncation split
+// (int8 is exact in bf16, so every product is exact), and
+//   A_p <- fma(P_p, s[n,b], A_p)                 (v_fma_mix: fp16 scale, one rounding)
+// runs over the blocks of a K part in ascending order.  The KS K parts are
+// summed in part order per p, and y = (A_0 + A_1) + A_2.
+//
+// Mapping.  A wave owns RT tiles of 16 weight rows and one K part; a step is
+// 64 K (two blocks).  Lane (r, q) loads 16 bytes of row r at K offset
+// 64s + 16q, so lanes q < 2 hold block 2s and q >= 2 block 2s+1; one
+// v_permlane32_swap per dword pair regroups them so each block's 32 values
+// sit 8 per lane group in the order {0, 16, 8, 24} + 0..7, the MFMA A layout.
+// The MFMA B operand has one column per (m, p): column 3m + p, so M <= 5 needs
+// one 16-column MFMA per block and M <= 8 two.  The wave splits X for the step
+// once (EPL elements per lane) into its own LDS area in that layout, and every
+// tile of the wave reads it back.  Scales: once per 16 steps lane (r, q)
+// loads the 8 fp16 scales of row r for blocks 2 s0 + 8q .. +7 of the chunk
+// (so each 64-byte piece of a scale row is fetched by one instruction); a
+// bpermute hands each lane the dword of output row 4q' + i for the step.
+// Every global load is an unconditional buffer load (dead steps and masked
+// lanes read past the resource and get zeros).
 #include "common.h"
 #include "launch.h"
 
 namespace moe {
 
-constexpr int Q8_WAVES = 4;
+constexpr int Q8_MAX_WAVES = 8;
+constexpr int kQ8Chunk = 16;  // steps per scale load (32 blocks)
 
-__device__ __forceinline__ float half_bits_to_f32(uint16_t h) {
-  _Float16 v;
-  __builtin_memcpy(&v, &h, sizeof(v));
-  return (float)v;
+// Upper halves of two fp32 bit patterns as one packed pair (a low, b high).
+__device__ __forceinline__ uint32_t q8_pack_hi16(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
-// bf16 bits of an integer in [-128, 127] (exact).
-__device__ __forceinline__ uint32_t i8_to_bf16_bits(int v) { return __float_as_uint((float)v) >> 16; }
+// Four int8 (element 0 in byte 0) as four bf16, exact.
+__device__ __forceinline__ u32x2 q8_i8x4_to_bf16(uint32_t w) {
+  const float f0 = (float)(int8_t)w, f1 = (float)(int8_t)(w >> 8);
+  const float f2 = (float)(int8_t)(w >> 16), f3 = (float)(int8_t)(w >> 24);
+  return u32x2{q8_pack_hi16(__float_as_uint(f0), __float_as_uint(f1)),
+               q8_pack_hi16(__float_as_uint(f2), __float_as_uint(f3))};
+}
 
-// split fp32 into three bf16 parts by truncation; v == hi + mid + lo exactly
-__device__ __forceinline__ void split3_trunc(float v, uint32_t &hi, uint32_t &mid, uint32_t &lo) {
+// v == hi + mid + lo exactly; each part is the upper 16 bits of the returned
+// fp32 pattern (truncation: hi keeps the top 8 significant bits of v, mid the
+// top 8 of the remainder, lo the at most 8 bits left).
+__device__ __forceinline__ void q8_split3(float v, uint32_t &hi, uint32_t &mid, uint32_t &lo) {
   const uint32_t u = __float_as_uint(v);
-  hi = u >> 16;
   const float r1 = v - __uint_as_float(u & 0xFFFF0000u);
   const uint32_t u1 = __float_as_uint(r1);
-  mid = u1 >> 16;
   const float r2 = r1 - __uint_as_float(u1 & 0xFFFF0000u);
-  lo = __float_as_uint(r2) >> 16;
+  hi = u;
+  mid = u1;
+  lo = __float_as_uint(r2);
 }
 
-template <int RT>
-__global__ __launch_bounds__(Q8_WAVES * 64) void q8_0_kernel(const float *__restrict__ X, int M, int K,
-                                                             const int8_t *__restrict__ wq,
-                                                             const uint16_t *__restrict__ ws, int N,
-                                                             float *__restrict__ Y) {
+__device__ __forceinline__ float q8_f16_lo(uint32_t v) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
+}
+__device__ __forceinline__ float q8_f16_hi(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16)); }
+
+// LDS of one wave: the X fragments of one step (2 blocks x 4 lane groups x
+// 16*NMF columns x 16 B, then a 16-byte dummy slot for masked writes); after
+// the main loop the same bytes hold the wave's partial sums [RT][NMF][4][65].
+template <int RT, int NMF>
+struct Q8Lds {
+  static constexpr int kCols = 16 * NMF;
+  static constexpr int kFrag = 2 * 4 * kCols * 16;
+  static constexpr int kPart = RT * NMF * 4 * 65 * 4;
+  static constexpr int kWave = ((kFrag + 16 > kPart ? kFrag + 16 : kPart) + 15) / 16 * 16;
+};
+
+template <int RT, int PF, int EPL, int NMF, bool MASKED, int WPE>
+__global__ __launch_bounds__(Q8_MAX_WAVES * 64) __attribute__((amdgpu_waves_per_eu(WPE))) void q8_0_kernel(const float *__restrict__ X, int M, int K,
+                                                                 const int8_t *__restrict__ wq,
+                                                                 const uint16_t *__restrict__ ws, int N,
+                                                                 float *__restrict__ Y, int KS, int RG) {
+  static_assert(kQ8Chunk % PF == 0, "ring depth divides the scale chunk");
+  static_assert(EPL == 1 || EPL == 2 || EPL == 4 || EPL == 8, "X elements per lane");
+  using L = Q8Lds<RT, NMF>;
   extern __shared__ __align__(16) uint8_t smem[];
-  const int nbk = K >> 5;                 // blocks per row
-  const int srow = nbk + 2;               // padded fp16 row of scales (halves)
-  uint16_t *sc_lds = (uint16_t *)smem;    // [RT*16][srow]
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, q = lane >> 4;
-  const int n0 = blockIdx.x * RT * 16;
-  const int rows_here = (N - n0) < RT * 16 ? (N - n0) : RT * 16;
+  const int rg = wv / KS, part = wv - rg * KS;
+  uint8_t *wl = smem + wv * L::kWave;
+  const int nb = K >> 5, ns = (nb + 1) >> 1;
+  const int row0 = (blockIdx.x * RG + rg) * RT * 16;
 
-  for (int idx = tid; idx < RT * 16 * nbk; idx += Q8_WAVES * 64) {
-    const int rr = idx / nbk, cc = idx % nbk;
-    sc_lds[rr * srow + cc] = rr < rows_here ? ws[(int64_t)(n0 + rr) * nbk + cc] : (uint16_t)0;
-  }
-
-  const bool col_ok = r < M;
-  const float *xrow = X + (int64_t)(col_ok ? r : 0) * K;
-  const int8_t *arow[RT];
-  bool aok[RT];
-#pragma unroll
-  for (int t = 0; t < RT; ++t) {
-    const int row = n0 + 16 * t + r;
-    aok[t] = row < N;
-    arow[t] = wq + (int64_t)(aok[t] ? row : 0) * K;
-  }
-  const int b_begin = (wv * nbk) / Q8_WAVES, b_end = ((wv + 1) * nbk) / Q8_WAVES;
-  f32x4 acc[RT];
-#pragma unroll
-  for (int t = 0; t < RT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  __syncthreads();
-
-  constexpr int PF = 4;  // blocks of weights in flight per lane
-  u32x2 a_buf[PF][RT];
-#pragma unroll
-  for (int p = 0; p < PF; ++p)
-#pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      const int b = b_begin + p;
-      a_buf[p][t] = (aok[t] && b < b_end) ? *(const u32x2 *)(arow[t] + 32 * b + 8 * q) : u32x2{0u, 0u};
-    }
-
-  for (int b0 = b_begin; b0 < b_end; b0 += PF) {
-#pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      const int b = b0 + p;
-      if (b >= b_end) break;
-      u32x2 a_cur[RT];
-#pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        a_cur[t] = a_buf[p][t];
-        const int bn = b + PF;
-        a_buf[p][t] = (aok[t] && bn < b_end) ? *(const u32x2 *)(arow[t] + 32 * bn + 8 * q) : u32x2{0u, 0u};
-      }
-      // B: X[col r][32b + 8q .. +8] split in three exact bf16 parts
-      f32x4 x0 = f32x4{0.f, 0.f, 0.f, 0.f}, x1 = x0;
-      if (col_ok) {
-        x0 = *(const f32x4 *)(xrow + 32 * b + 8 * q);
-        x1 = *(const f32x4 *)(xrow + 32 * b + 8 * q + 4);
-      }
-      uint32_t hi[8], mi[8], lo[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        split3_trunc(x0[e], hi[e], mi[e], lo[e]);
-        split3_trunc(x1[e], hi[e + 4], mi[e + 4], lo[e + 4]);
-      }
-      u32x4 ph, pm, pl;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        ph[e] = hi[2 * e] | (hi[2 * e + 1] << 16);
-        pm[e] = mi[2 * e] | (mi[2 * e + 1] << 16);
-        pl[e] = lo[2 * e] | (lo[2 * e + 1] << 16);
-      }
-      const bf16x8 bh = bits_to_bf16x8(ph), bm = bits_to_bf16x8(pm), bl = bits_to_bf16x8(pl);
-#pragma unroll
-      for (int t = 0; t < RT; ++t) {
-        u32x4 av;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint32_t wdw = a_cur[t][h];
-          const uint32_t e0 = i8_to_bf16_bits((int)(int8_t)(wdw & 0xFF));
-          const uint32_t e1 = i8_to_bf16_bits((int)(int8_t)((wdw >> 8) & 0xFF));
-          const uint32_t e2 = i8_to_bf16_bits((int)(int8_t)((wdw >> 16) & 0xFF));
-          const uint32_t e3 = i8_to_bf16_bits((int)(int8_t)(wdw >> 24));
-          av[2 * h] = e0 | (e1 << 16);
-          av[2 * h + 1] = e2 | (e3 << 16);
-        }
-        const bf16x8 a = bits_to_bf16x8(av);
-        f32x4 p = mfma16x16x32(a, bh, f32x4{0.f, 0.f, 0.f, 0.f});
-        p = mfma16x16x32(a, bm, p);
-        p = mfma16x16x32(a, bl, p);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rr = 16 * t + 4 * q + i;
-          const float s = half_bits_to_f32(sc_lds[rr * srow + b]);
-          acc[t][i] = __builtin_fmaf(p[i], s, acc[t][i]);
-        }
-      }
-    }
-  }
-
-  // fixed-order sum of the 4 K quarters
-  __syncthreads();
-  float *red = (float *)smem;  // [wave][RT*4][64]
+  f32x4 acc[RT][NMF];
 #pragma unroll
   for (int t = 0; t < RT; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[(wv * RT * 4 + t * 4 + i) * 64 + lane] = acc[t][i];
-  __syncthreads();
-  for (int idx = tid; idx < RT * 4 * 64; idx += Q8_WAVES * 64) {
-    const int ln = idx & 63, ti = idx >> 6;
-    float v = 0.f;
+    for (int mf = 0; mf < NMF; ++mf) acc[t][mf] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (row0 < N) {  // uniform per wave
+    const int s_begin = (int)((int64_t)part * ns / KS), s_end = (int)((int64_t)(part + 1) * ns / KS);
+    const int b_end = 2 * s_end < nb ? 2 * s_end : nb;
+    const int nchunks = (s_end - s_begin + kQ8Chunk - 1) / kQ8Chunk;
+    const int rows_here = N - row0 < RT * 16 ? N - row0 : RT * 16;
+
+    // weights and scales of this wave's rows; rows past N read row N-1
+    const rsrc_t wrs = make_rsrc(wq + (int64_t)row0 * K, (uint32_t)rows_here * (uint32_t)K);
+    const rsrc_t srs = make_rsrc(ws + (int64_t)row0 * nb, (uint32_t)rows_here * (uint32_t)nb * 2u);
+    uint32_t woff[RT], soff[RT];
 #pragma unroll
-    for (int w = 0; w < Q8_WAVES; ++w) v += red[(w * RT * 4 + ti) * 64 + ln];
-    const int col = ln & 15;
-    const int t = ti >> 2, i = ti & 3;
-    const int row = n0 + 16 * t + 4 * (ln >> 4) + i;
-    if (col < M && row < N) Y[(int64_t)col * N + row] = v;
+    for (int t = 0; t < RT; ++t) {
+      const int rr = 16 * t + r < rows_here ? 16 * t + r : rows_here - 1;
+      woff[t] = (uint32_t)rr * (uint32_t)K + 16u * q;
+      soff[t] = (uint32_t)rr * (uint32_t)nb * 2u;
+    }
+    // X: lane handles row xm, elements xk .. xk+EPL-1 of each step's 64
+    constexpr int LPR = 64 / EPL;
+    const int xm = lane / LPR, xk = (lane % LPR) * EPL;
+    const rsrc_t xrs = make_rsrc(X, (uint32_t)M * (uint32_t)K * 4u);
+    const uint32_t xoff = xm < M ? ((uint32_t)xm * (uint32_t)K + (uint32_t)xk) * 4u : kOOB;
+    // where this lane's split goes: block j, lane group g, column 3 xm + p
+    const int xj = xk >> 5, xg8 = (xk & 31) >> 3, xe = xk & 7;
+    const int xg = ((xg8 & 1) << 1) | (xg8 >> 1);
+    const uint32_t xdst = xm < M ? (uint32_t)(((xj * 4 + xg) * L::kCols + 3 * xm) * 16 + 2 * xe) : (uint32_t)L::kFrag;
+    const uint32_t xpstep = xm < M ? 16u : 0u;  // next part's column (dummy stays put)
+    // fragment reads: lane (r, q) reads column 16 mf + r of lane group q
+    const uint32_t frd = (uint32_t)((q * L::kCols + r) * 16);
+    // scale bpermute source addresses: output row 4q + i lives in lane 4q + i
+    int baddr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) baddr[i] = (4 * q + i) * 4;
+
+    // zero the fragment area once: columns >= 3M are never written
+#pragma unroll
+    for (int i = 0; i < L::kFrag / (64 * 16); ++i)
+      *(u32x4 *)(wl + (i * 64 + lane) * 16) = u32x4{0u, 0u, 0u, 0u};
+
+    u32x4 wr[PF][RT];
+    uint32_t xr[PF][EPL];
+    uint32_t sc_cur[RT][4], sc_nxt[RT][4];
+
+    auto issue = [&](int s, int slot) {
+      const bool live_step = s < s_end;  // uniform
+      const uint32_t wstep = live_step ? 64u * (uint32_t)s : kDead;
+      const uint32_t xstep = live_step ? 256u * (uint32_t)s : kDead;
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        uint32_t o = woff[t];
+        if constexpr (MASKED) o = 2 * s + (q >> 1) < b_end ? o : kOOB;
+        wr[slot][t] = buf_load16(wrs, o + wstep);
+      }
+      uint32_t xo = xoff;
+      if constexpr (MASKED) xo = 2 * s + xj < b_end ? xo : kOOB;
+      xo += xstep;
+      if constexpr (EPL == 8) {
+        const u32x4 a = buf_load16(xrs, xo), b = buf_load16(xrs, xo + 16u);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xr[slot][e] = a[e];
+          xr[slot][4 + e] = b[e];
+        }
+      } else if constexpr (EPL == 4) {
+        const u32x4 a = buf_load16(xrs, xo);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xr[slot][e] = a[e];
+      } else if constexpr (EPL == 2) {
+        const u32x2 a = buf_load8(xrs, xo);
+        xr[slot][0] = a[0];
+        xr[slot][1] = a[1];
+      } else {
+        xr[slot][0] = buf_load4(xrs, xo);
+      }
+    };
+    // scales of chunk c: lane (r, q) takes the 8 fp16 of row r for blocks
+    // 2 s_begin + 32 c + 8 q .. +7 (one 64-byte piece of the row per 4 lanes)
+    auto load_scales = [&](int c, uint32_t (&sc)[RT][4]) {
+      const int b = 2 * s_begin + 2 * kQ8Chunk * c + 8 * q;
+      const uint32_t gs = c < nchunks ? 0u : kDead;  // uniform
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        if constexpr (!MASKED) {
+          const u32x4 v = buf_load16(srs, soff[t] + 2u * (uint32_t)b + gs);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sc[t][e] = v[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int b0 = b + 2 * e;
+            const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(
+                srs, (b0 < b_end ? soff[t] + 2u * (uint32_t)b0 : kOOB) + gs, 0, 0);
+            const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(
+                srs, (b0 + 1 < b_end ? soff[t] + 2u * (uint32_t)b0 + 2u : kOOB) + gs, 0, 0);
+            sc[t][e] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+          }
+        }
+      }
+    };
+
+    load_scales(0, sc_cur);
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      issue(s_begin + i, i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // start the loop with nothing in flight, so the waits inside it are the
+    // steady-state ones (one slot's loads at a time); the empty asm keeps the
+    // compiler from sinking the prefill loads below the wait
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    asm volatile("" ::: "memory");
+
+    // a do-while: every part has at least one step (at most ns parts), and a
+    // loop guard would let the compiler sink the prefill into the guarded block
+    int c = 0;
+    do {
+      load_scales(c + 1, sc_nxt);
+#pragma unroll
+      for (int u = 0; u < kQ8Chunk; ++u) {
+        const int s = s_begin + kQ8Chunk * c + u;
+        const int slot = u % PF;
+        // 1. split this step's X into the fragment area
+        {
+          uint32_t hp[EPL], mp[EPL], lp[EPL];
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) q8_split3(__uint_as_float(xr[slot][e]), hp[e], mp[e], lp[e]);
+          uint32_t d = xdst;
+#pragma unroll
+          for (int p = 0; p < 3; ++p) {
+            const uint32_t *src = p == 0 ? hp : (p == 1 ? mp : lp);
+            if constexpr (EPL == 8) {
+              *(u32x4 *)(wl + d) = u32x4{q8_pack_hi16(src[0], src[1]), q8_pack_hi16(src[2], src[3]),
+                                         q8_pack_hi16(src[4], src[5]), q8_pack_hi16(src[6], src[7])};
+            } else if constexpr (EPL == 4) {
+              *(u32x2 *)(wl + d) = u32x2{q8_pack_hi16(src[0], src[1]), q8_pack_hi16(src[2], src[3])};
+            } else if constexpr (EPL == 2) {
+              *(uint32_t *)(wl + d) = q8_pack_hi16(src[0], src[1]);
+            } else {
+              *(uint16_t *)(wl + d) = (uint16_t)(src[0] >> 16);
+            }
+            d += xpstep;
+          }
+        }
+        // 2. weights of both blocks as bf16 A fragments
+        bf16x8 a[RT][2];
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          const u32x4 v = wr[slot][t];
+          const auto s02 = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+          const auto s13 = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+          const u32x2 a0 = q8_i8x4_to_bf16(s02[0]), a1 = q8_i8x4_to_bf16(s13[0]);
+          const u32x2 b0 = q8_i8x4_to_bf16(s02[1]), b1 = q8_i8x4_to_bf16(s13[1]);
+          a[t][0] = bits_to_bf16x8(u32x4{a0[0], a0[1], a1[0], a1[1]});
+          a[t][1] = bits_to_bf16x8(u32x4{b0[0], b0[1], b1[0], b1[1]});
+        }
+        // 3. this step's scales (row 4q + i; low half block 2s, high half 2s+1)
+        uint32_t sv[RT][4];
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sv[t][i] = (uint32_t)__builtin_amdgcn_ds_bpermute(baddr[i] + 64 * (u >> 2), (int)sc_cur[t][u & 3]);
+        // 4. per block: fresh product, scaled into the accumulators
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+          bf16x8 bfr[NMF];
+#pragma unroll
+          for (int mf = 0; mf < NMF; ++mf)
+            bfr[mf] = bits_to_bf16x8(*(const u32x4 *)(wl + frd + (uint32_t)((jb * 4 * L::kCols + 16 * mf) * 16)));
+#pragma unroll
+          for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int mf = 0; mf < NMF; ++mf) {
+              const f32x4 p = mfma16x16x32(a[t][jb], bfr[mf], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float sc = jb == 0 ? q8_f16_lo(sv[t][i]) : q8_f16_hi(sv[t][i]);
+                acc[t][mf][i] = __builtin_fmaf(p[i], sc, acc[t][mf][i]);
+              }
+            }
+        }
+        // 5. refill the slot
+        issue(s + PF, slot);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc_cur[t][e] = sc_nxt[t][e];
+    } while (++c < nchunks);
+  }
+
+  // partial sums of this wave -> LDS (its own area), then a fixed-order sum
+  float *pw = (float *)wl;
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int mf = 0; mf < NMF; ++mf)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pw[((t * NMF + mf) * 4 + i) * 65 + lane] = acc[t][mf][i];
+  lds_barrier();
+  const int per_rg = RT * 16 * M;
+  for (int it = tid; it < RG * per_rg; it += blockDim.x) {
+    const int g = it / per_rg, rem = it - g * per_rg;
+    const int m = rem / (RT * 16), row = rem - m * (RT * 16);
+    const int n = (blockIdx.x * RG + g) * RT * 16 + row;
+    if (n >= N) continue;
+    const int t = row >> 4, qq = (row >> 2) & 3, i = row & 3;
+    float part_sum[3];
+#pragma unroll
+    for (int p = 0; p < 3; ++p) {
+      const int col = 3 * m + p, mf = col >> 4, c = col & 15;
+      const int idx = ((t * NMF + mf) * 4 + i) * 65 + 16 * qq + c;
+      float v = ((const float *)(smem + (g * KS) * L::kWave))[idx];
+      for (int w = 1; w < KS; ++w) v += ((const float *)(smem + (g * KS + w) * L::kWave))[idx];
+      part_sum[p] = v;
+    }
+    Y[(int64_t)m * N + n] = (part_sum[0] + part_sum[1]) + part_sum[2];
   }
 }
 
-template <int RT>
-static int q8_launch_rt(const float *X, int M, int K, const int8_t *wq, const uint16_t *ws, int N, float *Y,
-                        hipStream_t stream) {
-  const int nbk = K / 32;
-  const size_t sc = (size_t)RT * 16 * (nbk + 2) * sizeof(uint16_t);
-  const size_t rd = (size_t)Q8_WAVES * RT * 4 * 64 * sizeof(float);
-  const size_t smem = sc > rd ? sc : rd;
-  const int grid = (N + RT * 16 - 1) / (RT * 16);
-  hipLaunchKernelGGL(q8_0_kernel<RT>, dim3(grid), dim3(Q8_WAVES * 64), smem, stream, X, M, K, wq, ws, N, Y);
+// Launch one configuration.  KS K parts x RG row groups = waves per workgroup;
+// WPE is the register budget as a target of resident waves per SIMD.
+template <int RT, int PF, int EPL, int NMF, bool MASKED, int WPE>
+static int q8_run(const float *X, int M, int K, const int8_t *wq, const uint16_t *ws, int N, float *Y, int KS,
+                  int RG, hipStream_t stream) {
+  using L = Q8Lds<RT, NMF>;
+  if (KS < 1 || RG < 1 || KS * RG > Q8_MAX_WAVES || M > EPL || 3 * M > 16 * NMF) return -3;
+  const size_t smem = (size_t)KS * RG * L::kWave;
+  auto kern = q8_0_kernel<RT, PF, EPL, NMF, MASKED, WPE>;
+  if (smem > 65536 &&
+      hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
+    return -3;
+  const int64_t groups = ((int64_t)N + RT * 16 - 1) / (RT * 16);
+  const int64_t grid = (groups + RG - 1) / RG;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * KS * RG), smem, stream, X, M, K, wq, ws, N, Y, KS, RG);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
+// K parts depend on K and N only, so every M sees the same reduction order.
+// The fast path needs whole 16-step chunks per part.
+static int q8_k_parts(int K, int N) {
+  const int ns = (K / 32 + 1) / 2;
+  const int64_t tiles = ((int64_t)N + 15) / 16;
+  const int target = tiles >= 4096 ? 1 : Q8_MAX_WAVES;
+  if (ns % kQ8Chunk == 0) {
+    for (int ks = target; ks >= 1; --ks)
+      if ((ns / kQ8Chunk) % ks == 0) return ks;
+  }
+  return target < ns ? target : ns;
+}
+
+static bool q8_fast_path(int K, int KS, const uint16_t *ws) {
+  const int nb = K / 32, ns = (nb + 1) / 2;
+  return nb % 8 == 0 && ns % (kQ8Chunk * KS) == 0 && reinterpret_cast<uintptr_t>(ws) % 16 == 0;
+}
+
+// Launch shapes by X rows and weight size (measured on MI355X); none of them
+// changes the arithmetic, which depends on K and N only.
 int q8_0_launch(const float *X, int M, int K, const int8_t *wq, const uint16_t *ws, int N, float *Y,
                 hipStream_t stream) {
-  if (N <= 16384) return q8_launch_rt<2>(X, M, K, wq, ws, N, Y, stream);
-  return q8_launch_rt<4>(X, M, K, wq, ws, N, Y, stream);
+  const int KS = q8_k_parts(K, N);
+  const int RG = Q8_MAX_WAVES / KS >= 4 ? 4 : 1;
+  const bool big = ((int64_t)N + 15) / 16 >= 4096;
+  if (!q8_fast_path(K, KS, ws)) {
+    if (M <= 1) return q8_run<2, 4, 1, 1, true, 1>(X, M, K, wq, ws, N, Y, KS, RG, stream);
+    if (M <= 2) return q8_run<2, 4, 2, 1, true, 1>(X, M, K, wq, ws, N, Y, KS, RG, stream);
+    if (M <= 4) return q8_run<2, 4, 4, 1, true, 1>(X, M, K, wq, ws, N, Y, KS, RG, stream);
+    if (M <= 5) return q8_run<2, 4, 8, 1, true, 1>(X, M, K, wq, ws, N, Y, KS, RG, stream);
+    return q8_run<2, 4, 8, 2, true, 1>(X, M, K, wq, ws, N, Y, KS, RG, stream);
+  }
+  if (M <= 1)
+    return big ? q8_run<2, 4, 1, 1, false, 1>(X, M, K, wq, ws, N, Y, KS, RG, stream)
+               : q8_run<1, 4, 1, 1, false, 6>(X, M, K, wq, ws, N, Y, KS, RG, stream);
+  if (M <= 2)
+    return big ? q8_run<2, 4, 2, 1, false, 1>(X, M, K, wq, ws, N, Y, KS, RG, stream)
+               : q8_run<1, 4, 2, 1, false, 1>(X, M, K, wq, ws, N, Y, KS, RG, stream);
+  if (M <= 4)
+    return big ? q8_run<2, 4, 4, 1, false, 1>(X, M, K, wq, ws, N, Y, KS, RG, stream)
+               : q8_run<2, 2, 4, 1, false, 5>(X, M, K, wq, ws, N, Y, KS, RG, stream);
+  if (M <= 5)
+    return big ? q8_run<2, 4, 8, 1, false, 1>(X, M, K, wq, ws, N, Y, KS, RG, stream)
+               : q8_run<2, 2, 8, 1, false, 4>(X, M, K, wq, ws, N, Y, KS, RG, stream);
+  return big ? q8_run<4, 2, 8, 2, false, 1>(X, M, K, wq, ws, N, Y, KS, RG, stream)
+             : q8_run<2, 2, 8, 2, false, 4>(X, M, K, wq, ws, N, Y, KS, RG, stream);
 }
 
 }  // namespace moe

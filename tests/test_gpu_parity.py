@@ -414,8 +414,9 @@ def _q8(seed, K, N, M):
     return X, wq, ws
 
 
-@pytest.mark.parametrize("K,N", [(7168, 7168), (256, 100), (96, 33), (7168, 18432)])
-@pytest.mark.parametrize("M", [1, 2, 4, 8])
+@pytest.mark.parametrize("K,N,M", [(K, N, M) for (K, N) in [(7168, 7168), (256, 100), (96, 33), (7168, 18432)]
+                                    for M in (1, 2, 4, 8)]
+                         + [(K, N, M) for (K, N) in [(7168, 7168), (512, 70)] for M in (3, 5, 6, 7)])
 def test_q8_0_parity(K, N, M):
     moe = _moe()
     X, wq, ws = _q8(10, K, N, M)
@@ -436,7 +437,26 @@ def test_q8_0_large_sampled_and_row_invariance():
     cols = np.sort(synth.rng(12).choice(N, 512, replace=False))
     ref = oracle.q8_0_matmul(X, wq[cols], ws[cols])
     assert_close(y8[:, cols], ref, "q8_0 163840 sampled")
-    for M in (1, 2, 4):
+    for M in (1, 2, 3, 4, 5, 6, 7):
         YM = torch.empty((M, N), dtype=torch.float32, device="cuda")
         moe.q8_0_matmul(_dev(X[:M]), dwq, dws, YM)
         assert np.array_equal(_host(YM).view(np.uint8), y8[:M].view(np.uint8)), M
+
+
+def test_q8_0_unaligned_scales():
+    """A scale plane that is not 16-byte aligned takes the per-element load
+    path; the result is the oracle's, and bit-identical to the aligned call."""
+    moe = _moe()
+    K, N, M = 7168, 300, 3
+    X, wq, ws = _q8(13, K, N, M)
+    dwq = _dev(wq)
+    flat = torch.zeros(N * (K // 32) + 8, dtype=torch.int16, device="cuda")
+    dws_u = flat[1:1 + N * (K // 32)].view(N, K // 32)  # 2 bytes past a 16-byte boundary
+    dws_u.copy_(torch.from_numpy(ws.view(np.int16)))
+    assert dws_u.data_ptr() % 16 != 0
+    Yu = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    Ya = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    moe.q8_0_matmul(_dev(X), dwq, dws_u, Yu)
+    moe.q8_0_matmul(_dev(X), dwq, _dev(ws, torch.int16), Ya)
+    assert_close(_host(Yu), oracle.q8_0_matmul(X, wq, ws), "q8_0 unaligned scales")
+    assert np.array_equal(_host(Yu).view(np.uint8), _host(Ya).view(np.uint8))
