@@ -42,7 +42,25 @@ struct GroupSrc {
   const int32_t *n_groups; // plan mode
 };
 
-__device__ __forceinline__ bool load_group(const GroupSrc &src, int g, int &expert, int &start, int &count) {
+__device__ __forceinline__ int group_count(const GroupSrc &src) { return src.groups ? *src.n_groups : *src.n_active; }
+
+// The chip's 8 XCDs each have their own L2, and workgroup i of a launch runs
+// on XCD i % 8.  Work items (group, row tile) are handed out so that XCD x
+// takes a contiguous run of the real items in order: the workgroups of one
+// group then share an L2 and read the group's B operand (x or h) from it
+// instead of from HBM once per workgroup.  The grid holds at least the real
+// item count rounded up to a multiple of 8; returns -1 for a workgroup
+// without an item.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_item(int real) {
+  const int x = (int)(blockIdx.x % kXcds), j = (int)(blockIdx.x / kXcds);
+  const int per = (real + kXcds - 1) / kXcds;
+  const int w = x * per + j;
+  return (j < per && w < real) ? w : -1;
+}
+
+__device__ __forceinline__ bool load_group(const GroupSrc &src, int g, int &expert, int &start, int &count,
+                                           int maxc) {
   if (src.groups) {
     if (g >= *src.n_groups) return false;
     const int4 v = src.groups[g];
@@ -53,50 +71,89 @@ __device__ __forceinline__ bool load_group(const GroupSrc &src, int g, int &expe
     start = src.offsets[expert];
     count = src.offsets[expert + 1] - start;
   }
-  count = count < kGroupCols ? count : kGroupCols;
+  count = count < maxc ? count : maxc;
   return count > 0;
 }
 
-// One workgroup: cut every active expert's segment into groups of <= 16 slots.
+// Many rows: one workgroup cuts every active expert's segment into groups
+// and sorts them into three lists by width (without `wide`, every segment is
+// cut into narrow groups of 16, all in list 0).  An expert with at most 16 slots
+// is one narrow group; a longer segment is cut into groups of 64 slots, and
+// its remainder (if any) is a narrow (<= 16), a 32-wide (17..32) or a 64-wide
+// (33..63) group.  Lists: class 0 narrow, 1 up to 32 slots, 2 up to 64.
+constexpr int kWideCols = 64;
+constexpr int kGroupClasses = 3;
+
+__device__ __forceinline__ int group_class(int cnt) { return cnt <= kGroupCols ? 0 : (cnt <= 32 ? 1 : 2); }
+
 __global__ __launch_bounds__(1024) void plan_groups_kernel(const int32_t *offsets, const int32_t *active,
-                                                           const int32_t *n_active, int4 *groups,
-                                                           int32_t *n_groups) {
-  __shared__ int32_t wave_tot[16];
+                                                           const int32_t *n_active, int4 *groups0, int4 *groups1,
+                                                           int4 *groups2, int32_t *n_groups, int wide) {
+  __shared__ int32_t wave_tot[kGroupClasses][16];
   const int na = *n_active;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  int running = 0;  // groups emitted by earlier passes
+  int4 *const lists[kGroupClasses] = {groups0, groups1, groups2};
+  int running[kGroupClasses] = {0, 0, 0};  // groups emitted by earlier passes, per class
   for (int base = 0; base < na; base += 1024) {
     const int i = base + tid;
-    int cnt = 0, ng = 0, e = 0;
+    int cnt = 0, e = 0;
+    int ng[kGroupClasses] = {0, 0, 0};
     if (i < na) {
       e = active[i];
       cnt = offsets[e + 1] - offsets[e];
-      ng = (cnt + kGroupCols - 1) / kGroupCols;
+      if (!wide) {
+        ng[0] = (cnt + kGroupCols - 1) / kGroupCols;
+      } else if (cnt <= kGroupCols) {
+        ng[0] = cnt > 0 ? 1 : 0;
+      } else {
+        const int full = cnt / kWideCols, rem = cnt - full * kWideCols;
+        ng[2] = full;
+        if (rem > 0) ++ng[group_class(rem)];
+      }
     }
-    int v = ng;  // inclusive scan of ng over the workgroup
-    for (int o = 1; o < 64; o <<= 1) {
-      const int t = __shfl_up(v, o, 64);
-      if (lane >= o) v += t;
+    int excl[kGroupClasses], total[kGroupClasses];
+#pragma unroll
+    for (int c = 0; c < kGroupClasses; ++c) {
+      int v = ng[c];  // inclusive scan over the workgroup
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(v, o, 64);
+        if (lane >= o) v += t;
+      }
+      if (lane == 63) wave_tot[c][wv] = v;
+      __syncthreads();
+      int before = 0, tot = 0;
+      for (int w = 0; w < 16; ++w) {
+        const int t = wave_tot[c][w];
+        if (w < wv) before += t;
+        tot += t;
+      }
+      excl[c] = running[c] + before + v - ng[c];
+      total[c] = tot;
+      __syncthreads();
     }
-    if (lane == 63) wave_tot[wv] = v;
-    __syncthreads();
-    int before = 0, total = 0;
-    for (int w = 0; w < 16; ++w) {
-      const int t = wave_tot[w];
-      if (w < wv) before += t;
-      total += t;
+    if (i < na && cnt > 0) {
+      const int o = offsets[e];
+      if (!wide) {
+        for (int jj = 0; jj < ng[0]; ++jj) {
+          const int rem = cnt - jj * kGroupCols;
+          lists[0][excl[0] + jj] = make_int4(e, o + jj * kGroupCols, rem < kGroupCols ? rem : kGroupCols, 0);
+        }
+      } else if (cnt <= kGroupCols) {
+        lists[0][excl[0]] = make_int4(e, o, cnt, 0);
+      } else {
+        const int full = cnt / kWideCols, rem = cnt - full * kWideCols;
+        for (int j = 0; j < full; ++j) lists[2][excl[2] + j] = make_int4(e, o + j * kWideCols, kWideCols, 0);
+        if (rem > 0) {
+          const int c = group_class(rem);
+          lists[c][excl[c] + (c == 2 ? full : 0)] = make_int4(e, o + full * kWideCols, rem, 0);
+        }
+      }
     }
-    const int excl = running + before + v - ng;
-    for (int j = 0; j < ng; ++j) {
-      const int rem = cnt - j * kGroupCols;
-      groups[excl + j] = make_int4(e, offsets[e] + j * kGroupCols, rem < kGroupCols ? rem : kGroupCols, 0);
-    }
-    running += total;
-    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < kGroupClasses; ++c) running[c] += total[c];
   }
-  if (tid == 0) *n_groups = running;
+  if (tid < kGroupClasses) n_groups[tid] = running[tid];
 }
-
 
 // ------------------------------------------------------------------ B staging
 // Ring mode: the B operand of a step (a 128-element segment of every B row)
@@ -147,8 +204,9 @@ __host__ __device__ __forceinline__ size_t gateup_lds_bytes(int d, int pf, int n
   return gateup_dummy_off(d, pf, np, maxc, bres, rows) + 16 * 3;
 }
 // Down LDS: the scale rows (ROWS), then B (resident: 3*MAXC rows; ring: PF
-// slots of 3*MAXC rows), whose space the per-(row, column) part sums (ROWS x
-// (3*MAXC + 1) floats) reuse once the main loop is done, then the dummy area.
+// slots of 3*MAXC rows), whose space the per-(row, column) part sums of YC
+// columns at a time (ROWS x (YC + 1) floats, see down_yc) reuse once the
+// main loop is done, then the dummy area.
 __host__ __device__ __forceinline__ size_t down_b_off(int f, int rows) { return lds_align16((size_t)rows * sc_pitch(f)); }
 __host__ __device__ __forceinline__ size_t down_b_bytes(int f, int pf, int maxc, bool bres) {
   return bres ? (size_t)3 * maxc * bres_row_bytes(f) : (size_t)pf * 3 * maxc * kBRow;
@@ -156,8 +214,18 @@ __host__ __device__ __forceinline__ size_t down_b_bytes(int f, int pf, int maxc,
 __host__ __device__ __forceinline__ size_t down_y_off(int f, int pf, int maxc, bool bres, int rows) {
   return down_b_off(f, rows);
 }
+// Columns of the epilogue's per-(row, column) sums held at a time: all of
+// them for up to 16 slots (or a resident B), else as many whole 16-slot
+// blocks (48 columns) as the ring slots' bytes hold.
+__host__ __device__ constexpr int down_yc(int pf, int maxc, bool bres, int rows) {
+  const int nc = 3 * maxc;
+  const int avail = (int)((size_t)pf * nc * kBRow / ((size_t)rows * 4)) - 1;
+  const int yc = avail / 48 * 48;
+  return (bres || nc <= 48) ? nc : (yc < 48 ? 48 : (yc > nc ? nc : yc));
+}
 __host__ __device__ __forceinline__ size_t down_dummy_off(int f, int pf, int maxc, bool bres, int rows) {
-  const size_t b = down_b_bytes(f, pf, maxc, bres), y = (size_t)rows * (3 * maxc + 1) * sizeof(float);
+  const int yc = down_yc(pf, maxc, bres, rows);
+  const size_t b = down_b_bytes(f, pf, maxc, bres), y = (size_t)rows * (yc + 1) * sizeof(float);
   return lds_align16(down_b_off(f, rows) + (b > y ? b : y));
 }
 __host__ __device__ __forceinline__ size_t down_lds_bytes(int f, int pf, int maxc, bool bres, int rows) {
@@ -172,68 +240,74 @@ __host__ __device__ __forceinline__ size_t down_lds_bytes(int f, int pf, int max
 // few steps, and the streaming loop is bound by the number of requests.)
 // At step s lane (r, q) reads byte 4s + q of its row: the scale of its block.
 //
-// stage_scales: rows [0, nrows) of `lds_sc` (pitch sc_pitch(K)) get the nb =
+// ScaleStage: rows [0, nrows) of `lds_sc` (pitch sc_pitch(K)) get the nb =
 // K/32 scale bytes of global weight rows row0.. (scales plane at `plane`);
-// rows at or past `rows_valid` and every tail get zeros.  Loads are issued
-// before stores, and every load is stored (to `dummy` when out of range).
+// rows at or past `rows_valid` and every tail get zeros.  begin() issues the
+// loads of the first round of pieces, end() stores them and stages any
+// further rounds (loads before stores), so that a kernel can issue begin()
+// before its ring prefill and let one wait cover both.  Every load is stored
+// (to `dummy` when out of range).
 template <bool W16>
-__device__ __forceinline__ void stage_scales(rsrc_t wr, uint32_t plane, int row0, int rows_valid, int nrows, int K,
-                                             uint8_t *lds_sc, uint32_t dummy_off, uint8_t *lds, int tid, int nth) {
-  const int nb = K >> 5, sp = sc_pitch(K);
-  if (W16) {
-    // nb is a multiple of 16: 16-byte pieces
-    const int per_row = nb >> 4, npieces = nrows * per_row;
-    constexpr int CH = 4;
-    for (int base = 0; base < npieces; base += CH * nth) {
-      u32x4 v[CH];
-      int pr[CH], pc[CH];
+struct ScaleStage {
+  static constexpr int CH = W16 ? 4 : 8;  // pieces per thread per round
+  u32x4 v16[W16 ? CH : 1];
+  uint32_t v1[W16 ? 1 : CH];
+  int pr[CH], pc[CH];
+  int per_row, npieces;
+
+  __device__ __forceinline__ void load_round(rsrc_t wr, uint32_t plane, int row0, int rows_valid, int nb, int base,
+                                             int tid, int nth) {
 #pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const int piece = base + c * nth + tid;
-        pr[c] = piece / per_row;
-        pc[c] = piece - pr[c] * per_row;
-        const bool ok = piece < npieces && pr[c] < rows_valid;
-        v[c] = buf_load16(wr, ok ? plane + (uint32_t)(row0 + pr[c]) * (uint32_t)nb + 16u * pc[c] : kOOB);
-      }
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const bool live = base + c * nth + tid < npieces;
-        *(u32x4 *)(live ? lds_sc + pr[c] * sp + 16 * pc[c] : lds + dummy_off) = v[c];
-      }
+    for (int c = 0; c < CH; ++c) {
+      const int piece = base + c * nth + tid;
+      pr[c] = piece / per_row;
+      pc[c] = piece - pr[c] * per_row;
+      const bool ok = piece < npieces && pr[c] < rows_valid;
+      if (W16)
+        v16[c] = buf_load16(wr, ok ? plane + (uint32_t)(row0 + pr[c]) * (uint32_t)nb + 16u * pc[c] : kOOB);
+      else
+        v1[c] = buf_load1(wr, ok ? plane + (uint32_t)(row0 + pr[c]) * (uint32_t)nb + (uint32_t)pc[c] : kOOB);
     }
-  } else {
-    const int npieces = nrows * nb;
-    constexpr int CH = 8;
-    for (int base = 0; base < npieces; base += CH * nth) {
-      uint32_t v[CH];
-      int pr[CH], pc[CH];
+  }
+  __device__ __forceinline__ void store_round(uint8_t *lds_sc, int sp, uint32_t dummy_off, uint8_t *lds, int base,
+                                              int tid, int nth) {
 #pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const int piece = base + c * nth + tid;
-        pr[c] = piece / nb;
-        pc[c] = piece - pr[c] * nb;
-        const bool ok = piece < npieces && pr[c] < rows_valid;
-        v[c] = buf_load1(wr, ok ? plane + (uint32_t)(row0 + pr[c]) * (uint32_t)nb + (uint32_t)pc[c] : kOOB);
-      }
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const bool live = base + c * nth + tid < npieces;
-        *(live ? lds_sc + pr[c] * sp + pc[c] : lds + dummy_off) = (uint8_t)v[c];
+    for (int c = 0; c < CH; ++c) {
+      const bool live = base + c * nth + tid < npieces;
+      if (W16)
+        *(u32x4 *)(live ? lds_sc + pr[c] * sp + 16 * pc[c] : lds + dummy_off) = v16[c];
+      else
+        *(live ? lds_sc + pr[c] * sp + pc[c] : lds + dummy_off) = (uint8_t)v1[c];
+    }
+  }
+  __device__ __forceinline__ void begin(rsrc_t wr, uint32_t plane, int row0, int rows_valid, int nrows, int K, int tid,
+                                        int nth) {
+    const int nb = K >> 5;
+    per_row = W16 ? nb >> 4 : nb;  // W16: nb is a multiple of 16, 16-byte pieces
+    npieces = nrows * per_row;
+    load_round(wr, plane, row0, rows_valid, nb, 0, tid, nth);
+  }
+  __device__ __forceinline__ void end(rsrc_t wr, uint32_t plane, int row0, int rows_valid, int nrows, int K,
+                                      uint8_t *lds_sc, uint32_t dummy_off, uint8_t *lds, int tid, int nth) {
+    const int nb = K >> 5, sp = sc_pitch(K);
+    store_round(lds_sc, sp, dummy_off, lds, 0, tid, nth);
+    for (int base = CH * nth; base < npieces; base += CH * nth) {
+      load_round(wr, plane, row0, rows_valid, nb, base, tid, nth);
+      store_round(lds_sc, sp, dummy_off, lds, base, tid, nth);
+    }
+    // zero tails: bytes [nb, sp) of every row
+    const int tail16 = (sp - (nb & ~15)) >> 4;  // 16-byte pieces from the last aligned offset
+    for (int idx = tid; idx < nrows * tail16; idx += nth) {
+      const int row = idx / tail16, c = idx - row * tail16;
+      uint8_t *pt = lds_sc + row * sp + (nb & ~15) + 16 * c;
+      if (c == 0 && (nb & 15)) {
+        for (int k = nb & 15; k < 16; ++k) pt[k] = 0;
+      } else {
+        *(u32x4 *)pt = u32x4{0u, 0u, 0u, 0u};
       }
     }
   }
-  // zero tails: bytes [nb, sp) of every row
-  const int tail16 = (sp - (nb & ~15)) >> 4;  // 16-byte pieces from the last aligned offset
-  for (int idx = tid; idx < nrows * tail16; idx += nth) {
-    const int row = idx / tail16, c = idx - row * tail16;
-    uint8_t *pt = lds_sc + row * sp + (nb & ~15) + 16 * c;
-    if (c == 0 && (nb & 15)) {
-      for (int k = nb & 15; k < 16; ++k) pt[k] = 0;
-    } else {
-      *(u32x4 *)pt = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-}
+};
 
 // Scale of lane (r, q)'s block at step s, from its LDS row.
 __device__ __forceinline__ float lds_scale(const uint8_t *row, int s, int q) {
@@ -275,10 +349,12 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
   constexpr int SPT = BRES ? 0 : (MAXC * 16 + NTH - 1) / NTH;
   constexpr int SPTA = SPT > 0 ? SPT : 1;  // array extent
   extern __shared__ __align__(16) uint8_t lds[];
-  const int g = blockIdx.x / n_ftiles;
-  const int ft = blockIdx.x - g * n_ftiles;
+  const int item = xcd_item(group_count(src) * n_ftiles);
+  if (item < 0) return;
+  const int g = item / n_ftiles;
+  const int ft = item - g * n_ftiles;
   int expert, start, count;
-  if (!load_group(src, g, expert, start, count)) return;
+  if (!load_group(src, g, expert, start, count, MAXC)) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = lane & 15, q = lane >> 4;
@@ -342,20 +418,21 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
       for (int h = 0; h < EL / 2; ++h) xst[p][i][h] = buf_load16(xr, pbase[i] + kx + 16 * h);
     }
   };
+  // the scale staging loads go first, then the ring prefill; one wait covers
+  // both (ring mode: with every load arrived the compiler sees the same loads
+  // in flight at every loop iteration, instead of keeping the prefill's issue
+  // order in mind at the loop head and waiting far deeper than the ring needs)
+  const int rv = f - i0 < ROWS ? f - i0 : ROWS;
+  ScaleStage<SX4> sg, su;
+  sg.begin(wr, plane_c, i0, rv, ROWS, d, tid, NTH);
+  su.begin(wr, 2 * plane_c + plane_s, i0, rv, ROWS, d, tid, NTH);
 #pragma unroll
   for (int p = 0; p < PF; ++p) issue(p, p);
-  // ring mode: the first loads arrive together; waiting for all of them here
-  // lets the compiler see the same loads in flight at every loop iteration
-  // (otherwise it keeps the prefill's issue order in mind at the loop head
-  // and waits far deeper than the ring needs, every iteration)
+  asm volatile("" ::: "memory");
   if constexpr (!BRES) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-
-  // scale and B staging run while the first ring loads are in flight
-  {
-    const int rv = f - i0 < ROWS ? f - i0 : ROWS;
-    stage_scales<SX4>(wr, plane_c, i0, rv, ROWS, d, lds, dummy, lds, tid, NTH);
-    stage_scales<SX4>(wr, 2 * plane_c + plane_s, i0, rv, ROWS, d, lds + ROWS * sc_pitch(d), dummy, lds, tid, NTH);
-  }
+  asm volatile("" ::: "memory");
+  sg.end(wr, plane_c, i0, rv, ROWS, d, lds, dummy, lds, tid, NTH);
+  su.end(wr, 2 * plane_c + plane_s, i0, rv, ROWS, d, lds + ROWS * sc_pitch(d), dummy, lds, tid, NTH);
   if constexpr (BRES) {
     // x of the group's columns for the whole d, 8 elements per piece, all
     // loads of a round issued before its LDS writes.  The x row of each
@@ -519,6 +596,198 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
   }
 }
 
+// ------------------------------------------------------------------ wide gate/up
+// Groups of up to 16*NCB slots (an expert with many rows): the arithmetic of
+// ffn_gateup_kernel (same decode, same K order, same parts), with NCB
+// 16-column blocks per group so that each decoded weight fragment feeds NCB
+// MFMAs per part.  Each of the GW waves owns two 16-row tiles of W_gate and
+// the same rows of W_up (ROWS = 32 GW) and forms SwiGLU itself.  The B
+// operand of a step (16*NCB columns, columns past the group's slots staged as
+// zeros) goes through an LDS ring of PF slots as in ring mode.  Scales travel
+// with the loads instead of being staged: every 4 steps lane (r, q) of a tile
+// loads the dword of its row that holds the 4 block scales of step 4j + q,
+// and at step 4j + u a bpermute from lane (r, u) hands lane (r, q) byte q.
+// Needs d % 128 == 0 (dword-aligned scale rows).
+template <int XBF16, int GW, int PF, int NCB>
+__global__ __launch_bounds__(GW * 64) void ffn_gateup_wide_kernel(
+    const void *__restrict__ x, int d, int f, int kps, int n_slots, const uint8_t *__restrict__ experts,
+    int64_t stride, GroupSrc src, const int32_t *__restrict__ perm, int n_ftiles, uint16_t *__restrict__ h_ws) {
+  static_assert(4 % PF == 0 && PF >= 2, "ring depth divides the 4-step scale group");
+  constexpr int NT = 4;  // W_gate rows +0, +16; W_up rows +0, +16
+  constexpr int ROWS = GW * 32;
+  constexpr int MAXC = 16 * NCB;
+  constexpr int NP = XBF16 ? 1 : 3;
+  constexpr int EL = XBF16 ? 2 : 4;
+  constexpr int NTH = GW * 64;
+  constexpr int SPT = (MAXC * 16 + NTH - 1) / NTH;
+  constexpr uint32_t SLOT = (uint32_t)NP * MAXC * kBRow;
+  extern __shared__ __align__(16) uint8_t lds[];
+  const int item = xcd_item(group_count(src) * n_ftiles);
+  if (item < 0) return;
+  const int g = item / n_ftiles;
+  const int ft = item - g * n_ftiles;
+  int expert, start, count;
+  if (!load_group(src, g, expert, start, count, MAXC)) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int r = lane & 15, q = lane >> 4;
+  const int i0 = ft * ROWS;
+  const int nb = d >> 5;
+  const uint32_t plane_c = (uint32_t)((int64_t)f * d / 2), plane_s = (uint32_t)((int64_t)f * d / 32);
+  const rsrc_t wr = make_rsrc(experts + (int64_t)expert * stride, (uint32_t)stride);
+  const int M = n_slots / kps;
+  const rsrc_t xr = make_rsrc(x, (uint32_t)((int64_t)M * d * EL));
+  const uint32_t dummy = PF * SLOT;
+
+  uint32_t pbase[SPT];
+  int pcol[SPT], pel[SPT];
+#pragma unroll
+  for (int i = 0; i < SPT; ++i) {
+    const int piece = tid + i * NTH;
+    pcol[i] = piece >> 4;
+    pel[i] = (piece & 15) * 8;
+    const int t = perm[start + (pcol[i] < count ? pcol[i] : count - 1)];
+    pbase[i] = (piece < MAXC * 16 && pcol[i] < count && t >= 0 && t < n_slots)
+                   ? (uint32_t)(t / kps) * (uint32_t)(d * EL)
+                   : kOOB;
+  }
+  uint32_t aoff[NT], soff[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int tm = t >> 1;
+    const int row = i0 + wv * 32 + (t & 1) * 16 + r;
+    aoff[t] = sel_off(row < f, (tm ? plane_c + plane_s : 0u) + (uint32_t)row * (uint32_t)(d / 2));
+    soff[t] = sel_off(row < f, (tm ? 2 * plane_c + plane_s : plane_c) + (uint32_t)row * (uint32_t)nb + 4u * q);
+  }
+  f32x4 acc[NT][NCB];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc[t][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nsteps = (d + 127) >> 7;
+  const int smax = (d - (q << 5) + 127) >> 7;
+  const int ngroups = (nsteps + 3) >> 2;
+  u32x4 ring[PF][NT];
+  u32x4 xst[PF][SPT][EL / 2];
+  uint32_t sc_cur[NT], sc_nxt[NT];
+  auto issue = [&](int s, int p) {
+    const int kq = (s << 7) + (q << 5);
+    const uint32_t ka = s < smax ? (uint32_t)(kq >> 1) : kDead;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) ring[p][t] = buf_load16(wr, aoff[t] + ka);
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+      const int k = (s << 7) + pel[i];
+      const uint32_t kx = k < d ? (uint32_t)(k * EL) : kDead;
+#pragma unroll
+      for (int h = 0; h < EL / 2; ++h) xst[p][i][h] = buf_load16(xr, pbase[i] + kx + 16 * h);
+    }
+  };
+  auto load_sc = [&](int j, uint32_t (&sc)[NT]) {
+    const uint32_t js = j < ngroups ? 16u * (uint32_t)j : kDead;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) sc[t] = buf_load4(wr, soff[t] + js);
+  };
+
+  load_sc(0, sc_cur);
+#pragma unroll
+  for (int p = 0; p < PF; ++p) issue(p, p);
+  // start the loop with nothing in flight (the waits inside it are then the
+  // steady-state ones); the empty asm keeps the loads above the wait
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  asm volatile("" ::: "memory");
+
+  // whole groups of 4 steps: steps past d load zeros and add exact zeros
+  int j = 0;
+  do {
+    load_sc(j + 1, sc_nxt);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int s = 4 * j + u;
+      const int p = u % PF;
+      // stage x of step s into slot p (last read at step s-PF, before the
+      // previous barrier)
+#pragma unroll
+      for (int i = 0; i < SPT; ++i) {
+        const bool live = tid + i * NTH < MAXC * 16;
+        uint8_t *dst = live ? lds + p * SLOT + pcol[i] * kBRow + pel[i] * 2 : lds + dummy;
+        const uint32_t pstep = live ? MAXC * kBRow : 16;
+        if (XBF16) {
+          *(u32x4 *)dst = xst[p][i][0];
+        } else {
+          uint32_t hi[8], mi[8], lo[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) split3_bf16(__uint_as_float(xst[p][i][e >> 2][e & 3]), hi[e], mi[e], lo[e]);
+          u32x4 ph, pm, pl;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            ph[e] = hi[2 * e] | (hi[2 * e + 1] << 16);
+            pm[e] = mi[2 * e] | (mi[2 * e + 1] << 16);
+            pl[e] = lo[2 * e] | (lo[2 * e + 1] << 16);
+          }
+          *(u32x4 *)dst = ph;
+          *(u32x4 *)(dst + pstep) = pm;
+          *(u32x4 *)(dst + 2 * pstep) = pl;
+        }
+      }
+      lds_barrier();
+      float sc[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint32_t w = (uint32_t)__builtin_amdgcn_ds_bpermute((r + 16 * u) * 4, (int)sc_cur[t]);
+        sc[t] = e8m0_to_f32((w >> (8 * q)) & 0xFFu);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        bf16x8 b[NCB][NP];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+          for (int pp = 0; pp < NP; ++pp)
+            b[cb][pp] = lds_b_fragment(lds, p * SLOT + (pp * MAXC + 16 * cb + r) * kBRow + ((q << 5) + 8 * jj) * 2);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const bf16x8 a = fp4x8_to_bf16(ring[p][t][jj], sc[t]);
+#pragma unroll
+          for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int pp = 0; pp < NP; ++pp) acc[t][cb] = mfma16x16x32(a, b[cb][pp], acc[t][cb]);
+        }
+      }
+      issue(s + PF, p);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) sc_cur[t] = sc_nxt[t];
+  } while (++j < ngroups);
+
+  // SwiGLU and the exact three-part split of h, as in ffn_gateup_kernel
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    const int col = 16 * cb + r;
+    if (col < count) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int row = i0 + wv * 32 + 16 * t + 4 * q;
+        if (row < f) {
+          uint32_t hi[4], mi[4], lo[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float gv = acc[t][cb][i], uv = acc[t + 2][cb][i];
+            split3_bf16((gv / (1.0f + expf(-gv))) * uv, hi[i], mi[i], lo[i]);
+          }
+          uint16_t *hp = h_ws + (int64_t)(start + col) * 3 * f + row;
+          *(uint2 *)(hp) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+          *(uint2 *)(hp + f) = make_uint2(mi[0] | (mi[1] << 16), mi[2] | (mi[3] << 16));
+          *(uint2 *)(hp + 2 * f) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+        }
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ down
 // Workgroup = (group, DW*TPW*16 rows of d); each wave owns TPW row tiles and
 // the whole f reduction.  B = the group's h in three exact bf16 parts, three
@@ -530,26 +799,34 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
 // fixed order, independent of the column's position; the epilogue adds a
 // slot's three part sums, hi + mid, then + lo.  Lanes of columns past the
 // group's read B row 0 (those columns are never used).
-template <int TPW, int DW, int PF, int MAXC, bool SX4, bool BRES>
+template <int TPW, int DW, int PF, int MAXC, bool SX4, bool BRES, int CS>
 __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
     int d, int f, int n_slots, const uint8_t *__restrict__ experts, int64_t stride, GroupSrc src,
     const int32_t *__restrict__ perm, int n_dtiles, const uint16_t *__restrict__ h_ws, float *__restrict__ y) {
-  constexpr int ROWS = DW * TPW * 16;
+  constexpr int ROWS = DW / CS * TPW * 16;
   constexpr int NTH = DW * 64;
   constexpr int NC = 3 * MAXC;        // B rows at most
   constexpr int NCB = (NC + 15) / 16;  // column blocks at most
+  static_assert(DW % CS == 0 && NCB % CS == 0, "column split");
+  constexpr int NCBW = NCB / CS;       // column blocks per wave
   constexpr int NPIECE = NC * 16;     // ring staging pieces per step (8 elements each)
   constexpr int SPT = BRES ? 0 : (NPIECE + NTH - 1) / NTH;
   constexpr int SPTA = SPT > 0 ? SPT : 1;
-  constexpr int YP = NC + 1;  // epilogue row pitch (floats)
+  constexpr int YC = down_yc(PF, MAXC, BRES, ROWS);  // epilogue columns per phase
+  constexpr int SPP = YC / 3;                         // slots per phase
+  constexpr int NPH = (MAXC + SPP - 1) / SPP;         // epilogue phases
+  constexpr int YP = YC + 1;                          // epilogue row pitch (floats)
   extern __shared__ __align__(16) uint8_t lds[];
-  const int g = blockIdx.x / n_dtiles;
-  const int dt = blockIdx.x - g * n_dtiles;
+  const int item = xcd_item(group_count(src) * n_dtiles);
+  if (item < 0) return;
+  const int g = item / n_dtiles;
+  const int dt = item - g * n_dtiles;
   int expert, start, count;
-  if (!load_group(src, g, expert, start, count)) return;
+  if (!load_group(src, g, expert, start, count, MAXC)) return;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = lane & 15, q = lane >> 4;
+  const int cs = wv % CS, rgw = wv / CS;  // column part and row group of this wave
   const int nc = 3 * count, ncb = (nc + 15) >> 4;
   const uint32_t plane = (uint32_t)((int64_t)f * d / 2 + (int64_t)f * d / 32);
   const uint32_t dn_c = 2 * plane, dn_s = dn_c + (uint32_t)((int64_t)d * f / 2);
@@ -560,9 +837,12 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
   const uint32_t brow = bres_row_bytes(f);
   const uint32_t dummy = (uint32_t)down_dummy_off(f, PF, MAXC, BRES, ROWS);
   uint8_t *const bmem = lds + down_b_off(f, ROWS);  // B area (after the scale rows)
-  int bsel[NCB];  // B row read by this lane in each column block
+  int bsel[NCBW];  // B row read by this lane in each of its column blocks
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) bsel[cb] = cb * 16 + r < nc ? cb * 16 + r : 0;
+  for (int cbl = 0; cbl < NCBW; ++cbl) {
+    const int cb = cs * NCBW + cbl;
+    bsel[cbl] = cb * 16 + r < nc ? cb * 16 + r : 0;
+  }
 
   // ring staging pieces: piece i is B row i/16, elements 8*(i%16)..+8 of the step
   uint32_t pbase[SPTA];
@@ -578,16 +858,16 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
   const uint8_t *srow[TPW];  // this lane's LDS scale row per tile
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
-    const int lrow = (wv * TPW + t) * 16 + r;
+    const int lrow = (rgw * TPW + t) * 16 + r;
     const int row = r0 + lrow;
     aoff[t] = sel_off(row < d, dn_c + (uint32_t)row * (uint32_t)(f / 2));
     srow[t] = lds + lrow * sc_pitch(f);
   }
-  f32x4 acc[TPW][NCB];
+  f32x4 acc[TPW][NCBW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) acc[t][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int cbl = 0; cbl < NCBW; ++cbl) acc[t][cbl] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nsteps = (f + 127) >> 7;
   const int smax = (f - (q << 5) + 127) >> 7;
@@ -604,16 +884,16 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
       hst[p][i] = buf_load16(hr, pbase[i] + (k < f ? (uint32_t)(k * 2) : kDead));
     }
   };
+  // scale staging loads, then the ring prefill, one wait (see the gate/up kernel)
+  const int rv = d - r0 < ROWS ? d - r0 : ROWS;
+  ScaleStage<SX4> ss;
+  ss.begin(wr, dn_s, r0, rv, ROWS, f, tid, NTH);
 #pragma unroll
   for (int p = 0; p < PF; ++p) issue(p, p);
-  // ring mode: the first loads arrive together; waiting for all of them here
-  // lets the compiler see the same loads in flight at every loop iteration
-  // (otherwise it keeps the prefill's issue order in mind at the loop head
-  // and waits far deeper than the ring needs, every iteration)
+  asm volatile("" ::: "memory");
   if constexpr (!BRES) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-
-  // scale and B staging run while the first ring loads are in flight
-  stage_scales<SX4>(wr, dn_s, r0, d - r0 < ROWS ? d - r0 : ROWS, ROWS, f, lds, dummy, lds, tid, NTH);
+  asm volatile("" ::: "memory");
+  ss.end(wr, dn_s, r0, rv, ROWS, f, lds, dummy, lds, tid, NTH);
   if constexpr (BRES) {
     // the group's nc h rows for the whole f, all loads of a round issued first
     constexpr int CH = 8;
@@ -658,15 +938,18 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
 #pragma unroll
         for (int t = 0; t < TPW; ++t) a[t] = fp4x8_to_bf16(ring[p][t][j], sc[t]);
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          if (cb < ncb) {
+        for (int cbl = 0; cbl < NCBW; ++cbl) {
+          // narrow groups skip their empty column blocks; wide groups are
+          // nearly full and run straight-line code (the extra columns read
+          // B row 0 and are never stored)
+          if (MAXC > 16 || cs * NCBW + cbl < ncb) {
             bf16x8 b;
             if constexpr (BRES)
-              b = lds_b_fragment(bmem, bsel[cb] * brow + (s < smax ? ((s << 7) + (q << 5) + 8 * j) * 2 : f * 2 + 16 * j));
+              b = lds_b_fragment(bmem, bsel[cbl] * brow + (s < smax ? ((s << 7) + (q << 5) + 8 * j) * 2 : f * 2 + 16 * j));
             else
-              b = lds_b_fragment(bmem, (p * NC + bsel[cb]) * kBRow + ((q << 5) + 8 * j) * 2);
+              b = lds_b_fragment(bmem, (p * NC + bsel[cbl]) * kBRow + ((q << 5) + 8 * j) * 2);
 #pragma unroll
-            for (int t = 0; t < TPW; ++t) acc[t][cb] = mfma16x16x32(a[t], b, acc[t][cb]);
+            for (int t = 0; t < TPW; ++t) acc[t][cbl] = mfma16x16x32(a[t], b, acc[t][cbl]);
           }
         }
       }
@@ -678,30 +961,38 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
   }
 
   // every (row, column) sum goes through LDS (in the B area: all waves are
-  // past their last B read at the barrier); each slot's three part sums are
-  // added in a fixed order and its rows written as float4
+  // past their last B read at the first barrier), SPP slots (YC columns) per
+  // phase; each slot's three part sums are added in a fixed order and its
+  // rows written as float4
   float *ys = (float *)(lds + down_y_off(f, PF, MAXC, BRES, ROWS));
-  lds_barrier();
 #pragma unroll
-  for (int t = 0; t < TPW; ++t)
+  for (int ph = 0; ph < NPH; ++ph) {
+    lds_barrier();
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-      if (cb * 16 + r < nc)
+    for (int t = 0; t < TPW; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ys[((wv * TPW + t) * 16 + 4 * q + i) * YP + cb * 16 + r] = acc[t][cb][i];
-  lds_barrier();
-  for (int idx = tid; idx < count * (ROWS / 4); idx += NTH) {
-    const int j = idx / (ROWS / 4), lrow = (idx - j * (ROWS / 4)) * 4;
-    const int row = r0 + lrow;
-    const int t_slot = perm[start + j];
-    if (row < d && t_slot >= 0 && t_slot < n_slots) {
-      f32x4 v;
+      for (int cbl = 0; cbl < NCBW; ++cbl) {
+        const int col = (cs * NCBW + cbl) * 16 + r;
+        if (col >= YC * ph && col < YC * (ph + 1) && col < nc)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float *yr = ys + (lrow + i) * YP + 3 * j;
-        v[i] = (yr[0] + yr[1]) + yr[2];
+          for (int i = 0; i < 4; ++i)
+            ys[((rgw * TPW + t) * 16 + 4 * q + i) * YP + col - YC * ph] = acc[t][cbl][i];
       }
-      *(f32x4 *)(y + (int64_t)t_slot * d + row) = v;
+    lds_barrier();
+    const int j0 = SPP * ph, nj = count - j0 < SPP ? count - j0 : SPP;
+    for (int idx = tid; idx < nj * (ROWS / 4); idx += NTH) {
+      const int jl = idx / (ROWS / 4), lrow = (idx - jl * (ROWS / 4)) * 4;
+      const int row = r0 + lrow;
+      const int t_slot = perm[start + j0 + jl];
+      if (row < d && t_slot >= 0 && t_slot < n_slots) {
+        f32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float *yr = ys + (lrow + i) * YP + 3 * jl;
+          v[i] = (yr[0] + yr[1]) + yr[2];
+        }
+        *(f32x4 *)(y + (int64_t)t_slot * d + row) = v;
+      }
     }
   }
 }
@@ -709,19 +1000,33 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
 // ------------------------------------------------------------------ host side
 static inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Group list capacities with many rows: narrow groups (at most ceil(T/16) +
+// one per expert when every group is narrow), 32-wide (at most one per
+// expert, at least 17 slots each) and 64-wide (at least 33 slots each).
+static void group_caps(int64_t M, int k, int S, int n_experts, int64_t cap[kGroupClasses]) {
+  const int64_t T = M * (k + S);
+  cap[0] = (T + kGroupCols - 1) / kGroupCols + n_experts;
+  cap[1] = std::min<int64_t>(n_experts, T / 17);
+  cap[2] = T / 33;
+}
+
 int64_t ffn_max_groups(int64_t M, int k, int S, int n_experts) {
   const int64_t T = M * (k + S);
-  const int64_t ne = n_experts < T ? n_experts : T;
-  if (M <= kGroupCols) return ne;
-  return (T + kGroupCols - 1) / kGroupCols + ne;
+  if (M <= kGroupCols) return n_experts < T ? n_experts : T;
+  int64_t cap[kGroupClasses];
+  group_caps(M, k, S, n_experts, cap);
+  return cap[0] + cap[1] + cap[2];
 }
 
 size_t ffn_workspace_bytes(int64_t M, int k, int S, int d, int f, int n_experts) {
   const int64_t T = M * (k + S);
-  const int64_t maxg = ffn_max_groups(M, k, S, n_experts);
   size_t b = align_up((size_t)T * 3 * f * sizeof(uint16_t), 256);
-  b += align_up((size_t)maxg * sizeof(int4), 256);
-  b += 256;  // n_groups
+  if (M > kGroupCols) {
+    int64_t cap[kGroupClasses];
+    group_caps(M, k, S, n_experts, cap);
+    for (int c = 0; c < kGroupClasses; ++c) b += align_up((size_t)cap[c] * sizeof(int4), 256);
+  }
+  b += 256;  // group counts
   (void)d;
   return b;
 }
@@ -747,26 +1052,45 @@ static int launch_gateup(const void *x, int d, int f, int kps, int T, const uint
                          const GroupSrc &src, const int32_t *perm, int64_t maxg, uint16_t *h_ws, hipStream_t stream) {
   constexpr int ROWS = (PAIR ? GW : GW / 2) * TPW * 16;
   const int n_ftiles = (f + ROWS - 1) / ROWS;
+  if (maxg <= 0) return 0;
   const size_t smem = gateup_lds_bytes(d, PF, XBF16 ? 1 : 3, MAXC, BRES, ROWS);
   if (smem > (size_t)kMaxLds) return -3;
   static const bool lds_ok =
       allow_lds(reinterpret_cast<const void *>(&ffn_gateup_kernel<XBF16, TPW, GW, PF, MAXC, SX4, BRES, PAIR>));
   if (!lds_ok) return -3;
-  hipLaunchKernelGGL((ffn_gateup_kernel<XBF16, TPW, GW, PF, MAXC, SX4, BRES, PAIR>), dim3((unsigned)(maxg * n_ftiles)), dim3(GW * 64),
+  hipLaunchKernelGGL((ffn_gateup_kernel<XBF16, TPW, GW, PF, MAXC, SX4, BRES, PAIR>), dim3((unsigned)align_up((size_t)(maxg * n_ftiles), kXcds)), dim3(GW * 64),
                      smem, stream, x, d, f, kps, T, experts, stride, src, perm, n_ftiles, h_ws);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
-template <int TPW, int DW, int PF, int MAXC, bool SX4, bool BRES>
+template <int XBF16, int GW, int PF, int NCB>
+static int launch_gateup_wide(const void *x, int d, int f, int kps, int T, const uint8_t *experts, int64_t stride,
+                              const GroupSrc &src, const int32_t *perm, int64_t maxg, uint16_t *h_ws,
+                              hipStream_t stream) {
+  constexpr int ROWS = GW * 32;
+  const int n_ftiles = (f + ROWS - 1) / ROWS;
+  if (maxg <= 0) return 0;
+  const size_t smem = (size_t)PF * (XBF16 ? 1 : 3) * 16 * NCB * kBRow + 48;
+  if (smem > (size_t)kMaxLds) return -3;
+  static const bool lds_ok = allow_lds(reinterpret_cast<const void *>(&ffn_gateup_wide_kernel<XBF16, GW, PF, NCB>));
+  if (!lds_ok) return -3;
+  hipLaunchKernelGGL((ffn_gateup_wide_kernel<XBF16, GW, PF, NCB>), dim3((unsigned)align_up((size_t)(maxg * n_ftiles), kXcds)), dim3(GW * 64),
+                     smem, stream, x, d, f, kps, T, experts, stride, src, perm, n_ftiles, h_ws);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+template <int TPW, int DW, int PF, int MAXC, bool SX4, bool BRES, int CS>
 static int launch_down(int d, int f, int T, const uint8_t *experts, int64_t stride, const GroupSrc &src,
                        const int32_t *perm, int64_t maxg, const uint16_t *h_ws, float *y, hipStream_t stream) {
-  constexpr int ROWS = DW * TPW * 16;
+  constexpr int ROWS = DW / CS * TPW * 16;
   const int n_dtiles = (d + ROWS - 1) / ROWS;
+  if (maxg <= 0) return 0;
   const size_t smem = down_lds_bytes(f, PF, MAXC, BRES, ROWS);
   if (smem > (size_t)kMaxLds) return -3;
-  static const bool lds_ok = allow_lds(reinterpret_cast<const void *>(&ffn_down_kernel<TPW, DW, PF, MAXC, SX4, BRES>));
+  static const bool lds_ok =
+      allow_lds(reinterpret_cast<const void *>(&ffn_down_kernel<TPW, DW, PF, MAXC, SX4, BRES, CS>));
   if (!lds_ok) return -3;
-  hipLaunchKernelGGL((ffn_down_kernel<TPW, DW, PF, MAXC, SX4, BRES>), dim3((unsigned)(maxg * n_dtiles)), dim3(DW * 64), smem,
+  hipLaunchKernelGGL((ffn_down_kernel<TPW, DW, PF, MAXC, SX4, BRES, CS>), dim3((unsigned)align_up((size_t)(maxg * n_dtiles), kXcds)), dim3(DW * 64), smem,
                      stream, d, f, T, experts, stride, src, perm, n_dtiles, h_ws, y);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
@@ -781,41 +1105,59 @@ int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *exper
   uint8_t *ws = (uint8_t *)workspace;
   uint16_t *h_ws = (uint16_t *)ws;
   size_t off = align_up((size_t)T * 3 * f * sizeof(uint16_t), 256);
-  int4 *groups = (int4 *)(ws + off);
-  const int64_t maxg = ffn_max_groups(M, k, S, n_experts);
-  off += align_up((size_t)maxg * sizeof(int4), 256);
+  const bool many = M > kGroupCols;
+  // with many rows: groups of up to 64 slots where the wide gate/up kernel
+  // applies (dword-aligned scale rows)
+  const bool wide = many && d % 128 == 0;
+  int64_t cap[kGroupClasses] = {ffn_max_groups(M, k, S, n_experts), 0, 0};
+  int4 *glist[kGroupClasses] = {nullptr, nullptr, nullptr};
+  if (many) {
+    group_caps(M, k, S, n_experts, cap);
+    for (int c = 0; c < kGroupClasses; ++c) {
+      glist[c] = (int4 *)(ws + off);
+      off += align_up((size_t)cap[c] * sizeof(int4), 256);
+    }
+    if (!wide) cap[1] = cap[2] = 0;
+  }
   int32_t *n_groups = (int32_t *)(ws + off);
 
-  GroupSrc src{offsets, active, n_active, nullptr, nullptr};
-  if (M > kGroupCols) {
+  GroupSrc src[kGroupClasses];
+  for (int c = 0; c < kGroupClasses; ++c) src[c] = GroupSrc{offsets, active, n_active, nullptr, nullptr};
+  if (many) {
     // the group plan lives in the workspace and serves both stages
     if (stages & kStageGateUp) {
-      hipLaunchKernelGGL(plan_groups_kernel, dim3(1), dim3(1024), 0, stream, offsets, active, n_active, groups,
-                         n_groups);
+      hipLaunchKernelGGL(plan_groups_kernel, dim3(1), dim3(1024), 0, stream, offsets, active, n_active, glist[0],
+                         glist[1], glist[2], n_groups, wide ? 1 : 0);
       if (hipGetLastError() != hipSuccess) return -3;
     }
-    src.groups = groups;
-    src.n_groups = n_groups;
+    for (int c = 0; c < kGroupClasses; ++c) {
+      src[c].groups = glist[c];
+      src[c].n_groups = n_groups + c;
+    }
   }
   // Launch shapes only change how many rows a wave/workgroup owns and how
-  // many B columns are staged (a group never has more slots than M), never
-  // the order of any reduction: every choice gives bit-identical results.
+  // many B columns are staged (a group never has more slots than its kernel's
+  // column limit), never the order of any reduction: every choice gives
+  // bit-identical results.
   const bool gsx4 = (d / 32) % 16 == 0, dsx4 = (f / 32) % 16 == 0;
   const int T_ = (int)T;
 #define MOE_GU(XB, T, G, P, C, R, PR)                                                                          \
-  (gsx4 ? launch_gateup<XB, T, G, P, C, true, R, PR>(x, d, f, kps, T_, experts, stride, src, perm, maxg, h_ws, stream) \
-        : launch_gateup<XB, T, G, P, C, false, R, PR>(x, d, f, kps, T_, experts, stride, src, perm, maxg, h_ws, stream))
-#define MOE_DN(T, D, P, C, R)                                                                                   \
-  (dsx4 ? launch_down<T, D, P, C, true, R>(d, f, T_, experts, stride, src, perm, maxg, h_ws, y, stream) \
-        : launch_down<T, D, P, C, false, R>(d, f, T_, experts, stride, src, perm, maxg, h_ws, y, stream))
+  (gsx4 ? launch_gateup<XB, T, G, P, C, true, R, PR>(x, d, f, kps, T_, experts, stride, src[0], perm, cap[0], h_ws, stream) \
+        : launch_gateup<XB, T, G, P, C, false, R, PR>(x, d, f, kps, T_, experts, stride, src[0], perm, cap[0], h_ws, stream))
+#define MOE_GUW(XB, G, P, NCB, CL) \
+  launch_gateup_wide<XB, G, P, NCB>(x, d, f, kps, T_, experts, stride, src[CL], perm, cap[CL], h_ws, stream)
+#define MOE_DN(T, D, P, C, R, CL, CS)                                                                                   \
+  (dsx4 ? launch_down<T, D, P, C, true, R, CS>(d, f, T_, experts, stride, src[CL], perm, cap[CL], h_ws, y, stream) \
+        : launch_down<T, D, P, C, false, R, CS>(d, f, T_, experts, stride, src[CL], perm, cap[CL], h_ws, y, stream))
   // few rows: each group's B operand (x or h) stays resident in LDS for the
   // whole reduction; more rows: B is staged step by step through a ring.
   // Launch shapes (measured at the Kimi shape): gate/up 2 waves each with
   // the W_gate and W_up tiles of 16 rows (32 rows of f) and a 4-step ring at
-  // 1-2 rows, 8 waves (4 W_gate + 4 W_up) with a 4-step ring beyond; down 4 waves x 1 tile (64 rows of d) at up to 4
-  // rows, 8 waves x 2 tiles beyond (fewer workgroups per group re-stage its
-  // h).  A resident B is used only where the
-  // LDS it takes still lets two or more workgroups share a CU.
+  // 1-2 rows, 8 waves (4 W_gate + 4 W_up) with a 4-step ring beyond, and
+  // the wide kernel (8 waves x 32 rows) for the 32- and 64-slot groups; down
+  // 4 waves x 1 tile (64 rows of d) at up to 4 rows, 8 waves x 2 tiles beyond
+  // (fewer workgroups per group re-stage its h).  A resident B is used only
+  // where the LDS it takes still lets two or more workgroups share a CU.
   int rc = 0;
   if (stages & kStageGateUp) {
     const int np = x_bf16 ? 1 : 3;
@@ -824,19 +1166,26 @@ int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *exper
       if (M == 1 && gateup_lds_bytes(d, 4, np, 1, true, 32) <= half) rc = MOE_GU(1, 1, 2, 4, 1, true, true);
       else if (M == 2 && gateup_lds_bytes(d, 4, np, 2, true, 32) <= half) rc = MOE_GU(1, 1, 2, 4, 2, true, true);
       else rc = MOE_GU(1, 1, 8, 4, 16, false, false);
+      if (!rc && wide) rc = MOE_GUW(1, 8, 4, 2, 1);
+      if (!rc && wide) rc = MOE_GUW(1, 8, 4, 4, 2);
     } else {
       if (M <= 4 && gateup_lds_bytes(d, 4, np, 4, true, 32) <= half) rc = MOE_GU(0, 1, 2, 4, 4, true, true);
       else rc = MOE_GU(0, 1, 8, 4, 16, false, false);
+      if (!rc && wide) rc = MOE_GUW(0, 8, 2, 2, 1);
+      if (!rc && wide) rc = MOE_GUW(0, 8, 2, 4, 2);
     }
     if (rc) return rc;
   }
   if (stages & kStageDown) {
     const size_t half = (size_t)kMaxLds / 2;
-    if (M == 1 && down_lds_bytes(f, 4, 1, true, 64) <= half) rc = MOE_DN(1, 4, 4, 1, true);
-    else if (M <= 4 && down_lds_bytes(f, 4, 4, true, 64) <= half) rc = MOE_DN(1, 4, 4, 4, true);
-    else rc = MOE_DN(2, 8, 4, 16, false);
+    if (M == 1 && down_lds_bytes(f, 4, 1, true, 64) <= half) rc = MOE_DN(1, 4, 4, 1, true, 0, 1);
+    else if (M <= 4 && down_lds_bytes(f, 4, 4, true, 64) <= half) rc = MOE_DN(1, 4, 4, 4, true, 0, 1);
+    else rc = MOE_DN(2, 8, 4, 16, false, 0, 1);
+    if (!rc && wide) rc = MOE_DN(4, 8, 4, 32, false, 1, 2);
+    if (!rc && wide) rc = MOE_DN(4, 8, 2, 64, false, 2, 2);
   }
 #undef MOE_GU
+#undef MOE_GUW
 #undef MOE_DN
   return rc;
 }

@@ -208,6 +208,42 @@ def test_ffn_ragged_parity(shape, M):
     _compare_layer(res, ref, f"{shape.name} M={M}", shape.k, shape.n_shared)
 
 
+# d % 128 == 0: with many rows, experts with more than 16 slots are cut into
+# groups of up to 64 slots that run on the wide gate/up kernel and on the
+# 32- and 64-column down kernels
+WIDE = [
+    synth.LayerShape("w1", 256, 96, 5, 1, 2, -6, -2, 0.05, "f32"),
+    synth.LayerShape("w2", 384, 160, 6, 1, 2, -6, -2, 0.05, "bf16"),
+]
+
+
+@pytest.mark.parametrize("shape", WIDE, ids=lambda s: s.name)
+@pytest.mark.parametrize("M", [40, 90, 150])
+def test_ffn_wide_groups_parity_and_row_identity(shape, M):
+    """Parity with the oracle, and every sampled row bit-identical to the
+    same row run alone (one-row decode path)."""
+    moe = _moe()
+    ex, recs = _small_layer(shape, 21)
+    wr = synth.router_weight(shape, 21)
+    x = synth.rows_x(shape, 22, M)
+    xd = _x_dev(shape, x)
+    layer = moe.MoELayer(ex, shape.k, M, w_router=_dev(wr))
+    res = layer.forward(xd)
+    ref = oracle.layer(x, shape.k, shape.n_routed, shape.n_shared, shape.d, shape.f, recs.__getitem__, w_r=wr)
+    _compare_layer(res, ref, f"{shape.name} M={M}", shape.k, shape.n_shared)
+    counts = np.diff(ref["offsets"])
+    assert counts.max() > 32, "the case must reach the 64-wide groups"
+    one = moe.MoELayer(ex, shape.k, 1)
+    lg = res["logits"].clone()
+    for m in (0, M // 2, M - 1):
+        r1 = one.forward(xd[m:m + 1], logits=lg[m:m + 1].contiguous())
+        a = _row_outputs(res, m, shape.k, shape.n_shared)
+        b = _row_outputs(r1, 0, shape.k, shape.n_shared)
+        for key in ("ids", "w", "y", "out"):
+            assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), (m, key)
+    _stages_equal_full(moe, ex, shape.k, xd, layer, layer.forward(xd))
+
+
 def _stages_equal_full(moe, ex, k, xd, layer, res):
     """moe_ffn_gateup_mxfp4 + moe_ffn_down_mxfp4 == moe_expert_ffn_mxfp4, bit for bit."""
     y_full = _host(res["y_slots"]).copy()
