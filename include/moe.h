@@ -158,6 +158,23 @@ size_t moe_workspace_bytes(int32_t M, int32_t k, const moe_experts *W);
 int moe_combine(const float *y_slots, const float *topk_w, int32_t M, int32_t k, int32_t n_shared, int32_t d,
                 float *out, void *stream);
 
+/* One MoE layer in one call: moe_route, moe_bucket, moe_expert_ffn_mxfp4 and
+ * moe_combine in that order ("Read the experts the router needs": router,
+ * then the selected experts; "A drafter that leaves the answer unchanged":
+ * rows bucketed per expert, each expert read once, outputs combined).  Every
+ * argument means what it means there, with E = W->n_routed and d = W->d, and
+ * every output (logits when computed, topk_ids, topk_w, the bucketing
+ * arrays, dev_error, y_slots, out) is bit-identical to what those four calls
+ * give: the same kernels, enqueued by one call.
+ *   workspace  at least moe_workspace_bytes(M, k, W) bytes; contents on
+ *              entry do not matter; calls that share a workspace must not
+ *              overlap (same stream, or ordered by events).
+ * Requirements and errors are the union of the four functions'. */
+int moe_layer_mxfp4(const void *x, moe_dtype x_dtype, const float *w_router, float *logits, int32_t M, int32_t k,
+                    const moe_experts *W, int32_t *topk_ids, float *topk_w, int32_t *offsets, int32_t *perm,
+                    int32_t *active, int32_t *n_active, int32_t *dev_error, float *y_slots, float *out,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
 /* Q8_0 spine matmul ("A drafter that leaves the answer unchanged": the
  * spine's matrix multiplies load each weight once for up to eight rows;
  * "One GPU, three storage tiers": the spine's matrices are Q8_0):

@@ -22,7 +22,7 @@ MOE_F32, MOE_BF16 = 0, 1
 
 # names exported by include/moe.h
 ABI_FUNCTIONS = ("moe_route", "moe_bucket", "moe_expert_ffn_mxfp4", "moe_ffn_gateup_mxfp4", "moe_ffn_down_mxfp4",
-                 "moe_workspace_bytes", "moe_combine", "q8_0_matmul", "moe_status_str")
+                 "moe_workspace_bytes", "moe_combine", "moe_layer_mxfp4", "q8_0_matmul", "moe_status_str")
 
 
 class MoeError(RuntimeError):
@@ -52,6 +52,7 @@ def _load() -> ctypes.CDLL:
         "moe_ffn_down_mxfp4": (ctypes.c_int, [i32, i32, EP, P, P, P, P, P, P, sz, P]),
         "moe_workspace_bytes": (sz, [i32, i32, EP]),
         "moe_combine": (ctypes.c_int, [P, P, i32, i32, i32, i32, P, P]),
+        "moe_layer_mxfp4": (ctypes.c_int, [P, ctypes.c_int, P, P, i32, i32, EP, P, P, P, P, P, P, P, P, P, P, sz, P]),
         "q8_0_matmul": (ctypes.c_int, [P, i32, i32, P, P, i32, P, P]),
         "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     }
@@ -214,6 +215,36 @@ def moe_combine(y_slots, topk_w, k, n_shared, out, stream=None):
     _check("moe_combine", rc)
 
 
+def moe_layer_mxfp4(x, w_router, logits, k, experts: Experts, topk_ids, topk_w, offsets, perm, active, n_active,
+                    dev_error, y_slots, out, workspace, stream=None):
+    """One layer in one call: what moe_route, moe_bucket, moe_expert_ffn_mxfp4
+    and moe_combine give in sequence, bit for bit.  With w_router None,
+    ``logits`` [M x E] is the input."""
+    M, d = x.shape
+    E, S = experts.n_routed, experts.n_shared
+    if d != experts.d or tuple(logits.shape) != (M, E) or tuple(out.shape) != (M, d):
+        raise ValueError("x [M x d], logits [M x E] and out [M x d] must match the experts")
+    if tuple(topk_ids.shape) != (M, k) or tuple(topk_w.shape) != (M, k):
+        raise ValueError("topk outputs must be [M x k]")
+    if tuple(y_slots.shape) != (M * (k + S), d) or y_slots.dtype != torch.float32 or out.dtype != torch.float32:
+        raise ValueError("y_slots must be float32 [M*(k+S) x d], out float32")
+    for t in (topk_ids, offsets, perm, active, n_active, dev_error):
+        if t.dtype != torch.int32:
+            raise ValueError("ids and bucket tensors are int32")
+    if offsets.numel() < E + S + 1 or perm.numel() < M * (k + S) or active.numel() < E + S:
+        raise ValueError("bucket outputs too small")
+    if w_router is not None and (w_router.dtype != torch.float32 or tuple(w_router.shape) != (E, d)):
+        raise ValueError("w_router must be float32 [E x d]")
+    if workspace.dtype != torch.uint8:
+        raise ValueError("workspace must be a uint8 tensor")
+    s = experts.c_struct()
+    rc = _lib.moe_layer_mxfp4(_ptr(x), _x_dtype(x), _ptr(w_router), _ptr(logits), M, k, ctypes.byref(s),
+                              _ptr(topk_ids), _ptr(topk_w), _ptr(offsets), _ptr(perm), _ptr(active), _ptr(n_active),
+                              _ptr(dev_error), _ptr(y_slots), _ptr(out), _ptr(workspace), workspace.numel(),
+                              _stream(stream))
+    _check("moe_layer_mxfp4", rc)
+
+
 def q8_0_matmul(X, Wq, Ws, Y, stream=None):
     """Y[M x N] = X[M x K] . W^T with W in Q8_0 (int8 [N x K], fp16 bits [N x K/32])."""
     M, K = X.shape
@@ -230,7 +261,8 @@ def q8_0_matmul(X, Wq, Ws, Y, stream=None):
 # ----------------------------------------------------------------------------- one layer
 class MoELayer:
     """Buffers for one MoE layer pass over up to ``max_rows`` rows, and the pass
-    itself as the four ABI calls in order (route, bucket, expert FFN, combine)."""
+    itself: one moe_layer_mxfp4 call, or (fused=False) the four ABI calls in
+    order (route, bucket, expert FFN, combine); both give the same bits."""
 
     def __init__(self, experts: Experts, k: int, max_rows: int, w_router: torch.Tensor | None = None,
                  device="cuda"):
@@ -259,7 +291,7 @@ class MoELayer:
                     n_active=self.n_active, dev_error=self.dev_error, y_slots=self.y_slots[:M * (self.k + S)],
                     out=self.out[:M])
 
-    def forward(self, x: torch.Tensor, logits: torch.Tensor | None = None, stream=None):
+    def forward(self, x: torch.Tensor, logits: torch.Tensor | None = None, stream=None, fused: bool = True):
         """One layer pass over x [M x d].  With ``logits`` given the router
         GEMV is skipped and those logits are routed."""
         M = x.shape[0]
@@ -267,6 +299,13 @@ class MoELayer:
             raise ValueError("more rows than the layer buffers hold")
         v = self.views(M)
         E, S = self.experts.n_routed, self.experts.n_shared
+        if fused:
+            if logits is not None:
+                v["logits"] = logits
+            moe_layer_mxfp4(x, None if logits is not None else self.w_router, v["logits"], self.k, self.experts,
+                            v["topk_ids"], v["topk_w"], v["offsets"], v["perm"], v["active"], v["n_active"],
+                            v["dev_error"], v["y_slots"], v["out"], self.workspace, stream)
+            return v
         if logits is not None:
             v["logits"] = logits
             moe_route(None, None, logits, self.k, v["topk_ids"], v["topk_w"], stream)

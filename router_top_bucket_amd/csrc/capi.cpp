@@ -56,6 +56,21 @@ int run_ffn(const void *x, moe_dtype x_dtype, int32_t M, int32_t k, const moe_ex
              : MOE_EHIP;
 }
 
+int route_check(const void *x, moe_dtype x_dtype, const float *w_router, const float *logits, int32_t M, int32_t d,
+                int32_t E, int32_t k, const int32_t *topk_ids, const float *topk_w) {
+  if (M < 0 || E <= 0 || k < 1 || k > E) return MOE_EINVAL;
+  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_EINVAL;
+  if (!logits || !topk_ids || !topk_w) return MOE_EINVAL;
+  if (w_router) {
+    if (!x || d <= 0 || d % 32) return MOE_EINVAL;
+    if (reinterpret_cast<uintptr_t>(w_router) % 16 || reinterpret_cast<uintptr_t>(x) % 16) return MOE_EINVAL;
+  }
+  if (E > kMaxExperts || k > 64) return MOE_EUNSUPPORTED;
+  // router operands are addressed with 32-bit buffer offsets below 2^30
+  if (w_router && ((int64_t)E * d * 4 >= (1 << 30) || (int64_t)M * d * 4 >= (1 << 30))) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -72,17 +87,8 @@ const char *moe_status_str(int status) {
 
 int moe_route(const void *x, moe_dtype x_dtype, const float *w_router, float *logits, int32_t M, int32_t d,
               int32_t E, int32_t k, int32_t *topk_ids, float *topk_w, void *stream) {
-  if (M < 0 || E <= 0 || k < 1 || k > E) return MOE_EINVAL;
-  if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return MOE_EINVAL;
-  if (!logits || !topk_ids || !topk_w) return MOE_EINVAL;
-  if (w_router) {
-    if (!x || d <= 0 || d % 32) return MOE_EINVAL;
-    if (reinterpret_cast<uintptr_t>(w_router) % 16 || reinterpret_cast<uintptr_t>(x) % 16) return MOE_EINVAL;
-  }
-  if (E > kMaxExperts || k > 64) return MOE_EUNSUPPORTED;
-  // router operands are addressed with 32-bit buffer offsets below 2^30
-  if (w_router && ((int64_t)E * d * 4 >= (1 << 30) || (int64_t)M * d * 4 >= (1 << 30))) return MOE_EUNSUPPORTED;
-  if (M == 0) return MOE_OK;
+  const int rc = route_check(x, x_dtype, w_router, logits, M, d, E, k, topk_ids, topk_w);
+  if (rc != MOE_OK || M == 0) return rc;
   return status_of(moe::route_launch(x, x_dtype == MOE_BF16, w_router, logits, M, d, E, k, topk_ids, topk_w,
                                      as_stream(stream)));
 }
@@ -141,6 +147,28 @@ int moe_combine(const float *y_slots, const float *topk_w, int32_t M, int32_t k,
   if (reinterpret_cast<uintptr_t>(y_slots) % 16 || reinterpret_cast<uintptr_t>(out) % 16) return MOE_EINVAL;
   if (M == 0) return MOE_OK;
   return status_of(moe::combine_launch(y_slots, topk_w, M, k, n_shared, d, out, as_stream(stream)));
+}
+
+int moe_layer_mxfp4(const void *x, moe_dtype x_dtype, const float *w_router, float *logits, int32_t M, int32_t k,
+                    const moe_experts *W, int32_t *topk_ids, float *topk_w, int32_t *offsets, int32_t *perm,
+                    int32_t *active, int32_t *n_active, int32_t *dev_error, float *y_slots, float *out,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+  if (!experts_ok(W)) return MOE_EINVAL;
+  const int E = W->n_routed, S = W->n_shared, d = W->d;
+  int rc = route_check(x, x_dtype, w_router, logits, M, d, E, k, topk_ids, topk_w);
+  if (rc != MOE_OK) return rc;
+  if (!dev_error || !out || reinterpret_cast<uintptr_t>(out) % 16) return MOE_EINVAL;
+  rc = ffn_check(x, x_dtype, true, M, k, W, offsets, perm, active, n_active, y_slots, true, workspace,
+                 workspace_bytes);
+  if (rc != MOE_OK || M == 0) return rc;
+  const hipStream_t st = as_stream(stream);
+  const int bf = x_dtype == MOE_BF16;
+  if (moe::route_launch(x, bf, w_router, logits, M, d, E, k, topk_ids, topk_w, st)) return MOE_EHIP;
+  if (moe::bucket_launch(topk_ids, M, k, E, S, offsets, perm, active, n_active, dev_error, st)) return MOE_EHIP;
+  if (run_ffn(x, x_dtype, M, k, W, offsets, perm, active, n_active, y_slots, workspace,
+              moe::kStageGateUp | moe::kStageDown, stream) != MOE_OK)
+    return MOE_EHIP;
+  return status_of(moe::combine_launch(y_slots, topk_w, M, k, S, d, out, st));
 }
 
 int q8_0_matmul(const float *X, int32_t M, int32_t K, const int8_t *Wq, const uint16_t *Ws, int32_t N, float *Y,

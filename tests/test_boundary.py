@@ -156,3 +156,33 @@ def test_binding_fails_loudly_without_library(tmp_path):
             "    print('RAISED', e)\n")
     r = subprocess.run(["python", "-c", code], cwd=str(tmp_path), capture_output=True, text=True)
     assert "RAISED" in r.stdout, r.stdout + r.stderr
+
+
+def test_layer_validation():
+    import router_top_bucket_amd as moe
+    lib = moe.raw_library()
+    EINVAL, EUNSUP = moe.MOE_EINVAL, moe.MOE_EUNSUPPORTED
+    ok = _experts()
+    ws = lib.moe_workspace_bytes(2, 2, ctypes.byref(ok))
+
+    def call(x=FAKE, dt=0, wr=FAKE, lg=FAKE, M=2, k=2, ex=ok, out=FAKE, dev_error=FAKE, y=FAKE, wsp=FAKE,
+             nbytes=ws):
+        return lib.moe_layer_mxfp4(x, dt, wr, lg, M, k, ctypes.byref(ex), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   dev_error, y, out, wsp, nbytes, None)
+
+    assert call(ex=_experts(d=100)) == EINVAL
+    assert call(ex=_experts(base=0)) == EINVAL
+    assert call(M=-1) == EINVAL
+    assert call(k=0) == EINVAL
+    assert call(k=17) == EINVAL  # k > E
+    assert call(dt=5) == EINVAL
+    assert call(lg=None) == EINVAL
+    assert call(x=None) == EINVAL  # x is needed by the FFN even with given logits
+    assert call(out=None) == EINVAL
+    assert call(out=FAKE + 4) == EINVAL
+    assert call(dev_error=None) == EINVAL
+    assert call(y=None) == EINVAL
+    assert call(nbytes=ws - 1) == EINVAL
+    assert call(wsp=FAKE + 16) == EINVAL
+    assert call(ex=_experts(n_routed=5000, n_shared=0)) == EUNSUP
+    assert call(M=0) == moe.MOE_OK

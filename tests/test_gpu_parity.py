@@ -266,6 +266,65 @@ def test_ffn_stages_equal_full_call(shape, M):
     _stages_equal_full(moe, ex, shape.k, xd, layer, layer.forward(xd))
 
 
+def _layer_outputs(res, M, k, S):
+    na = int(_host(res["n_active"])[0])
+    return dict(logits=_host(res["logits"][:M]), ids=_host(res["topk_ids"][:M]), w=_host(res["topk_w"][:M]),
+                offsets=_host(res["offsets"]), perm=_host(res["perm"][:M * (k + S)]), n_active=np.array([na]),
+                active=_host(res["active"])[:na], dev_error=_host(res["dev_error"]),
+                y=_host(res["y_slots"][:M * (k + S)]), out=_host(res["out"][:M]))
+
+
+def _fused_equals_calls(moe, ex, k, xd, w_router, what):
+    """moe_layer_mxfp4 == moe_route + moe_bucket + moe_expert_ffn_mxfp4 +
+    moe_combine, every output bit for bit (fresh buffers for each side, the
+    fused side's poisoned first)."""
+    M = xd.shape[0]
+    S = ex.n_shared
+    outs = []
+    for fused in (False, True):
+        layer = moe.MoELayer(ex, k, M, w_router=w_router)
+        for t in (layer.y_slots, layer.out, layer.topk_w, layer.logits):
+            t.fill_(float("nan"))
+        for t in (layer.perm, layer.offsets, layer.active, layer.topk_ids):
+            t.fill_(-7)
+        layer.workspace.fill_(0xA5)  # workspace contents on entry do not matter
+        outs.append(_layer_outputs(layer.forward(xd, fused=fused), M, k, S))
+    a, b = outs
+    for key in a:
+        assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), (what, M, key)
+
+
+@pytest.mark.parametrize("shape", [synth.TINY] + RAGGED + WIDE, ids=lambda s: s.name)
+def test_layer_call_equals_four_calls(shape):
+    moe = _moe()
+    ex, _ = _small_layer(shape, 31)
+    wr = _dev(synth.router_weight(shape, 31))
+    for M in (1, 2, 3, 5, 16, 17, 40):
+        xd = _x_dev(shape, synth.rows_x(shape, 32 + M, M))
+        _fused_equals_calls(moe, ex, shape.k, xd, wr, shape.name)
+
+
+def test_layer_call_back_to_back_and_given_logits():
+    """Calls in a row on one set of buffers with M going up and down, and
+    with logits given instead of a router."""
+    moe = _moe()
+    shape = RAGGED[2]
+    ex, recs = _small_layer(shape, 41)
+    wr = synth.router_weight(shape, 41)
+    layer = moe.MoELayer(ex, shape.k, 16, w_router=_dev(wr))
+    for M in (16, 9, 1, 16, 4):
+        x = synth.rows_x(shape, 42 + M, M)
+        res = layer.forward(_x_dev(shape, x))
+        ref = oracle.layer(x, shape.k, shape.n_routed, shape.n_shared, shape.d, shape.f, recs.__getitem__, w_r=wr)
+        _compare_layer(res, ref, f"back-to-back M={M}", shape.k, shape.n_shared)
+    lg = synth.random_logits(43, 7, shape.n_routed)
+    x = synth.rows_x(shape, 44, 7)
+    given = moe.MoELayer(ex, shape.k, 7)
+    res = given.forward(_x_dev(shape, x), logits=_dev(lg))
+    ref = oracle.layer(x, shape.k, shape.n_routed, shape.n_shared, shape.d, shape.f, recs.__getitem__, logits=lg)
+    _compare_layer(res, ref, "given logits", shape.k, shape.n_shared)
+
+
 # ----------------------------------------------------------------------------- Kimi decode
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_kimi_one_row_parity(kimi_layer, seed):
@@ -336,6 +395,15 @@ def test_kimi_expert_order_independence(kimi_layer):
         moe.moe_expert_ffn_mxfp4(x, shp.k, L["experts"], res["offsets"], res["perm"], act, res["n_active"],
                                  res["y_slots"], layer.workspace)
         assert np.array_equal(_host(res["y_slots"]).view(np.uint8), y_ref.view(np.uint8)), order
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_kimi_layer_call_equals_four_calls(kimi_layer, M):
+    moe = _moe()
+    L = kimi_layer
+    shp = L["shape"]
+    xd = _x_dev(shp, synth.block_x(shp, 7, M))
+    _fused_equals_calls(moe, L["experts"], shp.k, xd, L["wr_dev"], "kimi")
 
 
 @pytest.mark.parametrize("M", [1, 16])
