@@ -175,6 +175,80 @@ int moe_layer_mxfp4(const void *x, moe_dtype x_dtype, const float *w_router, flo
                     int32_t *active, int32_t *n_active, int32_t *dev_error, float *y_slots, float *out,
                     void *workspace, size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Expert streaming ("One GPU, three storage tiers": a device expert cache in
+ * front of a pinned host pool; "Read the experts the router needs": a
+ * device-cache hit computes at once, a host-pool hit is uploaded first on one
+ * of several upload streams, and experts are computed as they arrive).
+ * The disk tier of the pages is not modelled: the host pool holds every
+ * expert of n_layers layers.
+ *
+ * Device pool slots (records of `stride` bytes):
+ *   [0, n_layers*n_shared)            the shared experts, uploaded at creation
+ *   next n_transient slots             experts used for one call only
+ *   the rest (at least one)            cached experts, by (layer, expert)
+ * Cache policy (also run on the host alone by moe_cache_simulate): the
+ * experts of a call are taken in ascending id; those cached are hits.  With
+ * admit_min_rows > 0 ("A drafter that leaves the answer unchanged": keep only
+ * the experts that enough of a block's rows use), a miss used by fewer rows
+ * takes a transient slot while one is left.  Other misses are admitted into
+ * the lowest free cached slot, else the least recently used cached slot
+ * (lowest on equal age) not holding an expert of this call; with none left
+ * they take transient slots. */
+typedef struct moe_expert_cache moe_expert_cache; /* opaque, owned by the library */
+
+typedef struct {
+  void *device_pool;       /* device, n_slots * stride bytes, 16-byte aligned, caller-owned */
+  int32_t n_slots;
+  const void *host_pool;   /* PINNED host memory (hipHostMalloc, torch pin_memory), caller-owned:
+                              n_layers * (n_routed + n_shared) records of `stride` bytes, layer
+                              after layer, each layer laid out as moe_experts records */
+  int32_t n_layers, n_routed, n_shared;
+  int32_t d, f;            /* multiples of 32 */
+  int64_t stride;          /* >= 3*d*f*17/32, multiple of 16 */
+  int32_t n_upload_streams; /* 1..8 */
+  int32_t upload_groups;   /* 1..16: misses are uploaded and computed in this many groups */
+  int32_t admit_min_rows;  /* 0 = plain LRU */
+  int32_t n_transient;     /* >= 0 */
+} moe_cache_config;
+
+typedef struct {
+  int64_t calls, hits, misses, admitted, bytes_uploaded; /* routed experts only; since creation */
+} moe_cache_stats;
+
+/* Creates the cache: upload streams, events, small pinned and device plan
+ * buffers (owned by the cache) and a synchronous upload of every shared
+ * expert.  The pools stay owned by the caller and must outlive the cache.
+ * MOE_EINVAL for a bad configuration or a host pool that is not pinned. */
+int moe_cache_create(const moe_cache_config *cfg, moe_expert_cache **out);
+/* Waits for the device to be idle, then frees what moe_cache_create made. */
+int moe_cache_destroy(moe_expert_cache *cache);
+int moe_cache_get_stats(const moe_expert_cache *cache, moe_cache_stats *stats);
+
+/* moe_layer_mxfp4 for layer `layer` of the host pool, its experts streamed
+ * into the device cache as needed.  Arguments and outputs are those of
+ * moe_layer_mxfp4 (d, f, E, S from the configuration), and every output is
+ * bit-identical to moe_layer_mxfp4 on the same layer held in device memory.
+ * Unlike the other calls it SYNCHRONISES `stream` once, after the bucketing
+ * (the experts to fetch are known only then), so it cannot be captured in a
+ * graph.  Calls on one cache must come from one host thread on one stream.
+ * MOE_EUNSUPPORTED if min(E, M*k) exceeds the transient plus cached slots.
+ * Device pool offsets of a slot's record are 64-bit; a record itself is
+ * addressed with 32-bit offsets (stride < 2^30). */
+int moe_layer_streamed(moe_expert_cache *cache, int32_t layer, const void *x, moe_dtype x_dtype,
+                       const float *w_router, float *logits, int32_t M, int32_t k, int32_t *topk_ids, float *topk_w,
+                       int32_t *offsets, int32_t *perm, int32_t *active, int32_t *n_active, int32_t *dev_error,
+                       float *y_slots, float *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/* The cache policy alone, on the host (no device call): n_calls calls, call
+ * i of layer call_layer[i] with call_n[i] routed experts (ascending, distinct)
+ * at experts[...] used by rows[...] rows each, concatenated over the calls.
+ * Writes per entry its slot (0 .. n_transient-1 transient, then cached),
+ * hit (0/1) and admitted (0/1).  MOE_EUNSUPPORTED if a call does not fit. */
+int moe_cache_simulate(int32_t n_layers, int32_t n_routed, int32_t n_cache, int32_t n_transient,
+                       int32_t admit_min_rows, int32_t n_calls, const int32_t *call_layer, const int32_t *call_n,
+                       const int32_t *experts, const int32_t *rows, int32_t *slot, int32_t *hit, int32_t *admitted);
+
 /* Q8_0 spine matmul ("A drafter that leaves the answer unchanged": the
  * spine's matrix multiplies load each weight once for up to eight rows;
  * "One GPU, three storage tiers": the spine's matrices are Q8_0):

@@ -22,7 +22,8 @@ MOE_F32, MOE_BF16 = 0, 1
 
 # names exported by include/moe.h
 ABI_FUNCTIONS = ("moe_route", "moe_bucket", "moe_expert_ffn_mxfp4", "moe_ffn_gateup_mxfp4", "moe_ffn_down_mxfp4",
-                 "moe_workspace_bytes", "moe_combine", "moe_layer_mxfp4", "q8_0_matmul", "moe_status_str")
+                 "moe_workspace_bytes", "moe_combine", "moe_layer_mxfp4", "moe_cache_create", "moe_cache_destroy",
+                 "moe_cache_get_stats", "moe_layer_streamed", "moe_cache_simulate", "q8_0_matmul", "moe_status_str")
 
 
 class MoeError(RuntimeError):
@@ -34,6 +35,19 @@ class MoeError(RuntimeError):
 class _Experts(ctypes.Structure):
     _fields_ = [("base", ctypes.c_void_p), ("stride", ctypes.c_int64), ("d", ctypes.c_int32),
                 ("f", ctypes.c_int32), ("n_routed", ctypes.c_int32), ("n_shared", ctypes.c_int32)]
+
+
+class _CacheConfig(ctypes.Structure):
+    _fields_ = [("device_pool", ctypes.c_void_p), ("n_slots", ctypes.c_int32), ("host_pool", ctypes.c_void_p),
+                ("n_layers", ctypes.c_int32), ("n_routed", ctypes.c_int32), ("n_shared", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("f", ctypes.c_int32), ("stride", ctypes.c_int64),
+                ("n_upload_streams", ctypes.c_int32), ("upload_groups", ctypes.c_int32),
+                ("admit_min_rows", ctypes.c_int32), ("n_transient", ctypes.c_int32)]
+
+
+class _CacheStats(ctypes.Structure):
+    _fields_ = [("calls", ctypes.c_int64), ("hits", ctypes.c_int64), ("misses", ctypes.c_int64),
+                ("admitted", ctypes.c_int64), ("bytes_uploaded", ctypes.c_int64)]
 
 
 def _load() -> ctypes.CDLL:
@@ -53,6 +67,12 @@ def _load() -> ctypes.CDLL:
         "moe_workspace_bytes": (sz, [i32, i32, EP]),
         "moe_combine": (ctypes.c_int, [P, P, i32, i32, i32, i32, P, P]),
         "moe_layer_mxfp4": (ctypes.c_int, [P, ctypes.c_int, P, P, i32, i32, EP, P, P, P, P, P, P, P, P, P, P, sz, P]),
+        "moe_cache_create": (ctypes.c_int, [ctypes.POINTER(_CacheConfig), ctypes.POINTER(P)]),
+        "moe_cache_destroy": (ctypes.c_int, [P]),
+        "moe_cache_get_stats": (ctypes.c_int, [P, ctypes.POINTER(_CacheStats)]),
+        "moe_layer_streamed": (ctypes.c_int, [P, i32, P, ctypes.c_int, P, P, i32, i32, P, P, P, P, P, P, P, P, P, P,
+                                              sz, P]),
+        "moe_cache_simulate": (ctypes.c_int, [i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P]),
         "q8_0_matmul": (ctypes.c_int, [P, i32, i32, P, P, i32, P, P]),
         "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     }
@@ -115,11 +135,12 @@ class Experts:
     f: int
     n_routed: int
     n_shared: int
+    whole_layer: bool = True  # False: a descriptor of shapes only (an expert cache's pool)
 
     def c_struct(self) -> _Experts:
         if self.base.dtype != torch.uint8:
             raise ValueError("expert base must be a uint8 tensor")
-        if self.base.numel() < (self.n_routed + self.n_shared) * self.stride:
+        if self.whole_layer and self.base.numel() < (self.n_routed + self.n_shared) * self.stride:
             raise ValueError("expert base tensor is too small")
         return _Experts(_ptr(self.base), self.stride, self.d, self.f, self.n_routed, self.n_shared)
 
@@ -258,6 +279,95 @@ def q8_0_matmul(X, Wq, Ws, Y, stream=None):
     _check("q8_0_matmul", rc)
 
 
+# ----------------------------------------------------------------------------- expert streaming
+class ExpertCache:
+    """A device expert cache in front of a pinned host pool (moe_cache_create).
+
+    ``device_pool``: uint8 GPU tensor of n_slots * stride bytes.  ``host_pool``:
+    uint8 PINNED CPU tensor (``pin_memory=True``) of n_layers * (n_routed +
+    n_shared) expert records.  Both stay owned by the caller; this object keeps
+    references so they outlive the cache."""
+
+    def __init__(self, device_pool: torch.Tensor, host_pool: torch.Tensor, n_layers: int, n_routed: int,
+                 n_shared: int, d: int, f: int, stride: int, n_upload_streams: int = 8, upload_groups: int = 4,
+                 admit_min_rows: int = 0, n_transient: int = 0):
+        if device_pool.dtype != torch.uint8 or not device_pool.is_cuda:
+            raise ValueError("device_pool must be a uint8 GPU tensor")
+        if host_pool.dtype != torch.uint8 or host_pool.is_cuda or not host_pool.is_pinned():
+            raise ValueError("host_pool must be a pinned uint8 CPU tensor")
+        if host_pool.numel() < n_layers * (n_routed + n_shared) * stride:
+            raise ValueError("host_pool is too small")
+        self.device_pool, self.host_pool = device_pool, host_pool
+        self.n_slots = device_pool.numel() // stride
+        self.n_layers, self.n_routed, self.n_shared, self.d, self.f, self.stride = (n_layers, n_routed, n_shared, d,
+                                                                                    f, stride)
+        cfg = _CacheConfig(device_pool.data_ptr(), self.n_slots, host_pool.data_ptr(), n_layers, n_routed, n_shared,
+                           d, f, stride, n_upload_streams, upload_groups, admit_min_rows, n_transient)
+        h = ctypes.c_void_p()
+        _check("moe_cache_create", _lib.moe_cache_create(ctypes.byref(cfg), ctypes.byref(h)))
+        self._h = h
+
+    def descriptor(self) -> "Experts":
+        """An Experts descriptor with this cache's shapes (for buffer sizing;
+        the streamed call never addresses records through it)."""
+        return Experts(self.device_pool, self.stride, self.d, self.f, self.n_routed, self.n_shared,
+                       whole_layer=False)
+
+    def stats(self) -> dict:
+        st = _CacheStats()
+        _check("moe_cache_get_stats", _lib.moe_cache_get_stats(self._h, ctypes.byref(st)))
+        return {name: int(getattr(st, name)) for name, _ in _CacheStats._fields_}
+
+    def close(self):
+        if self._h:
+            _check("moe_cache_destroy", _lib.moe_cache_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def moe_layer_streamed(cache: ExpertCache, layer: int, x, w_router, logits, k, topk_ids, topk_w, offsets, perm,
+                       active, n_active, dev_error, y_slots, out, workspace, stream=None):
+    """moe_layer_mxfp4 on layer ``layer`` of the cache's host pool, experts
+    streamed into the device cache as needed (synchronises the stream once)."""
+    M, d = x.shape
+    E, S = cache.n_routed, cache.n_shared
+    if d != cache.d or tuple(logits.shape) != (M, E) or tuple(out.shape) != (M, d):
+        raise ValueError("x [M x d], logits [M x E] and out [M x d] must match the cache")
+    if tuple(y_slots.shape) != (M * (k + S), d) or tuple(topk_ids.shape) != (M, k):
+        raise ValueError("y_slots [M*(k+S) x d], topk [M x k]")
+    rc = _lib.moe_layer_streamed(cache._h, layer, _ptr(x), _x_dtype(x), _ptr(w_router), _ptr(logits), M, k,
+                                 _ptr(topk_ids), _ptr(topk_w), _ptr(offsets), _ptr(perm), _ptr(active),
+                                 _ptr(n_active), _ptr(dev_error), _ptr(y_slots), _ptr(out), _ptr(workspace),
+                                 workspace.numel(), _stream(stream))
+    _check("moe_layer_streamed", rc)
+
+
+def moe_cache_simulate(n_layers, n_routed, n_cache, n_transient, admit_min_rows, calls):
+    """Runs the cache policy alone on the host.  ``calls``: list of (layer,
+    experts (ascending), rows).  Returns per call (slot, hit, admitted) lists."""
+    import numpy as np
+    lay = np.array([c[0] for c in calls], dtype=np.int32)
+    cn = np.array([len(c[1]) for c in calls], dtype=np.int32)
+    ex = np.concatenate([np.asarray(c[1], dtype=np.int32) for c in calls]) if calls else np.zeros(0, np.int32)
+    rw = np.concatenate([np.asarray(c[2], dtype=np.int32) for c in calls]) if calls else np.zeros(0, np.int32)
+    tot = max(int(cn.sum()), 1)
+    slot, hit, adm = (np.zeros(tot, np.int32) for _ in range(3))
+    a = lambda v: v.ctypes.data_as(ctypes.c_void_p)
+    rc = _lib.moe_cache_simulate(n_layers, n_routed, n_cache, n_transient, admit_min_rows, len(calls), a(lay), a(cn),
+                                 a(ex), a(rw), a(slot), a(hit), a(adm))
+    _check("moe_cache_simulate", rc)
+    out, at = [], 0
+    for n in cn:
+        out.append((slot[at:at + n].tolist(), hit[at:at + n].tolist(), adm[at:at + n].tolist()))
+        at += n
+    return out
+
+
 # ----------------------------------------------------------------------------- one layer
 class MoELayer:
     """Buffers for one MoE layer pass over up to ``max_rows`` rows, and the pass
@@ -290,6 +400,21 @@ class MoELayer:
                     offsets=self.offsets, perm=self.perm[:M * (self.k + S)], active=self.active,
                     n_active=self.n_active, dev_error=self.dev_error, y_slots=self.y_slots[:M * (self.k + S)],
                     out=self.out[:M])
+
+    def forward_streamed(self, cache: ExpertCache, layer: int, x: torch.Tensor, logits: torch.Tensor | None = None,
+                         stream=None):
+        """One layer pass over x [M x d] with layer ``layer`` of the cache's
+        host pool (this object must be built on cache.descriptor())."""
+        M = x.shape[0]
+        if M > self.max_rows:
+            raise ValueError("more rows than the layer buffers hold")
+        v = self.views(M)
+        if logits is not None:
+            v["logits"] = logits
+        moe_layer_streamed(cache, layer, x, None if logits is not None else self.w_router, v["logits"], self.k,
+                           v["topk_ids"], v["topk_w"], v["offsets"], v["perm"], v["active"], v["n_active"],
+                           v["dev_error"], v["y_slots"], v["out"], self.workspace, stream)
+        return v
 
     def forward(self, x: torch.Tensor, logits: torch.Tensor | None = None, stream=None, fused: bool = True):
         """One layer pass over x [M x d].  With ``logits`` given the router

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include "../../include/moe.h"
+#include "checks.h"
 #include "launch.h"
 
 namespace {
@@ -51,7 +52,8 @@ int run_ffn(const void *x, moe_dtype x_dtype, int32_t M, int32_t k, const moe_ex
             const int32_t *perm, const int32_t *active, const int32_t *n_active, float *y_slots, void *workspace,
             int stages, void *stream) {
   return moe::ffn_launch(x, x_dtype == MOE_BF16, M, k, W->base, W->stride, W->d, W->f, W->n_routed, W->n_shared,
-                         offsets, perm, active, n_active, y_slots, workspace, stages, as_stream(stream)) == 0
+                         offsets, perm, active, n_active, y_slots, workspace, stages, nullptr, 0, 0,
+                         as_stream(stream)) == 0
              ? MOE_OK
              : MOE_EHIP;
 }
@@ -72,6 +74,20 @@ int route_check(const void *x, moe_dtype x_dtype, const float *w_router, const f
 }
 
 }  // namespace
+
+// The argument checks of moe_layer_mxfp4 (also those of moe_layer_streamed).
+int moe_layer_check(const void *x, moe_dtype x_dtype, const float *w_router, const float *logits, int32_t M,
+                    int32_t k, const moe_experts *W, const int32_t *topk_ids, const float *topk_w,
+                    const int32_t *offsets, const int32_t *perm, const int32_t *active, const int32_t *n_active,
+                    const int32_t *dev_error, const float *y_slots, const float *out, const void *workspace,
+                    size_t workspace_bytes) {
+  if (!experts_ok(W)) return MOE_EINVAL;
+  const int rc = route_check(x, x_dtype, w_router, logits, M, W->d, W->n_routed, k, topk_ids, topk_w);
+  if (rc != MOE_OK) return rc;
+  if (!dev_error || !out || reinterpret_cast<uintptr_t>(out) % 16) return MOE_EINVAL;
+  return ffn_check(x, x_dtype, true, M, k, W, offsets, perm, active, n_active, y_slots, true, workspace,
+                   workspace_bytes);
+}
 
 extern "C" {
 
@@ -153,14 +169,10 @@ int moe_layer_mxfp4(const void *x, moe_dtype x_dtype, const float *w_router, flo
                     const moe_experts *W, int32_t *topk_ids, float *topk_w, int32_t *offsets, int32_t *perm,
                     int32_t *active, int32_t *n_active, int32_t *dev_error, float *y_slots, float *out,
                     void *workspace, size_t workspace_bytes, void *stream) {
-  if (!experts_ok(W)) return MOE_EINVAL;
-  const int E = W->n_routed, S = W->n_shared, d = W->d;
-  int rc = route_check(x, x_dtype, w_router, logits, M, d, E, k, topk_ids, topk_w);
-  if (rc != MOE_OK) return rc;
-  if (!dev_error || !out || reinterpret_cast<uintptr_t>(out) % 16) return MOE_EINVAL;
-  rc = ffn_check(x, x_dtype, true, M, k, W, offsets, perm, active, n_active, y_slots, true, workspace,
-                 workspace_bytes);
+  const int rc = moe_layer_check(x, x_dtype, w_router, logits, M, k, W, topk_ids, topk_w, offsets, perm, active,
+                                 n_active, dev_error, y_slots, out, workspace, workspace_bytes);
   if (rc != MOE_OK || M == 0) return rc;
+  const int E = W->n_routed, S = W->n_shared, d = W->d;
   const hipStream_t st = as_stream(stream);
   const int bf = x_dtype == MOE_BF16;
   if (moe::route_launch(x, bf, w_router, logits, M, d, E, k, topk_ids, topk_w, st)) return MOE_EHIP;

@@ -40,7 +40,20 @@ struct GroupSrc {
   const int32_t *n_active; // direct mode
   const int4 *groups;      // plan mode: {expert, start, count, 0}
   const int32_t *n_groups; // plan mode
+  const int32_t *slot_map; // null: expert e is record e; else record slot_map[e]
+  int n_records;           // records at the weights base (with slot_map)
 };
+
+// Buffer resource over an expert's record.  With a slot map the record index
+// is looked up, and an index outside [0, n_records) gives an empty resource:
+// every load through it reads zero, none leaves the records.
+__device__ __forceinline__ rsrc_t expert_rsrc(const GroupSrc &src, const uint8_t *experts, int64_t stride,
+                                              int expert) {
+  if (!src.slot_map) return make_rsrc(experts + (int64_t)expert * stride, (uint32_t)stride);
+  const int slot = src.slot_map[expert];
+  const bool ok = slot >= 0 && slot < src.n_records;
+  return make_rsrc(experts + (ok ? (int64_t)slot * stride : 0), ok ? (uint32_t)stride : 0u);
+}
 
 __device__ __forceinline__ int group_count(const GroupSrc &src) { return src.groups ? *src.n_groups : *src.n_active; }
 
@@ -362,7 +375,7 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
   const int rw = wv - mat * HW;                    // row-tile group of this wave
   const int i0 = ft * ROWS;
   const uint32_t plane_c = (uint32_t)((int64_t)f * d / 2), plane_s = (uint32_t)((int64_t)f * d / 32);
-  const rsrc_t wr = make_rsrc(experts + (int64_t)expert * stride, (uint32_t)stride);
+  const rsrc_t wr = expert_rsrc(src, experts, stride, expert);
   const int M = n_slots / kps;
   const rsrc_t xr = make_rsrc(x, (uint32_t)((int64_t)M * d * EL));
   const uint32_t brow = bres_row_bytes(d);
@@ -634,7 +647,7 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_wide_kernel(
   const int i0 = ft * ROWS;
   const int nb = d >> 5;
   const uint32_t plane_c = (uint32_t)((int64_t)f * d / 2), plane_s = (uint32_t)((int64_t)f * d / 32);
-  const rsrc_t wr = make_rsrc(experts + (int64_t)expert * stride, (uint32_t)stride);
+  const rsrc_t wr = expert_rsrc(src, experts, stride, expert);
   const int M = n_slots / kps;
   const rsrc_t xr = make_rsrc(x, (uint32_t)((int64_t)M * d * EL));
   const uint32_t dummy = PF * SLOT;
@@ -830,7 +843,7 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
   const int nc = 3 * count, ncb = (nc + 15) >> 4;
   const uint32_t plane = (uint32_t)((int64_t)f * d / 2 + (int64_t)f * d / 32);
   const uint32_t dn_c = 2 * plane, dn_s = dn_c + (uint32_t)((int64_t)d * f / 2);
-  const rsrc_t wr = make_rsrc(experts + (int64_t)expert * stride, (uint32_t)stride);
+  const rsrc_t wr = expert_rsrc(src, experts, stride, expert);
   const rsrc_t hr = make_rsrc(h_ws, (uint32_t)((int64_t)n_slots * 3 * f * 2));
   const uint32_t hbase = (uint32_t)start * (uint32_t)(3 * f * 2);  // the group's first h row
   const int r0 = dt * ROWS;
@@ -1097,7 +1110,8 @@ static int launch_down(int d, int f, int T, const uint8_t *experts, int64_t stri
 
 int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *experts, int64_t stride, int d, int f,
                int n_routed, int n_shared, const int32_t *offsets, const int32_t *perm, const int32_t *active,
-               const int32_t *n_active, float *y, void *workspace, int stages, hipStream_t stream) {
+               const int32_t *n_active, float *y, void *workspace, int stages, const int32_t *slot_map,
+               int n_records, int64_t max_active, hipStream_t stream) {
   const int S = n_shared;
   const int kps = k + S;
   const int64_t T = M * kps;
@@ -1110,6 +1124,8 @@ int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *exper
   // applies (dword-aligned scale rows)
   const bool wide = many && d % 128 == 0;
   int64_t cap[kGroupClasses] = {ffn_max_groups(M, k, S, n_experts), 0, 0};
+  // with few rows a group is an active expert: a known bound on them sizes the grids
+  if (max_active > 0 && M <= kGroupCols) cap[0] = std::min<int64_t>(cap[0], max_active);
   int4 *glist[kGroupClasses] = {nullptr, nullptr, nullptr};
   if (many) {
     group_caps(M, k, S, n_experts, cap);
@@ -1122,7 +1138,8 @@ int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *exper
   int32_t *n_groups = (int32_t *)(ws + off);
 
   GroupSrc src[kGroupClasses];
-  for (int c = 0; c < kGroupClasses; ++c) src[c] = GroupSrc{offsets, active, n_active, nullptr, nullptr};
+  for (int c = 0; c < kGroupClasses; ++c)
+    src[c] = GroupSrc{offsets, active, n_active, nullptr, nullptr, slot_map, n_records};
   if (many) {
     // the group plan lives in the workspace and serves both stages
     if (stages & kStageGateUp) {

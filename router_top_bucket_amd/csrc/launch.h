@@ -19,9 +19,13 @@ bool ffn_shape_ok(int64_t M, int k, int S, int d, int f, int64_t stride);
 // stages: kStageGateUp (group plan + gate/up + SwiGLU into the workspace),
 // kStageDown (down projection from the workspace into y), or both.
 constexpr int kStageGateUp = 1, kStageDown = 2;
+// slot_map (device, [n_routed + n_shared], or null): expert e's record is
+// slot_map[e] of the n_records at `experts` (null: record e).  max_active > 0:
+// *n_active never exceeds it (sizes the grids with few rows).
 int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *experts, int64_t stride, int d, int f,
                int n_routed, int n_shared, const int32_t *offsets, const int32_t *perm, const int32_t *active,
-               const int32_t *n_active, float *y, void *workspace, int stages, hipStream_t stream);
+               const int32_t *n_active, float *y, void *workspace, int stages, const int32_t *slot_map,
+               int n_records, int64_t max_active, hipStream_t stream);
 
 int combine_launch(const float *y, const float *w, int M, int k, int S, int d, float *out, hipStream_t stream);
 
