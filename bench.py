@@ -5,8 +5,9 @@ FFN, combine) over one batch of rows, through the C ABI, with every input
 already resident in HBM.  The headline workload is the Kimi-K3.1-shaped
 decode layer at 1 row: d=7168, f=1536, 896 routed experts (top-16) plus 2
 shared, MXFP4 experts (17,547,264 bytes each), bf16 x, fp32 router.  The
-16-row verification block, the 1,533-row prefill and the Q8_0 spine matmul
-are reported in "results".
+16-row verification block, the 1,533-row prefill, the Q8_0 spine matmul and
+the experts streamed from a pinned host pool through a device cache are
+reported in "results".
 
 Timing: four distinct layers are resident (63 GB) and consecutive steps run
 consecutive layers, as a model's decode pass does, with input batches
@@ -54,8 +55,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-rows", type=int, default=10)
     p.add_argument("--only", default="",
-                   help="comma list of workloads: decode1,block16,prefill,q8_0 (copy = the copy kernel that "
-                        "calibrates the HBM counters, run alone)")
+                   help="comma list of workloads: decode1,block16,prefill,q8_0,stream (copy = the copy kernel "
+                        "that calibrates the HBM counters, run alone)")
     return p.parse_args()
 
 
@@ -103,6 +104,83 @@ class Timer:
         return a.elapsed_time(b) / n  # ms per launch
 
 
+def run_stream(torch, moe, synth, shp, layers, stream, dev):
+    """Experts streamed from a pinned host pool of 2 layers through a device
+    cache holding 272 routed experts (15% of the pool's): 1-row decode steps
+    and 16-row blocks (LRU, then admission of experts used by >= 2 rows).
+    Each call synchronises its stream once (the host learns the routing), so
+    the wall clock between two synchronisations times a run of calls."""
+    L, E, S = 2, shp.n_routed, shp.n_shared
+    rec = shp.n_experts * shp.stride
+    t0 = time.time()
+    host = torch.empty(L * rec, dtype=torch.uint8, pin_memory=True)
+    for l in range(L):
+        host[l * rec:(l + 1) * rec].copy_(layers[l][0].base)
+    n_transient, n_cache = 32, 240
+    n_slots = L * S + n_transient + n_cache
+    pool = torch.empty(n_slots * shp.stride, dtype=torch.uint8, device=dev)
+    log(f"[bench] stream: {L} layers in pinned host memory ({L * rec / 1e9:.1f} GB) in {time.time() - t0:.1f}s, "
+        f"device cache {n_slots} slots ({n_slots * shp.stride / 1e9:.1f} GB)")
+    # host -> device ceiling: 64 records (1.1 GB) as one copy, and as 8
+    # contiguous pieces on 8 streams; the faster of the two
+    ups = [torch.cuda.Stream(device=dev) for _ in range(8)]
+    nb = 64 * shp.stride
+    pcie = 0.0
+    for pieces in (1, 8, 1, 8):
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for j in range(pieces):
+            a, b = nb * j // pieces, nb * (j + 1) // pieces
+            with torch.cuda.stream(ups[j]):
+                pool[a:b].copy_(host[a:b], non_blocking=True)
+        torch.cuda.synchronize()
+        pcie = max(pcie, nb / (time.perf_counter() - t1) / 1e9)
+    log(f"[bench] stream: host->device copies {pcie:.1f} GB/s")
+    out = {"stream_pcie_h2d_GBps": pcie}
+
+    def run(name, M, xfn, admit, warm, n):
+        cache = moe.ExpertCache(pool, host, L, E, S, shp.d, shp.f, shp.stride, n_upload_streams=8, upload_groups=4,
+                                admit_min_rows=admit, n_transient=n_transient)
+        ml = moe.MoELayer(cache.descriptor(), shp.k, M)
+        xs = [xfn(i) for i in range(warm + n)]
+
+        def call(i):
+            ml.w_router = layers[i % L][1]
+            ml.forward_streamed(cache, i % L, xs[i], stream=stream)
+
+        for i in range(warm):
+            call(i)
+        stream.synchronize()
+        s0 = cache.stats()
+        t1 = time.perf_counter()
+        for i in range(warm, warm + n):
+            call(i)
+        stream.synchronize()
+        dt = (time.perf_counter() - t1) / n
+        s1 = cache.stats()
+        cache.close()
+        hits, misses = s1["hits"] - s0["hits"], s1["misses"] - s0["misses"]
+        up = (s1["bytes_uploaded"] - s0["bytes_uploaded"]) / n
+        r = dict(rows=M, ms_per_layer=dt * 1e3, rows_per_s=M / dt, hit_rate=hits / max(hits + misses, 1),
+                 misses_per_layer=misses / n, upload_GBps=up / dt / 1e9, upload_frac_of_h2d=up / dt / 1e9 / pcie,
+                 admit_min_rows=admit, layers_in_host_pool=L, cached_slots=n_cache, transient_slots=n_transient)
+        log(f"[bench] stream {name}: {dt * 1e3:.2f} ms/layer ({M / dt:.1f} rows/s), hit rate "
+            f"{r['hit_rate']:.2f}, {r['misses_per_layer']:.1f} misses/layer, uploads {r['upload_GBps']:.1f} GB/s")
+        out[f"stream_{name}"] = r
+
+    def x1(i):
+        return torch.from_numpy(synth.rows_x(shp, 5000 + i // L, 1)).view(torch.bfloat16).to(dev)
+
+    def x16(i):
+        return torch.from_numpy(synth.block_x(shp, 6000 + i // L, 16)).view(torch.bfloat16).to(dev)
+
+    run("decode_1row", 1, x1, 0, 20, 60)
+    run("block_16rows_lru", 16, x16, 0, 8, 24)
+    run("block_16rows_admit2", 16, x16, 2, 8, 24)
+    del pool, host
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -119,7 +197,7 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.Stream(device=dev)
     timer = Timer(torch, stream)
-    only = set(args.only.split(",")) if args.only else {"decode1", "block16", "prefill", "q8_0"}
+    only = set(args.only.split(",")) if args.only else {"decode1", "block16", "prefill", "q8_0", "stream"}
     if args.no_extra:
         only = {"decode1"}
 
@@ -292,6 +370,10 @@ def main():
                 log(f"[bench] q8_0 K={K} N={N} M={Mq}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
             del dwq, dws, copies
         results["q8_0"] = q8
+
+    # ------------------------------------------------------------ host-tier expert streaming
+    if "stream" in only:
+        results.update(run_stream(torch, moe, synth, shp, layers, stream, dev))
 
     # ------------------------------------------------------------ CPU baseline: the oracle
     cpu = None
