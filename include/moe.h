@@ -259,6 +259,39 @@ int moe_cache_simulate(int32_t n_layers, int32_t n_routed, int32_t n_cache, int3
 int q8_0_matmul(const float *X, int32_t M, int32_t K, const int8_t *Wq, const uint16_t *Ws, int32_t N, float *Y,
                 void *stream);
 
+/* ------------------------------------------------------------------------
+ * Block verification ("A drafter that leaves the answer unchanged": a block
+ * of up to 16 rows, the current token plus drafts, runs the same arithmetic
+ * as plain steps, and drafts are kept up to the first one the model
+ * disagrees with; the run record compares FNV-1a hashes of every position's
+ * logits between the paths, under greedy decoding).  Helpers of a harness
+ * that stacks layers; every result is exact. */
+
+/* Rows of a Q8_0 matrix as fp32 (an embedding lookup):
+ * X[m, c] = Wq[ids[m], c] * Ws[ids[m], c/32]; an id outside [0, N) gives a zero
+ * row.  X [M x K] 16-byte aligned, Wq [N x K] 4-byte aligned, K % 32 == 0. */
+int q8_0_rows(const int32_t *ids, int32_t M, int32_t K, const int8_t *Wq, const uint16_t *Ws, int32_t N, float *X,
+              void *stream);
+
+/* Residual update: if a != NULL, h[i] += a[i] (fp32); then, if h_bf16 != NULL,
+ * h_bf16[i] = bf16 bits of h[i], rounded to nearest even.  n >= 0 elements. */
+int moe_residual_bf16(float *h, const float *a, int64_t n, uint16_t *h_bf16, void *stream);
+
+/* RMS normalisation per row, no gain: out[m,c] = h[m,c] / sqrt(mean_c h[m,c]^2 + eps)
+ * (computed as h * (1 / sqrt(...)) in fp32, the sum of squares in an order
+ * that depends only on d), written as fp32 to `out` and/or as bf16 bits
+ * (nearest even) to `out_bf16` (either may be NULL, not both).  h [M x d]. */
+int moe_rmsnorm(const float *h, int32_t M, int32_t d, float eps, float *out, uint16_t *out_bf16, void *stream);
+
+/* Greedy choice per row: idx[m] = the index of the largest X[m, :], the lowest
+ * index among equal values, NaN below every number.  X [M x N]. */
+int moe_argmax_rows(const float *X, int32_t M, int32_t N, int32_t *idx, void *stream);
+
+/* hash[m] = 64-bit FNV-1a (offset basis 0xcbf29ce484222325, prime
+ * 0x100000001b3) of the 4*N bytes of row m of X [M x N] fp32, in memory order.
+ * A sequential recurrence: one thread per row, milliseconds for long rows. */
+int moe_fnv1a_rows(const float *X, int32_t M, int32_t N, uint64_t *hash, void *stream);
+
 /* Human-readable name of a status code (static string). */
 const char *moe_status_str(int status);
 

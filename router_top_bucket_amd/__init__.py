@@ -23,7 +23,8 @@ MOE_F32, MOE_BF16 = 0, 1
 # names exported by include/moe.h
 ABI_FUNCTIONS = ("moe_route", "moe_bucket", "moe_expert_ffn_mxfp4", "moe_ffn_gateup_mxfp4", "moe_ffn_down_mxfp4",
                  "moe_workspace_bytes", "moe_combine", "moe_layer_mxfp4", "moe_cache_create", "moe_cache_destroy",
-                 "moe_cache_get_stats", "moe_layer_streamed", "moe_cache_simulate", "q8_0_matmul", "moe_status_str")
+                 "moe_cache_get_stats", "moe_layer_streamed", "moe_cache_simulate", "q8_0_matmul", "q8_0_rows",
+                 "moe_residual_bf16", "moe_rmsnorm", "moe_argmax_rows", "moe_fnv1a_rows", "moe_status_str")
 
 
 class MoeError(RuntimeError):
@@ -74,6 +75,11 @@ def _load() -> ctypes.CDLL:
                                               sz, P]),
         "moe_cache_simulate": (ctypes.c_int, [i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P]),
         "q8_0_matmul": (ctypes.c_int, [P, i32, i32, P, P, i32, P, P]),
+        "q8_0_rows": (ctypes.c_int, [P, i32, i32, P, P, i32, P, P]),
+        "moe_residual_bf16": (ctypes.c_int, [P, P, i64, P, P]),
+        "moe_rmsnorm": (ctypes.c_int, [P, i32, i32, ctypes.c_float, P, P, P]),
+        "moe_argmax_rows": (ctypes.c_int, [P, i32, i32, P, P]),
+        "moe_fnv1a_rows": (ctypes.c_int, [P, i32, i32, P, P]),
         "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sigs.items():
@@ -277,6 +283,53 @@ def q8_0_matmul(X, Wq, Ws, Y, stream=None):
         raise ValueError("q8_0 shapes")
     rc = _lib.q8_0_matmul(_ptr(X), M, K, _ptr(Wq), _ptr(Ws), N, _ptr(Y), _stream(stream))
     _check("q8_0_matmul", rc)
+
+
+# ----------------------------------------------------------------------------- block-verification helpers
+def q8_0_rows(ids, Wq, Ws, X, stream=None):
+    """X[m] = row ids[m] of the Q8_0 matrix (int8 [N x K], fp16 bits [N x K/32]) in fp32."""
+    M, K = X.shape
+    N = Wq.shape[0]
+    if ids.dtype != torch.int32 or ids.numel() != M or X.dtype != torch.float32 or Wq.dtype != torch.int8:
+        raise ValueError("q8_0_rows: ids int32 [M], X float32 [M x K], Wq int8 [N x K]")
+    if tuple(Wq.shape) != (N, K) or tuple(Ws.shape) != (N, K // 32):
+        raise ValueError("q8_0_rows shapes")
+    _check("q8_0_rows", _lib.q8_0_rows(_ptr(ids), M, K, _ptr(Wq), _ptr(Ws), N, _ptr(X), _stream(stream)))
+
+
+def moe_residual_bf16(h, a=None, h_bf16=None, stream=None):
+    """h += a (if given); h_bf16 = bf16(h) rounded to nearest even (if given)."""
+    if h.dtype != torch.float32 or (a is not None and (a.dtype != torch.float32 or a.numel() != h.numel())):
+        raise ValueError("h and a must be float32 of one size")
+    if h_bf16 is not None and (h_bf16.element_size() != 2 or h_bf16.numel() != h.numel()):
+        raise ValueError("h_bf16 must hold 16-bit elements, one per h element")
+    _check("moe_residual_bf16", _lib.moe_residual_bf16(_ptr(h), _ptr(a), h.numel(), _ptr(h_bf16), _stream(stream)))
+
+
+def moe_rmsnorm(h, out=None, out_bf16=None, eps=1e-6, stream=None):
+    """out / out_bf16 = h / sqrt(mean(h^2) + eps) per row (either may be None, not both)."""
+    M, d = h.shape
+    if h.dtype != torch.float32 or (out is not None and (out.dtype != torch.float32 or out.shape != h.shape)):
+        raise ValueError("h and out must be float32 [M x d]")
+    if out_bf16 is not None and (out_bf16.element_size() != 2 or tuple(out_bf16.shape) != (M, d)):
+        raise ValueError("out_bf16 must hold 16-bit elements [M x d]")
+    _check("moe_rmsnorm", _lib.moe_rmsnorm(_ptr(h), M, d, eps, _ptr(out), _ptr(out_bf16), _stream(stream)))
+
+
+def moe_argmax_rows(X, idx, stream=None):
+    """idx[m] = argmax of row m (lowest index on ties, NaN lowest)."""
+    M, N = X.shape
+    if X.dtype != torch.float32 or idx.dtype != torch.int32 or idx.numel() < M:
+        raise ValueError("X float32 [M x N], idx int32 [M]")
+    _check("moe_argmax_rows", _lib.moe_argmax_rows(_ptr(X), M, N, _ptr(idx), _stream(stream)))
+
+
+def moe_fnv1a_rows(X, hashes, stream=None):
+    """hashes[m] = 64-bit FNV-1a of row m's fp32 bytes (an int64 tensor holds the bits)."""
+    M, N = X.shape
+    if X.dtype != torch.float32 or hashes.dtype != torch.int64 or hashes.numel() < M:
+        raise ValueError("X float32 [M x N], hashes int64 [M]")
+    _check("moe_fnv1a_rows", _lib.moe_fnv1a_rows(_ptr(X), M, N, _ptr(hashes), _stream(stream)))
 
 
 # ----------------------------------------------------------------------------- expert streaming

@@ -194,4 +194,40 @@ int q8_0_matmul(const float *X, int32_t M, int32_t K, const int8_t *Wq, const ui
   return status_of(moe::q8_0_launch(X, M, K, Wq, Ws, N, Y, as_stream(stream)));
 }
 
+int q8_0_rows(const int32_t *ids, int32_t M, int32_t K, const int8_t *Wq, const uint16_t *Ws, int32_t N, float *X,
+              void *stream) {
+  if (M < 0 || K <= 0 || K % 32 || N <= 0) return MOE_EINVAL;
+  if (!ids || !Wq || !Ws || !X) return MOE_EINVAL;
+  if (reinterpret_cast<uintptr_t>(X) % 16 || reinterpret_cast<uintptr_t>(Wq) % 4 ||
+      reinterpret_cast<uintptr_t>(Ws) % 2)
+    return MOE_EINVAL;
+  if (M == 0) return MOE_OK;
+  return status_of(moe::q8_0_rows_launch(ids, M, K, Wq, Ws, N, X, as_stream(stream)));
+}
+
+int moe_residual_bf16(float *h, const float *a, int64_t n, uint16_t *h_bf16, void *stream) {
+  if (n < 0 || !h || (!a && !h_bf16)) return MOE_EINVAL;
+  if (n == 0) return MOE_OK;
+  return status_of(moe::residual_bf16_launch(h, a, n, h_bf16, as_stream(stream)));
+}
+
+int moe_rmsnorm(const float *h, int32_t M, int32_t d, float eps, float *out, uint16_t *out_bf16, void *stream) {
+  if (M < 0 || d <= 0 || !h || (!out && !out_bf16) || !(eps >= 0.0f)) return MOE_EINVAL;
+  if (M == 0) return MOE_OK;
+  return status_of(moe::rmsnorm_launch(h, M, d, eps, out, out_bf16, as_stream(stream)));
+}
+
+int moe_argmax_rows(const float *X, int32_t M, int32_t N, int32_t *idx, void *stream) {
+  if (M < 0 || N <= 0 || !X || !idx) return MOE_EINVAL;
+  if (M == 0) return MOE_OK;
+  return status_of(moe::argmax_rows_launch(X, M, N, idx, as_stream(stream)));
+}
+
+int moe_fnv1a_rows(const float *X, int32_t M, int32_t N, uint64_t *hash, void *stream) {
+  if (M < 0 || N <= 0 || !X || !hash) return MOE_EINVAL;
+  if (reinterpret_cast<uintptr_t>(X) % 4 || reinterpret_cast<uintptr_t>(hash) % 8) return MOE_EINVAL;
+  if (M == 0) return MOE_OK;
+  return status_of(moe::fnv1a_rows_launch(X, M, N, hash, as_stream(stream)));
+}
+
 }  // extern "C"

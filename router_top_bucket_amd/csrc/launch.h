@@ -32,4 +32,12 @@ int combine_launch(const float *y, const float *w, int M, int k, int S, int d, f
 int q8_0_launch(const float *X, int M, int K, const int8_t *wq, const uint16_t *ws, int N, float *Y,
                 hipStream_t stream);
 
+// block-verification harness (verify.hip)
+int q8_0_rows_launch(const int32_t *ids, int M, int K, const int8_t *wq, const uint16_t *ws, int N, float *X,
+                     hipStream_t stream);
+int residual_bf16_launch(float *h, const float *a, int64_t n, uint16_t *hb, hipStream_t stream);
+int rmsnorm_launch(const float *h, int M, int d, float eps, float *out, uint16_t *outb, hipStream_t stream);
+int argmax_rows_launch(const float *X, int M, int N, int32_t *idx, hipStream_t stream);
+int fnv1a_rows_launch(const float *X, int M, int N, uint64_t *hash, hipStream_t stream);
+
 }  // namespace moe

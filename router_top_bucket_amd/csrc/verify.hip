@@ -1,0 +1,148 @@
+// Small kernels of the block-verification harness ("A drafter that leaves the
+// answer unchanged": a block of up to 16 rows runs the same arithmetic as
+// plain steps, drafts are kept up to the first one the model disagrees with,
+// and the logits of every position are hashed in both paths; "Run Kimi 3.1
+// locally on one GPU", run record: FNV-1a hashes of every position's logits,
+// greedy decoding).  The lookups, adds, casts, argmax and hashes are exact;
+// the RMS normalisation is fp32 in an order fixed by the row length.
+#include "common.h"
+#include "launch.h"
+
+namespace moe {
+
+// ---- rows of a Q8_0 matrix as fp32: X[m, c] = Wq[ids[m], c] * Ws[ids[m], c/32]
+// (the product of an int8 and an fp16 is exact in fp32).  One thread per 4
+// consecutive c.  Ids outside [0, N) give a zero row.
+__global__ void q8_0_rows_kernel(const int32_t *__restrict__ ids, int M, int K, const int8_t *__restrict__ wq,
+                                 const uint16_t *__restrict__ ws, int N, float *__restrict__ X) {
+  const int K4 = K >> 2;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)M * K4) return;
+  const int m = (int)(idx / K4), c = (int)(idx - (int64_t)m * K4) * 4;
+  const int id = ids[m];
+  f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (id >= 0 && id < N) {
+    const uint32_t q = *(const uint32_t *)(wq + (int64_t)id * K + c);
+    const float s = (float)__builtin_bit_cast(_Float16, ws[(int64_t)id * (K >> 5) + (c >> 5)]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (float)(int8_t)(q >> (8 * i)) * s;
+  }
+  *(f32x4 *)(X + (int64_t)m * K + c) = v;
+}
+
+// ---- h += a (if a), then hb = bf16(h) rounded to nearest even (if hb)
+__global__ void residual_bf16_kernel(float *__restrict__ h, const float *__restrict__ a, int64_t n,
+                                     uint16_t *__restrict__ hb) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float v = h[i];
+  if (a) {
+    v = v + a[i];
+    h[i] = v;
+  }
+  if (hb) hb[i] = (uint16_t)f32_to_bf16_bits(v);
+}
+
+// ---- RMS normalisation per row without a gain vector:
+// r = 1 / sqrt(sum_c h[c]^2 / d + eps), out[c] = h[c] * r, as fp32 and/or as
+// bf16 bits (round to nearest even).  One workgroup per row; each thread sums
+// its strided elements in ascending order, then a fixed DPP tree per wave and
+// the waves in order: the order depends only on d, never on M.
+constexpr int RN_THREADS = 256;
+__global__ __launch_bounds__(RN_THREADS) void rmsnorm_kernel(const float *__restrict__ h, int d, float eps,
+                                                             float *__restrict__ out, uint16_t *__restrict__ outb) {
+  __shared__ float part[RN_THREADS / 64];
+  const int m = blockIdx.x, tid = threadIdx.x;
+  const float *row = h + (int64_t)m * d;
+  float s = 0.f;
+  for (int i = tid; i < d; i += RN_THREADS) s = __builtin_fmaf(row[i], row[i], s);
+  s = wave_sum(s);
+  if ((tid & 63) == 0) part[tid >> 6] = s;
+  __syncthreads();
+  const float tot = ((part[0] + part[1]) + part[2]) + part[3];
+  const float r = 1.0f / __builtin_sqrtf(tot / (float)d + eps);
+  for (int i = tid; i < d; i += RN_THREADS) {
+    const float v = row[i] * r;
+    if (out) out[(int64_t)m * d + i] = v;
+    if (outb) outb[(int64_t)m * d + i] = (uint16_t)f32_to_bf16_bits(v);
+  }
+}
+
+// ---- per row: the index of the largest value (NaN below every number, the
+// lowest index among equal values).  One workgroup per row; each thread scans
+// a strided range, then the (value, index) pairs are reduced over the wave and
+// the workgroup.  The order key makes the answer unique, so the reduction order
+// cannot change it.
+constexpr int AM_THREADS = 256;
+__device__ __forceinline__ uint64_t am_key(float v, int i) {
+  if (v != v) v = -INFINITY;
+  if (v == 0.0f) v = 0.0f;
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint32_t)~(uint32_t)i;
+}
+__global__ __launch_bounds__(AM_THREADS) void argmax_rows_kernel(const float *__restrict__ X, int N,
+                                                                 int32_t *__restrict__ idx) {
+  __shared__ uint64_t part[AM_THREADS / 64];
+  const int m = blockIdx.x, tid = threadIdx.x;
+  const float *row = X + (int64_t)m * N;
+  uint64_t best = 0;
+  for (int i = tid; i < N; i += AM_THREADS) best = max_u64(best, am_key(row[i], i));
+  best = wave_max_u64(best);
+  if ((tid & 63) == 0) part[tid >> 6] = best;
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t b = part[0];
+    for (int w = 1; w < AM_THREADS / 64; ++w) b = max_u64(b, part[w]);
+    idx[m] = (int32_t)~(uint32_t)b;
+  }
+}
+
+// ---- per row: 64-bit FNV-1a over the row's bytes in memory order (fp32,
+// little endian).  FNV-1a is a sequential recurrence, so one thread walks one
+// row: h = (h ^ byte) * 0x100000001b3 from h = 0xcbf29ce484222325.
+__global__ void fnv1a_rows_kernel(const float *__restrict__ X, int M, int N, uint64_t *__restrict__ hash) {
+  const int m = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (m >= M) return;
+  const uint32_t *row = (const uint32_t *)(X + (int64_t)m * N);
+  uint64_t h = 0xcbf29ce484222325ull;
+  for (int i = 0; i < N; ++i) {
+    const uint32_t w = row[i];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      h ^= (w >> (8 * b)) & 0xFFu;
+      h *= 0x100000001b3ull;
+    }
+  }
+  hash[m] = h;
+}
+
+int q8_0_rows_launch(const int32_t *ids, int M, int K, const int8_t *wq, const uint16_t *ws, int N, float *X,
+                     hipStream_t stream) {
+  const int64_t n = (int64_t)M * (K / 4);
+  hipLaunchKernelGGL(q8_0_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, ids, M, K, wq, ws, N,
+                     X);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+int residual_bf16_launch(float *h, const float *a, int64_t n, uint16_t *hb, hipStream_t stream) {
+  hipLaunchKernelGGL(residual_bf16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, h, a, n, hb);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+int rmsnorm_launch(const float *h, int M, int d, float eps, float *out, uint16_t *outb, hipStream_t stream) {
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(M), dim3(RN_THREADS), 0, stream, h, d, eps, out, outb);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+int argmax_rows_launch(const float *X, int M, int N, int32_t *idx, hipStream_t stream) {
+  hipLaunchKernelGGL(argmax_rows_kernel, dim3(M), dim3(AM_THREADS), 0, stream, X, N, idx);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+int fnv1a_rows_launch(const float *X, int M, int N, uint64_t *hash, hipStream_t stream) {
+  hipLaunchKernelGGL(fnv1a_rows_kernel, dim3((M + 63) / 64), dim3(64), 0, stream, X, M, N, hash);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+}  // namespace moe
