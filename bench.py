@@ -5,9 +5,9 @@ FFN, combine) over one batch of rows, through the C ABI, with every input
 already resident in HBM.  The headline workload is the Kimi-K3.1-shaped
 decode layer at 1 row: d=7168, f=1536, 896 routed experts (top-16) plus 2
 shared, MXFP4 experts (17,547,264 bytes each), bf16 x, fp32 router.  The
-16-row verification block, the 1,533-row prefill, the Q8_0 spine matmul and
-the experts streamed from a pinned host pool through a device cache are
-reported in "results".
+16-row verification block, the 1,533-row prefill, the Q8_0 spine matmul, the
+experts streamed from a pinned host pool through a device cache, and block
+verification over a stack of the resident layers are reported in "results".
 
 Timing: four distinct layers are resident (63 GB) and consecutive steps run
 consecutive layers, as a model's decode pass does, with input batches
@@ -55,8 +55,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-rows", type=int, default=10)
     p.add_argument("--only", default="",
-                   help="comma list of workloads: decode1,block16,prefill,q8_0,stream (copy = the copy kernel "
-                        "that calibrates the HBM counters, run alone)")
+                   help="comma list of workloads: decode1,block16,prefill,q8_0,stream,verify (copy = the copy "
+                        "kernel that calibrates the HBM counters, run alone)")
     return p.parse_args()
 
 
@@ -102,6 +102,84 @@ class Timer:
         b.record(self.stream)
         self.stream.synchronize()
         return a.elapsed_time(b) / n  # ms per launch
+
+
+def run_verify(torch, moe, synth, shp, layers, stream, dev, timer):
+    """The resident layers as a stack (Q8_0 spine 7168 x 7168 per layer, Q8_0
+    head 163,840 x 7168 tied to the embedding): 16 plain greedy steps against
+    one 16-row block whose drafts are those steps' tokens (all kept), timed
+    without hashing; then both paths again with every position's logits
+    hashed (FNV-1a) and compared."""
+    import numpy as np
+    from router_top_bucket_amd.blockverify import Q8Matrix, Stack, plain_steps, verify_block
+    V = 163840
+    spines = []
+    for l in range(len(layers)):
+        wq, ws = synth.q8_0_weight(400 + l, shp.d, shp.d)
+        spines.append(Q8Matrix(torch.from_numpy(wq).to(dev), torch.from_numpy(ws.view(np.int16)).to(dev)))
+    hq, hs = synth.q8_0_weight(500, shp.d, V)
+    head = Q8Matrix(torch.from_numpy(hq).to(dev), torch.from_numpy(hs.view(np.int16)).to(dev))
+    del hq, hs
+    stack = Stack(layers, spines, head, shp.k, 16, device=dev)
+    t0 = 1234
+    with torch.cuda.stream(stream):
+        plain, _ = plain_steps(stack, t0, 16, hashes=False)  # the drafts, and a warm-up
+        drafts = plain[:15]
+        verify_block(stack, t0, drafts, hashes=False)
+        reps = 5
+        stream.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(reps):
+            plain_steps(stack, t0, 16, hashes=False)
+        stream.synchronize()
+        plain_ms = (time.perf_counter() - t1) / reps * 1e3
+        t1 = time.perf_counter()
+        for _ in range(reps):
+            emitted, kept, _ = verify_block(stack, t0, drafts, hashes=False)
+        stream.synchronize()
+        block_ms = (time.perf_counter() - t1) / reps * 1e3
+        p_tok, p_hash = plain_steps(stack, t0, 16)
+        b_tok, b_kept, b_hash = verify_block(stack, t0, drafts)
+    differ = sum(int(a != b) for a, b in zip(p_hash, b_hash))
+    # the same two paths replayed from HIP graphs (no host launch overhead):
+    # one plain step fed the previous step's choice, and the 16-row block
+    blk = torch.tensor([t0] + drafts, dtype=torch.int32, device=dev)
+    cap = torch.cuda.Stream(device=dev)
+    cap.wait_stream(stream)
+    g1, gb = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g1, stream=cap):
+        stack.run(stack.next[:1])
+    with torch.cuda.graph(gb, stream=cap):
+        stack.run(blk)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        def plain_graph(i):
+            if i % 16 == 0:
+                stack.next[:1].fill_(t0)
+            g1.replay()
+
+        for i in range(16):
+            plain_graph(i)
+        plain_g_ms = timer.region(plain_graph, 16 * reps) * 16
+        plain_graph(0)
+        for i in range(1, 16):
+            plain_graph(i)
+        chain_ok = int(stack.next[0].item()) == p_tok[15]
+        gb.replay()
+        block_g_ms = timer.region(lambda i: gb.replay(), reps)
+        block_ok = stack.next[:16].cpu().tolist() == p_tok[:16]
+    del g1, gb
+    r = dict(layers=len(layers), vocab=V, plain_16_steps_ms=plain_ms, block_16rows_ms=block_ms,
+             block_speedup=plain_ms / block_ms, plain_16_steps_graph_ms=plain_g_ms, block_16rows_graph_ms=block_g_ms,
+             block_speedup_graph=plain_g_ms / block_g_ms, graph_paths_match=bool(chain_ok and block_ok),
+             drafts_kept=b_kept, tokens_equal=(b_tok == p_tok), positions_hashed=len(b_hash),
+             hashes_differing=differ)
+    log(f"[bench] verify: {len(layers)} layers + head, 16 plain steps {plain_ms:.2f} ms, one 16-row block "
+        f"{block_ms:.2f} ms ({plain_ms / block_ms:.1f}x); from graphs {plain_g_ms:.2f} vs {block_g_ms:.2f} ms "
+        f"({plain_g_ms / block_g_ms:.1f}x, tokens match {chain_ok and block_ok}); {b_kept} drafts kept, tokens "
+        f"equal {b_tok == p_tok}, {differ} of {len(b_hash)} logits hashes differ")
+    del stack, spines, head
+    return {"verify_block_vs_plain": r}
 
 
 def run_stream(torch, moe, synth, shp, layers, stream, dev):
@@ -197,7 +275,8 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.Stream(device=dev)
     timer = Timer(torch, stream)
-    only = set(args.only.split(",")) if args.only else {"decode1", "block16", "prefill", "q8_0", "stream"}
+    only = (set(args.only.split(",")) if args.only else
+            {"decode1", "block16", "prefill", "q8_0", "stream", "verify"})
     if args.no_extra:
         only = {"decode1"}
 
@@ -370,6 +449,10 @@ def main():
                 log(f"[bench] q8_0 K={K} N={N} M={Mq}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
             del dwq, dws, copies
         results["q8_0"] = q8
+
+    # ------------------------------------------------------------ block verification over a layer stack
+    if "verify" in only:
+        results.update(run_verify(torch, moe, synth, shp, layers, stream, dev, timer))
 
     # ------------------------------------------------------------ host-tier expert streaming
     if "stream" in only:

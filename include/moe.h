@@ -280,11 +280,13 @@ int moe_residual_bf16(float *h, const float *a, int64_t n, uint16_t *h_bf16, voi
 /* RMS normalisation per row, no gain: out[m,c] = h[m,c] / sqrt(mean_c h[m,c]^2 + eps)
  * (computed as h * (1 / sqrt(...)) in fp32, the sum of squares in an order
  * that depends only on d), written as fp32 to `out` and/or as bf16 bits
- * (nearest even) to `out_bf16` (either may be NULL, not both).  h [M x d]. */
+ * (nearest even) to `out_bf16` (either may be NULL, not both).  h [M x d];
+ * h and out 16-byte aligned, out_bf16 8-byte aligned. */
 int moe_rmsnorm(const float *h, int32_t M, int32_t d, float eps, float *out, uint16_t *out_bf16, void *stream);
 
 /* Greedy choice per row: idx[m] = the index of the largest X[m, :], the lowest
- * index among equal values, NaN below every number.  X [M x N]. */
+ * index among equal values, NaN below every number.  X [M x N], 16-byte
+ * aligned. */
 int moe_argmax_rows(const float *X, int32_t M, int32_t N, int32_t *idx, void *stream);
 
 /* hash[m] = 64-bit FNV-1a (offset basis 0xcbf29ce484222325, prime

@@ -213,12 +213,17 @@ int moe_residual_bf16(float *h, const float *a, int64_t n, uint16_t *h_bf16, voi
 
 int moe_rmsnorm(const float *h, int32_t M, int32_t d, float eps, float *out, uint16_t *out_bf16, void *stream) {
   if (M < 0 || d <= 0 || !h || (!out && !out_bf16) || !(eps >= 0.0f)) return MOE_EINVAL;
+  // rows are read and written as float4 / 4 x bf16 when d % 4 == 0
+  if (reinterpret_cast<uintptr_t>(h) % 16 || reinterpret_cast<uintptr_t>(out) % 16 ||
+      reinterpret_cast<uintptr_t>(out_bf16) % 8)
+    return MOE_EINVAL;
   if (M == 0) return MOE_OK;
   return status_of(moe::rmsnorm_launch(h, M, d, eps, out, out_bf16, as_stream(stream)));
 }
 
 int moe_argmax_rows(const float *X, int32_t M, int32_t N, int32_t *idx, void *stream) {
   if (M < 0 || N <= 0 || !X || !idx) return MOE_EINVAL;
+  if (reinterpret_cast<uintptr_t>(X) % 16) return MOE_EINVAL;  // float4 loads when N % 4 == 0
   if (M == 0) return MOE_OK;
   return status_of(moe::argmax_rows_launch(X, M, N, idx, as_stream(stream)));
 }

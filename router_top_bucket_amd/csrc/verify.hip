@@ -45,35 +45,70 @@ __global__ void residual_bf16_kernel(float *__restrict__ h, const float *__restr
 
 // ---- RMS normalisation per row without a gain vector:
 // r = 1 / sqrt(sum_c h[c]^2 / d + eps), out[c] = h[c] * r, as fp32 and/or as
-// bf16 bits (round to nearest even).  One workgroup per row; each thread sums
-// its strided elements in ascending order, then a fixed DPP tree per wave and
-// the waves in order: the order depends only on d, never on M.
-constexpr int RN_THREADS = 256;
+// bf16 bits (round to nearest even).  One workgroup per row.  Rows of up to
+// RN_THREADS*4*RN_VEC elements with d % 4 == 0 stay in registers (float4 loads,
+// all issued before the sum); others are read twice.  The sum: each thread
+// adds its elements in ascending order, then a fixed DPP tree per wave and
+// the waves in order; the order depends only on d, never on M.
+constexpr int RN_THREADS = 256, RN_VEC = 8;
 __global__ __launch_bounds__(RN_THREADS) void rmsnorm_kernel(const float *__restrict__ h, int d, float eps,
                                                              float *__restrict__ out, uint16_t *__restrict__ outb) {
   __shared__ float part[RN_THREADS / 64];
   const int m = blockIdx.x, tid = threadIdx.x;
   const float *row = h + (int64_t)m * d;
+  const bool regs = (d & 3) == 0 && d <= RN_THREADS * 4 * RN_VEC;
+  f32x4 v[RN_VEC];
   float s = 0.f;
-  for (int i = tid; i < d; i += RN_THREADS) s = __builtin_fmaf(row[i], row[i], s);
+  if (regs) {
+#pragma unroll
+    for (int j = 0; j < RN_VEC; ++j) {
+      const int c = 4 * (tid + j * RN_THREADS);
+      v[j] = c < d ? *(const f32x4 *)(row + c) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int j = 0; j < RN_VEC; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s = __builtin_fmaf(v[j][i], v[j][i], s);
+  } else {
+    for (int i = tid; i < d; i += RN_THREADS) s = __builtin_fmaf(row[i], row[i], s);
+  }
   s = wave_sum(s);
   if ((tid & 63) == 0) part[tid >> 6] = s;
   __syncthreads();
   const float tot = ((part[0] + part[1]) + part[2]) + part[3];
   const float r = 1.0f / __builtin_sqrtf(tot / (float)d + eps);
-  for (int i = tid; i < d; i += RN_THREADS) {
-    const float v = row[i] * r;
-    if (out) out[(int64_t)m * d + i] = v;
-    if (outb) outb[(int64_t)m * d + i] = (uint16_t)f32_to_bf16_bits(v);
+  if (regs) {
+#pragma unroll
+    for (int j = 0; j < RN_VEC; ++j) {
+      const int c = 4 * (tid + j * RN_THREADS);
+      if (c < d) {
+        f32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = v[j][i] * r;
+        if (out) *(f32x4 *)(out + (int64_t)m * d + c) = o;
+        if (outb) {
+          const uint32_t b0 = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
+          const uint32_t b1 = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
+          *(uint2 *)(outb + (int64_t)m * d + c) = make_uint2(b0, b1);
+        }
+      }
+    }
+  } else {
+    for (int i = tid; i < d; i += RN_THREADS) {
+      const float o = row[i] * r;
+      if (out) out[(int64_t)m * d + i] = o;
+      if (outb) outb[(int64_t)m * d + i] = (uint16_t)f32_to_bf16_bits(o);
+    }
   }
 }
 
 // ---- per row: the index of the largest value (NaN below every number, the
-// lowest index among equal values).  One workgroup per row; each thread scans
-// a strided range, then the (value, index) pairs are reduced over the wave and
-// the workgroup.  The order key makes the answer unique, so the reduction order
-// cannot change it.
-constexpr int AM_THREADS = 256;
+// lowest index among equal values).  One 1024-thread workgroup per row; with
+// N % 4 == 0 each thread takes float4 pieces AM_UNROLL at a time (all loads of
+// a round issued before their compares), else single elements.  The (value,
+// index) keys are then reduced over the wave and the workgroup; the key
+// order is total, so the reduction order cannot change the answer.
+constexpr int AM_THREADS = 1024, AM_UNROLL = 4;
 __device__ __forceinline__ uint64_t am_key(float v, int i) {
   if (v != v) v = -INFINITY;
   if (v == 0.0f) v = 0.0f;
@@ -87,7 +122,26 @@ __global__ __launch_bounds__(AM_THREADS) void argmax_rows_kernel(const float *__
   const int m = blockIdx.x, tid = threadIdx.x;
   const float *row = X + (int64_t)m * N;
   uint64_t best = 0;
-  for (int i = tid; i < N; i += AM_THREADS) best = max_u64(best, am_key(row[i], i));
+  if ((N & 3) == 0) {
+    const int n4 = N >> 2;
+    for (int base = 0; base < n4; base += AM_THREADS * AM_UNROLL) {
+      f32x4 v[AM_UNROLL];
+#pragma unroll
+      for (int u = 0; u < AM_UNROLL; ++u) {
+        const int p = base + u * AM_THREADS + tid;
+        v[u] = *(const f32x4 *)(row + 4 * (p < n4 ? p : n4 - 1));
+      }
+#pragma unroll
+      for (int u = 0; u < AM_UNROLL; ++u) {
+        const int p = base + u * AM_THREADS + tid;
+        if (p < n4)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) best = max_u64(best, am_key(v[u][i], 4 * p + i));
+      }
+    }
+  } else {
+    for (int i = tid; i < N; i += AM_THREADS) best = max_u64(best, am_key(row[i], i));
+  }
   best = wave_max_u64(best);
   if ((tid & 63) == 0) part[tid >> 6] = best;
   __syncthreads();

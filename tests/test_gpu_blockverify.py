@@ -55,12 +55,13 @@ def test_residual_and_bf16_exact():
     assert np.array_equal(hb.cpu().numpy().view(np.uint16), synth.bf16_bits(s))
 
 
-def test_rmsnorm_close_and_row_independent():
+@pytest.mark.parametrize("d", [7168, 416, 418, 9000])
+def test_rmsnorm_close_and_row_independent(d):
     moe = _moe()
-    g = synth.rng(3, 78)
-    h = (g.standard_normal((9, 7168)) * np.arange(1, 10)[:, None]).astype(np.float32)
+    g = synth.rng(3, 78, d)
+    h = (g.standard_normal((9, d)) * np.arange(1, 10)[:, None]).astype(np.float32)
     out = torch.empty_like(_dev(h))
-    outb = torch.empty((9, 7168), dtype=torch.int16, device="cuda")
+    outb = torch.empty((9, d), dtype=torch.int16, device="cuda")
     moe.moe_rmsnorm(_dev(h), out, outb, 1e-6)
     h64 = h.astype(np.float64)
     ref = h64 / np.sqrt((h64 ** 2).mean(axis=1, keepdims=True) + 1e-6)
@@ -68,7 +69,7 @@ def test_rmsnorm_close_and_row_independent():
     assert_close(o, ref.astype(np.float32), "rmsnorm")
     assert np.array_equal(outb.cpu().numpy().view(np.uint16), synth.bf16_bits(o))
     # a row alone gives the same bits
-    one = torch.empty((1, 7168), dtype=torch.float32, device="cuda")
+    one = torch.empty((1, d), dtype=torch.float32, device="cuda")
     moe.moe_rmsnorm(_dev(h[4:5]), one, None, 1e-6)
     assert np.array_equal(one.cpu().numpy().view(np.uint32), o[4:5].view(np.uint32))
 
@@ -88,6 +89,13 @@ def test_argmax_rows_exact_with_ties_and_nan():
     ref = Xr.argmax(axis=1)
     assert idx.cpu().numpy().tolist() == ref.tolist()
     assert ref[1] == 10 and ref[2] == 123 and ref[3] == 0 and ref[4] == 163839
+    # a length that is not a multiple of 4, and one shorter than a round
+    for N in (1003, 37):
+        Y = g.standard_normal((3, N)).astype(np.float32)
+        Y[1, [N - 1, 2]] = 50.0
+        idx = torch.empty(3, dtype=torch.int32, device="cuda")
+        moe.moe_argmax_rows(_dev(Y), idx)
+        assert idx.cpu().numpy().tolist() == Y.argmax(axis=1).tolist()
 
 
 def test_fnv1a_rows_match_reference():
