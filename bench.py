@@ -307,8 +307,9 @@ def main():
     gu_bytes_per_expert = 2 * shp.f * shp.d * 17 // 32  # gate + up, codes and scales
 
     def run_workload(M, xs, logits, steps, warmup, graphs=True):
-        """Eager and graph-replayed layer passes plus the gate/up stage alone
-        and the whole FFN call, step i on layer i % L with batch i % len(xs)."""
+        """Eager (and, with ``graphs``, graph-replayed) layer passes plus the
+        gate/up stage alone and the whole FFN call, step i on layer i % L with
+        batch i % len(xs)."""
         n = len(xs)
         P = int(np.lcm(n, L))
         mls = [moe.MoELayer(ex, shp.k, M, w_router=None if logits is not None else wr) for ex, wr in layers]
@@ -397,29 +398,30 @@ def main():
 
     # ------------------------------------------------------------ 16-row verification blocks
     if "block16" in only:
-        B = 16
-        xs16 = [torch.from_numpy(synth.block_x(shp, s, B)).view(torch.bfloat16).to(dev) for s in range(20)]
-        res = layer_result(B, run_workload(B, xs16, None, max(40, args.steps // 4), 5))
-        results["block_16rows"] = res
-        log(f"[bench] 16 rows: {res['ms_per_layer'] * 1e3:.1f} us/layer ({res['rows_per_s']:.0f} rows/s; eager "
-            f"{res['ms_per_layer_eager'] * 1e3:.1f} us), U+S={res['experts_read']:.1f}, gate/up "
-            f"{res['gateup_us']:.1f} us, ffn {res['ffn_us']:.1f} us")
+        # blocks of 16 (the reported block) and of 2 and 8 rows
+        for B in (16, 2, 8):
+            xsb = [torch.from_numpy(synth.block_x(shp, s, B)).view(torch.bfloat16).to(dev) for s in range(20)]
+            res = layer_result(B, run_workload(B, xsb, None, max(40, args.steps // 4), 5, graphs=(B == 16)))
+            results[f"block_{B}rows"] = res
+            log(f"[bench] {B} rows: {res['ms_per_layer'] * 1e3:.1f} us/layer ({res['rows_per_s']:.0f} rows/s; eager "
+                f"{res['ms_per_layer_eager'] * 1e3:.1f} us), U+S={res['experts_read']:.1f}, gate/up "
+                f"{res['gateup_us']:.1f} us, ffn {res['ffn_us']:.1f} us")
 
-    # ------------------------------------------------------------ prefill 1533 rows
+    # ------------------------------------------------------------ prefill 1533 (and 270) rows
     if "prefill" in only:
-        Mp = 1533
-        xs_p = [torch.from_numpy(synth.rows_x(shp, 2000 + s, Mp)).view(torch.bfloat16).to(dev) for s in range(3)]
-        lg_p = [torch.from_numpy(synth.zipf_logits(shp, 2000 + s, Mp)).to(dev) for s in range(3)]
-        r = run_workload(Mp, xs_p, lg_p, 12, 2, graphs=False)
-        res = layer_result(Mp, r)
-        flops = 2.0 * Mp * (shp.k + shp.n_shared) * 3 * shp.d * shp.f
-        res.update(useful_TFLOPs=flops / (res["ms_per_layer"] / 1e3) / 1e12,
-                   mfma_frac=flops / (res["ms_per_layer"] / 1e3) / 1e12 / MFMA_BF16_PEAK_TFS,
-                   routing="given Zipf(1.1) logits")
-        results["prefill_1533rows"] = res
-        log(f"[bench] prefill 1533: {res['ms_per_layer']:.3f} ms/layer, experts {res['experts_read']:.0f}, "
-            f"{res['useful_TFLOPs']:.1f} TFLOP/s, gate/up {res['gateup_us'] / 1e3:.3f} ms, "
-            f"ffn {res['ffn_us'] / 1e3:.3f} ms")
+        for Mp in (1533, 270):
+            xs_p = [torch.from_numpy(synth.rows_x(shp, 2000 + s, Mp)).view(torch.bfloat16).to(dev) for s in range(3)]
+            lg_p = [torch.from_numpy(synth.zipf_logits(shp, 2000 + s, Mp)).to(dev) for s in range(3)]
+            r = run_workload(Mp, xs_p, lg_p, 12, 2, graphs=False)
+            res = layer_result(Mp, r)
+            flops = 2.0 * Mp * (shp.k + shp.n_shared) * 3 * shp.d * shp.f
+            res.update(useful_TFLOPs=flops / (res["ms_per_layer"] / 1e3) / 1e12,
+                       mfma_frac=flops / (res["ms_per_layer"] / 1e3) / 1e12 / MFMA_BF16_PEAK_TFS,
+                       routing="given Zipf(1.1) logits")
+            results[f"prefill_{Mp}rows"] = res
+            log(f"[bench] prefill {Mp}: {res['ms_per_layer']:.3f} ms/layer, experts {res['experts_read']:.0f}, "
+                f"{res['useful_TFLOPs']:.1f} TFLOP/s, gate/up {res['gateup_us'] / 1e3:.3f} ms, "
+                f"ffn {res['ffn_us'] / 1e3:.3f} ms")
 
     # ------------------------------------------------------------ Q8_0 spine matmul
     if "q8_0" in only:

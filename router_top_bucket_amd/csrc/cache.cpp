@@ -218,8 +218,15 @@ int moe_layer_streamed(moe_expert_cache *cache, int32_t layer, const void *x, mo
     for (int j = a; j < b; ++j) lists[pos++] = c.ex[miss_idx[j]];
     counts[1 + g] = b - a;
   }
-  if (hipMemcpyAsync(c.d_plan, c.h_plan, sizeof(int32_t) * c.plan_ints(), hipMemcpyHostToDevice, st) != hipSuccess)
+  // from here on a failure leaves this call's admitted misses unfilled: they
+  // leave the cache, so no later call takes a never-uploaded slot for a hit
+  auto fail = [&]() {
+    for (int i = 0; i < n; ++i)
+      if (c.adm[i]) c.policy.forget(layer, c.ex[i]);
     return MOE_EHIP;
+  };
+  if (hipMemcpyAsync(c.d_plan, c.h_plan, sizeof(int32_t) * c.plan_ints(), hipMemcpyHostToDevice, st) != hipSuccess)
+    return fail();
   const int32_t *d_map = c.d_plan, *d_lists = c.d_plan + NE, *d_counts = c.d_plan + 2 * NE;
 
   auto ffn = [&](int list_start, int count_idx, int count) -> int {
@@ -228,7 +235,7 @@ int moe_layer_streamed(moe_expert_cache *cache, int32_t layer, const void *x, mo
                            d_lists + list_start, d_counts + count_idx, y_slots, workspace,
                            moe::kStageGateUp | moe::kStageDown, d_map, cf.n_slots, count, st);
   };
-  if (ffn(0, 0, counts[0])) return MOE_EHIP;
+  if (ffn(0, 0, counts[0])) return fail();
   int lstart = counts[0], up_i = 0;
   for (int g = 0; g < groups && misses > 0; ++g) {
     bool used[kMaxUploadStreams] = {};
@@ -238,17 +245,17 @@ int moe_layer_streamed(moe_expert_cache *cache, int32_t layer, const void *x, mo
       const int s = up_i++ % cf.n_upload_streams;
       uint8_t *dst = (uint8_t *)cf.device_pool + (int64_t)(c.policy_base + c.slot[i]) * cf.stride;
       const uint8_t *src = (const uint8_t *)cf.host_pool + ((int64_t)layer * NE + c.ex[i]) * cf.stride;
-      if (hipMemcpyAsync(dst, src, (size_t)cf.stride, hipMemcpyHostToDevice, c.up[s]) != hipSuccess) return MOE_EHIP;
+      if (hipMemcpyAsync(dst, src, (size_t)cf.stride, hipMemcpyHostToDevice, c.up[s]) != hipSuccess) return fail();
       used[s] = true;
     }
     for (int s = 0; s < cf.n_upload_streams; ++s)
       if (used[s] && (hipEventRecord(c.ev[g][s], c.up[s]) != hipSuccess ||
                       hipStreamWaitEvent(st, c.ev[g][s], 0) != hipSuccess))
-        return MOE_EHIP;
-    if (ffn(lstart, 1 + g, b - a)) return MOE_EHIP;
+        return fail();
+    if (ffn(lstart, 1 + g, b - a)) return fail();
     lstart += b - a;
   }
-  if (moe::combine_launch(y_slots, topk_w, M, k, S, cf.d, out, st)) return MOE_EHIP;
+  if (moe::combine_launch(y_slots, topk_w, M, k, S, cf.d, out, st)) return fail();
 
   c.stats.calls += 1;
   c.stats.hits += n - misses;

@@ -89,6 +89,17 @@ class CachePolicy {
     return misses;
   }
 
+  // Drops (layer, expert) from the cache if it is there (its slot becomes
+  // free): for an expert whose upload could not be enqueued.
+  void forget(int layer, int e) {
+    if (layer < 0 || layer >= n_layers_ || e < 0 || e >= n_routed_) return;
+    const size_t k = key(layer, e);
+    const int s = slot_of_[k];
+    if (s < 0) return;
+    slot_of_[k] = -1;
+    key_of_[s] = -1;
+  }
+
  private:
   size_t key(int layer, int e) const { return (size_t)layer * n_routed_ + e; }
   // lowest free cached slot, else the least recently used one not held by
