@@ -186,3 +186,64 @@ def test_layer_validation():
     assert call(wsp=FAKE + 16) == EINVAL
     assert call(ex=_experts(n_routed=5000, n_shared=0)) == EUNSUP
     assert call(M=0) == moe.MOE_OK
+
+
+def test_cache_and_streamed_layer_validation():
+    import router_top_bucket_amd as moe
+    lib = moe.raw_library()
+    EINVAL = moe.MOE_EINVAL
+
+    def cfg(**kw):
+        v = dict(device_pool=FAKE, n_slots=20, host_pool=FAKE, n_layers=2, n_routed=16, n_shared=1, d=256, f=128,
+                 stride=52224, n_upload_streams=4, upload_groups=2, admit_min_rows=0, n_transient=2)
+        v.update(kw)
+        return moe._CacheConfig(*[v[name] for name, _ in moe._CacheConfig._fields_])
+
+    h = ctypes.c_void_p()
+    assert lib.moe_cache_create(None, ctypes.byref(h)) == EINVAL
+    for bad in (dict(device_pool=0), dict(host_pool=0), dict(n_layers=0), dict(d=100), dict(f=50),
+                dict(stride=1000), dict(stride=52224 + 8), dict(device_pool=FAKE + 4), dict(n_upload_streams=0),
+                dict(n_upload_streams=9), dict(upload_groups=0), dict(upload_groups=17), dict(admit_min_rows=-1),
+                dict(n_transient=-1), dict(n_slots=2 * 1 + 2)):  # no cached slot left
+        c = cfg(**bad)
+        assert lib.moe_cache_create(ctypes.byref(c), ctypes.byref(h)) == EINVAL, bad
+    assert lib.moe_cache_destroy(None) == EINVAL
+    assert lib.moe_cache_get_stats(None, ctypes.byref(moe._CacheStats())) == EINVAL
+    assert lib.moe_layer_streamed(None, 0, FAKE, 0, None, FAKE, 1, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  FAKE, FAKE, FAKE, 1 << 20, None) == EINVAL
+
+
+def test_cache_simulate_validation():
+    import router_top_bucket_amd as moe
+    lib = moe.raw_library()
+    EINVAL = moe.MOE_EINVAL
+    assert lib.moe_cache_simulate(0, 16, 4, 0, 0, 0, None, None, None, None, None, None, None) == EINVAL
+    assert lib.moe_cache_simulate(1, 16, 0, 0, 0, 0, None, None, None, None, None, None, None) == EINVAL
+    assert lib.moe_cache_simulate(1, 16, 4, -1, 0, 0, None, None, None, None, None, None, None) == EINVAL
+    assert lib.moe_cache_simulate(1, 16, 4, 0, 0, 1, None, None, None, None, None, None, None) == EINVAL
+    assert lib.moe_cache_simulate(1, 16, 4, 0, 0, 0, None, None, None, None, None, None, None) == moe.MOE_OK
+
+
+def test_verify_helpers_validation():
+    import router_top_bucket_amd as moe
+    lib = moe.raw_library()
+    EINVAL = moe.MOE_EINVAL
+    assert lib.q8_0_rows(FAKE, 1, 100, FAKE, FAKE, 10, FAKE, None) == EINVAL       # K % 32
+    assert lib.q8_0_rows(None, 1, 128, FAKE, FAKE, 10, FAKE, None) == EINVAL
+    assert lib.q8_0_rows(FAKE, 1, 128, FAKE, FAKE, 10, FAKE + 4, None) == EINVAL   # X alignment
+    assert lib.q8_0_rows(FAKE, 0, 128, FAKE, FAKE, 10, FAKE, None) == moe.MOE_OK
+    assert lib.moe_residual_bf16(None, FAKE, 10, None, None) == EINVAL
+    assert lib.moe_residual_bf16(FAKE, None, 10, None, None) == EINVAL             # nothing to do
+    assert lib.moe_residual_bf16(FAKE, FAKE, -1, None, None) == EINVAL
+    assert lib.moe_residual_bf16(FAKE, FAKE, 0, None, None) == moe.MOE_OK
+    assert lib.moe_rmsnorm(FAKE, 1, 0, 1e-6, FAKE, None, None) == EINVAL
+    assert lib.moe_rmsnorm(FAKE, 1, 16, 1e-6, None, None, None) == EINVAL
+    assert lib.moe_rmsnorm(FAKE, 1, 16, -1.0, FAKE, None, None) == EINVAL
+    assert lib.moe_rmsnorm(FAKE + 4, 1, 16, 1e-6, FAKE, None, None) == EINVAL
+    assert lib.moe_rmsnorm(FAKE, 0, 16, 1e-6, FAKE, None, None) == moe.MOE_OK
+    assert lib.moe_argmax_rows(FAKE, 1, 0, FAKE, None) == EINVAL
+    assert lib.moe_argmax_rows(FAKE + 4, 1, 8, FAKE, None) == EINVAL
+    assert lib.moe_argmax_rows(FAKE, 0, 8, FAKE, None) == moe.MOE_OK
+    assert lib.moe_fnv1a_rows(FAKE, 1, 8, FAKE + 4, None) == EINVAL
+    assert lib.moe_fnv1a_rows(FAKE, 1, 0, FAKE, None) == EINVAL
+    assert lib.moe_fnv1a_rows(FAKE, 0, 8, FAKE, None) == moe.MOE_OK
