@@ -38,6 +38,14 @@
  *    s has id n_routed + s.
  * E8M0 byte 255 (NaN) and bytes that would make a weight overflow fp32 are
  * outside the supported input range.
+ *
+ * Codes-plane order (moe_layout): the order above is MOE_LAYOUT_ROWS.  In
+ * MOE_LAYOUT_TILES the blocks of 32 elements (16 bytes) of each codes plane
+ * are permuted: block kb of row `row` sits at ((row/16)*(K/32) + kb)*256 +
+ * (row%16)*16, so one 16-row tile's blocks lie side by side; scales planes
+ * and record size are unchanged.  Every function gives bit-identical results
+ * for the two orders; the tile order reads faster (each wave's load is one
+ * contiguous kilobyte).  moe_pack_experts converts between them.
  */
 #ifndef MOE_H
 #define MOE_H
@@ -58,6 +66,8 @@ typedef enum {
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
+typedef enum { MOE_LAYOUT_ROWS = 0, MOE_LAYOUT_TILES = 1 } moe_layout;
+
 /* One layer's experts, resident in device memory. */
 typedef struct {
   const uint8_t *base; /* device: (n_routed + n_shared) * stride bytes, 16-byte aligned */
@@ -66,6 +76,7 @@ typedef struct {
   int32_t f;           /* expert FFN width, multiple of 32 */
   int32_t n_routed;    /* E */
   int32_t n_shared;    /* S, applied to every row with weight 1 */
+  int32_t layout;      /* moe_layout of the codes planes */
 } moe_experts;
 
 /* Router ("Read the experts the router needs": the router picks 16 of 896
@@ -145,6 +156,14 @@ int moe_ffn_down_mxfp4(int32_t M, int32_t k, const moe_experts *W, const int32_t
                        const int32_t *active, const int32_t *n_active, float *y_slots, void *workspace,
                        size_t workspace_bytes, void *stream);
 
+/* Copies n_records expert records (d, f, stride as in moe_experts) from src
+ * to dst with their codes planes in order `to_layout` (src holds the other
+ * order); scales planes and padding are copied unchanged.  src and dst are
+ * distinct device buffers of n_records * stride bytes, 16-byte aligned.
+ * Converting back gives the original bytes. */
+int moe_pack_experts(const uint8_t *src, uint8_t *dst, int64_t n_records, int64_t stride, int32_t d, int32_t f,
+                     moe_layout to_layout, void *stream);
+
 /* Bytes of workspace moe_expert_ffn_mxfp4 needs for M rows (host-only query;
  * returns 0 for invalid arguments). */
 size_t moe_workspace_bytes(int32_t M, int32_t k, const moe_experts *W);
@@ -210,6 +229,7 @@ typedef struct {
   int32_t upload_groups;   /* 1..16: misses are uploaded and computed in this many groups */
   int32_t admit_min_rows;  /* 0 = plain LRU */
   int32_t n_transient;     /* >= 0 */
+  int32_t layout;          /* moe_layout of the host pool's records (kept in the device pool) */
 } moe_cache_config;
 
 typedef struct {

@@ -19,10 +19,11 @@ from .build import LIB_PATH
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP = 0, -1, -2, -3
 MOE_F32, MOE_BF16 = 0, 1
+MOE_LAYOUT_ROWS, MOE_LAYOUT_TILES = 0, 1
 
 # names exported by include/moe.h
 ABI_FUNCTIONS = ("moe_route", "moe_bucket", "moe_expert_ffn_mxfp4", "moe_ffn_gateup_mxfp4", "moe_ffn_down_mxfp4",
-                 "moe_workspace_bytes", "moe_combine", "moe_layer_mxfp4", "moe_cache_create", "moe_cache_destroy",
+                 "moe_workspace_bytes", "moe_pack_experts", "moe_combine", "moe_layer_mxfp4", "moe_cache_create", "moe_cache_destroy",
                  "moe_cache_get_stats", "moe_layer_streamed", "moe_cache_simulate", "q8_0_matmul", "q8_0_rows",
                  "moe_residual_bf16", "moe_rmsnorm", "moe_argmax_rows", "moe_fnv1a_rows", "moe_status_str")
 
@@ -35,7 +36,8 @@ class MoeError(RuntimeError):
 
 class _Experts(ctypes.Structure):
     _fields_ = [("base", ctypes.c_void_p), ("stride", ctypes.c_int64), ("d", ctypes.c_int32),
-                ("f", ctypes.c_int32), ("n_routed", ctypes.c_int32), ("n_shared", ctypes.c_int32)]
+                ("f", ctypes.c_int32), ("n_routed", ctypes.c_int32), ("n_shared", ctypes.c_int32),
+                ("layout", ctypes.c_int32)]
 
 
 class _CacheConfig(ctypes.Structure):
@@ -43,7 +45,7 @@ class _CacheConfig(ctypes.Structure):
                 ("n_layers", ctypes.c_int32), ("n_routed", ctypes.c_int32), ("n_shared", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("f", ctypes.c_int32), ("stride", ctypes.c_int64),
                 ("n_upload_streams", ctypes.c_int32), ("upload_groups", ctypes.c_int32),
-                ("admit_min_rows", ctypes.c_int32), ("n_transient", ctypes.c_int32)]
+                ("admit_min_rows", ctypes.c_int32), ("n_transient", ctypes.c_int32), ("layout", ctypes.c_int32)]
 
 
 class _CacheStats(ctypes.Structure):
@@ -66,6 +68,7 @@ def _load() -> ctypes.CDLL:
         "moe_ffn_gateup_mxfp4": (ctypes.c_int, [P, ctypes.c_int, i32, i32, EP, P, P, P, P, P, sz, P]),
         "moe_ffn_down_mxfp4": (ctypes.c_int, [i32, i32, EP, P, P, P, P, P, P, sz, P]),
         "moe_workspace_bytes": (sz, [i32, i32, EP]),
+        "moe_pack_experts": (ctypes.c_int, [P, P, i64, i64, i32, i32, ctypes.c_int, P]),
         "moe_combine": (ctypes.c_int, [P, P, i32, i32, i32, i32, P, P]),
         "moe_layer_mxfp4": (ctypes.c_int, [P, ctypes.c_int, P, P, i32, i32, EP, P, P, P, P, P, P, P, P, P, P, sz, P]),
         "moe_cache_create": (ctypes.c_int, [ctypes.POINTER(_CacheConfig), ctypes.POINTER(P)]),
@@ -142,13 +145,14 @@ class Experts:
     n_routed: int
     n_shared: int
     whole_layer: bool = True  # False: a descriptor of shapes only (an expert cache's pool)
+    layout: int = MOE_LAYOUT_ROWS  # order of the codes planes (moe_pack_experts converts)
 
     def c_struct(self) -> _Experts:
         if self.base.dtype != torch.uint8:
             raise ValueError("expert base must be a uint8 tensor")
         if self.whole_layer and self.base.numel() < (self.n_routed + self.n_shared) * self.stride:
             raise ValueError("expert base tensor is too small")
-        return _Experts(_ptr(self.base), self.stride, self.d, self.f, self.n_routed, self.n_shared)
+        return _Experts(_ptr(self.base), self.stride, self.d, self.f, self.n_routed, self.n_shared, self.layout)
 
 
 # ----------------------------------------------------------------------------- ABI
@@ -182,6 +186,27 @@ def moe_bucket(topk_ids, E, n_shared, offsets, perm, active, n_active, dev_error
     rc = _lib.moe_bucket(_ptr(topk_ids), M, k, E, n_shared, _ptr(offsets), _ptr(perm), _ptr(active), _ptr(n_active),
                          _ptr(dev_error), _stream(stream))
     _check("moe_bucket", rc)
+
+
+def moe_pack_experts(src: torch.Tensor, dst: torch.Tensor, n_records: int, stride: int, d: int, f: int,
+                     to_layout: int, stream=None):
+    """dst = the n_records records of src with their codes planes in order
+    ``to_layout`` (src holds the other order); uint8 tensors on the GPU."""
+    for t in (src, dst):
+        if t.dtype != torch.uint8 or t.numel() < n_records * stride:
+            raise ValueError("src and dst must be uint8 tensors of n_records * stride bytes")
+    _check("moe_pack_experts", _lib.moe_pack_experts(_ptr(src), _ptr(dst), n_records, stride, d, f, to_layout,
+                                                     _stream(stream)))
+
+
+def tile_experts(ex: "Experts", stream=None) -> "Experts":
+    """A copy of a row-order expert table with its codes planes in tile order."""
+    if ex.layout != MOE_LAYOUT_ROWS:
+        raise ValueError("expected a row-order expert table")
+    n = ex.n_routed + ex.n_shared
+    dst = torch.empty(n * ex.stride, dtype=torch.uint8, device=ex.base.device)
+    moe_pack_experts(ex.base, dst, n, ex.stride, ex.d, ex.f, MOE_LAYOUT_TILES, stream)
+    return Experts(dst, ex.stride, ex.d, ex.f, ex.n_routed, ex.n_shared, layout=MOE_LAYOUT_TILES)
 
 
 def moe_workspace_bytes(M, k, experts: Experts) -> int:
@@ -343,7 +368,7 @@ class ExpertCache:
 
     def __init__(self, device_pool: torch.Tensor, host_pool: torch.Tensor, n_layers: int, n_routed: int,
                  n_shared: int, d: int, f: int, stride: int, n_upload_streams: int = 8, upload_groups: int = 4,
-                 admit_min_rows: int = 0, n_transient: int = 0):
+                 admit_min_rows: int = 0, n_transient: int = 0, layout: int = MOE_LAYOUT_ROWS):
         if device_pool.dtype != torch.uint8 or not device_pool.is_cuda:
             raise ValueError("device_pool must be a uint8 GPU tensor")
         if host_pool.dtype != torch.uint8 or host_pool.is_cuda or not host_pool.is_pinned():
@@ -354,8 +379,9 @@ class ExpertCache:
         self.n_slots = device_pool.numel() // stride
         self.n_layers, self.n_routed, self.n_shared, self.d, self.f, self.stride = (n_layers, n_routed, n_shared, d,
                                                                                     f, stride)
+        self.layout = layout
         cfg = _CacheConfig(device_pool.data_ptr(), self.n_slots, host_pool.data_ptr(), n_layers, n_routed, n_shared,
-                           d, f, stride, n_upload_streams, upload_groups, admit_min_rows, n_transient)
+                           d, f, stride, n_upload_streams, upload_groups, admit_min_rows, n_transient, layout)
         h = ctypes.c_void_p()
         _check("moe_cache_create", _lib.moe_cache_create(ctypes.byref(cfg), ctypes.byref(h)))
         self._h = h
@@ -364,7 +390,7 @@ class ExpertCache:
         """An Experts descriptor with this cache's shapes (for buffer sizing;
         the streamed call never addresses records through it)."""
         return Experts(self.device_pool, self.stride, self.d, self.f, self.n_routed, self.n_shared,
-                       whole_layer=False)
+                       whole_layer=False, layout=self.layout)
 
     def stats(self) -> dict:
         st = _CacheStats()

@@ -97,6 +97,7 @@ int moe_cache_create(const moe_cache_config *cfg, moe_expert_cache **out) {
   if (c.n_upload_streams < 1 || c.n_upload_streams > kMaxUploadStreams) return MOE_EINVAL;
   if (c.upload_groups < 1 || c.upload_groups > kMaxUploadGroups) return MOE_EINVAL;
   if (c.admit_min_rows < 0 || c.n_transient < 0) return MOE_EINVAL;
+  if (c.layout != MOE_LAYOUT_ROWS && c.layout != MOE_LAYOUT_TILES) return MOE_EINVAL;
   const int64_t shared = (int64_t)c.n_layers * c.n_shared;
   const int64_t n_cache = (int64_t)c.n_slots - shared - c.n_transient;
   if (n_cache < 1) return MOE_EINVAL;
@@ -163,7 +164,7 @@ int moe_layer_streamed(moe_expert_cache *cache, int32_t layer, const void *x, mo
   const int E = cf.n_routed, S = cf.n_shared, NE = c.NE();
   // the argument checks of moe_layer_mxfp4, on a descriptor of this layer's
   // device-pool view (its records are never addressed through it)
-  moe_experts W{(const uint8_t *)cf.device_pool, cf.stride, cf.d, cf.f, E, S};
+  moe_experts W{(const uint8_t *)cf.device_pool, cf.stride, cf.d, cf.f, E, S, cf.layout};
   const int rc = moe_layer_check(x, x_dtype, w_router, logits, M, k, &W, topk_ids, topk_w, offsets, perm, active,
                                  n_active, dev_error, y_slots, out, workspace, workspace_bytes);
   if (rc != MOE_OK || M == 0) return rc;
@@ -233,7 +234,8 @@ int moe_layer_streamed(moe_expert_cache *cache, int32_t layer, const void *x, mo
     if (count == 0) return 0;
     return moe::ffn_launch(x, bf, M, k, (const uint8_t *)cf.device_pool, cf.stride, cf.d, cf.f, E, S, offsets, perm,
                            d_lists + list_start, d_counts + count_idx, y_slots, workspace,
-                           moe::kStageGateUp | moe::kStageDown, d_map, cf.n_slots, count, st);
+                           moe::kStageGateUp | moe::kStageDown, d_map, cf.n_slots, count,
+                           cf.layout == MOE_LAYOUT_TILES, st);
   };
   if (ffn(0, 0, counts[0])) return fail();
   int lstart = counts[0], up_i = 0;

@@ -22,6 +22,7 @@ inline bool experts_ok(const moe_experts *W) {
   const int64_t rec = (int64_t)3 * W->d * W->f * 17 / 32;
   if (W->stride < rec || W->stride % 16) return false;
   if (reinterpret_cast<uintptr_t>(W->base) % 16) return false;
+  if (W->layout != MOE_LAYOUT_ROWS && W->layout != MOE_LAYOUT_TILES) return false;
   return true;
 }
 
@@ -53,7 +54,7 @@ int run_ffn(const void *x, moe_dtype x_dtype, int32_t M, int32_t k, const moe_ex
             int stages, void *stream) {
   return moe::ffn_launch(x, x_dtype == MOE_BF16, M, k, W->base, W->stride, W->d, W->f, W->n_routed, W->n_shared,
                          offsets, perm, active, n_active, y_slots, workspace, stages, nullptr, 0, 0,
-                         as_stream(stream)) == 0
+                         W->layout == MOE_LAYOUT_TILES, as_stream(stream)) == 0
              ? MOE_OK
              : MOE_EHIP;
 }
@@ -154,6 +155,20 @@ int moe_ffn_down_mxfp4(int32_t M, int32_t k, const moe_experts *W, const int32_t
   if (rc != MOE_OK || M == 0) return rc;
   return run_ffn(nullptr, MOE_BF16, M, k, W, offsets, perm, active, n_active, y_slots, workspace, moe::kStageDown,
                  stream);
+}
+
+int moe_pack_experts(const uint8_t *src, uint8_t *dst, int64_t n_records, int64_t stride, int32_t d, int32_t f,
+                     moe_layout to_layout, void *stream) {
+  if (!src || !dst || n_records < 0 || d <= 0 || f <= 0 || d % 32 || f % 32) return MOE_EINVAL;
+  if (to_layout != MOE_LAYOUT_ROWS && to_layout != MOE_LAYOUT_TILES) return MOE_EINVAL;
+  if (stride < (int64_t)3 * d * f * 17 / 32 || stride % 16) return MOE_EINVAL;
+  if (reinterpret_cast<uintptr_t>(src) % 16 || reinterpret_cast<uintptr_t>(dst) % 16) return MOE_EINVAL;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  const uintptr_t n = (uintptr_t)(n_records * stride);
+  if (a < b + n && b < a + n) return MOE_EINVAL;  // overlapping buffers
+  if (n_records == 0) return MOE_OK;
+  return status_of(moe::pack_launch(src, dst, n_records, stride, d, f, to_layout == MOE_LAYOUT_TILES,
+                                    as_stream(stream)));
 }
 
 int moe_combine(const float *y_slots, const float *topk_w, int32_t M, int32_t k, int32_t n_shared, int32_t d,

@@ -42,7 +42,21 @@ struct GroupSrc {
   const int32_t *n_groups; // plan mode
   const int32_t *slot_map; // null: expert e is record e; else record slot_map[e]
   int n_records;           // records at the weights base (with slot_map)
+  int tiled;               // codes planes in tile order (MOE_LAYOUT_TILES), else row order
 };
+
+// Where lane (r, q) of a 16-row tile finds its 16 bytes of codes (32
+// elements: block 4s+q of row `row`, row % 16 == r) inside a codes plane of
+// K columns, at step 0; step s adds s * code_step().
+//   row order:  row * K/2 + (4s+q) * 16
+//   tile order: ((row/16) * K/32 + 4s+q) * 256 + (row%16) * 16, so the 64
+//               lanes of one load read 1 KB in one piece (a permutation of
+//               the same blocks: every lane gets the same bytes)
+__device__ __forceinline__ uint32_t code_off(const GroupSrc &src, int row, int r, int q, int K) {
+  return src.tiled ? (uint32_t)(row >> 4) * (uint32_t)(K * 8) + (uint32_t)(r * 16 + q * 256)
+                   : (uint32_t)row * (uint32_t)(K / 2) + (uint32_t)(q * 16);
+}
+__device__ __forceinline__ uint32_t code_step(const GroupSrc &src) { return src.tiled ? 1024u : 64u; }
 
 // Buffer resource over an expert's record.  With a slot map the record index
 // is looked up, and an index outside [0, n_records) gives an empty resource:
@@ -403,7 +417,7 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
     const int tm = PAIR ? t / TPW : mat;  // matrix of tile t
     const int lrow = (rw * TPW + t % TPW) * 16 + r;
     const int row = i0 + lrow;
-    aoff[t] = sel_off(row < f, (tm ? plane_c + plane_s : 0u) + (uint32_t)row * (uint32_t)(d / 2));
+    aoff[t] = sel_off(row < f, (tm ? plane_c + plane_s : 0u) + code_off(src, row, r, q, d));
     srow[t] = lds + (tm * ROWS + lrow) * sc_pitch(d);
   }
   f32x4 acc[NT];
@@ -418,9 +432,9 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
   // counter retires in order): the codes, scales and x of step s are issued
   // together, PF-1 steps before they are used.  A dead step (past d) adds
   // kDead to every offset, which lands past every resource.
+  const uint32_t cstep = code_step(src);
   auto issue = [&](int s, int p) {
-    const int kq = (s << 7) + (q << 5);
-    const uint32_t ka = s < smax ? (uint32_t)(kq >> 1) : kDead;
+    const uint32_t ka = s < smax ? (uint32_t)s * cstep : kDead;
 #pragma unroll
     for (int t = 0; t < NT; ++t) ring[p][t] = buf_load16(wr, aoff[t] + ka);
 #pragma unroll
@@ -669,7 +683,7 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_wide_kernel(
   for (int t = 0; t < NT; ++t) {
     const int tm = t >> 1;
     const int row = i0 + wv * 32 + (t & 1) * 16 + r;
-    aoff[t] = sel_off(row < f, (tm ? plane_c + plane_s : 0u) + (uint32_t)row * (uint32_t)(d / 2));
+    aoff[t] = sel_off(row < f, (tm ? plane_c + plane_s : 0u) + code_off(src, row, r, q, d));
     soff[t] = sel_off(row < f, (tm ? 2 * plane_c + plane_s : plane_c) + (uint32_t)row * (uint32_t)nb + 4u * q);
   }
   f32x4 acc[NT][NCB];
@@ -684,9 +698,9 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_wide_kernel(
   u32x4 ring[PF][NT];
   u32x4 xst[PF][SPT][EL / 2];
   uint32_t sc_cur[NT], sc_nxt[NT];
+  const uint32_t cstep = code_step(src);
   auto issue = [&](int s, int p) {
-    const int kq = (s << 7) + (q << 5);
-    const uint32_t ka = s < smax ? (uint32_t)(kq >> 1) : kDead;
+    const uint32_t ka = s < smax ? (uint32_t)s * cstep : kDead;
 #pragma unroll
     for (int t = 0; t < NT; ++t) ring[p][t] = buf_load16(wr, aoff[t] + ka);
 #pragma unroll
@@ -873,7 +887,7 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
   for (int t = 0; t < TPW; ++t) {
     const int lrow = (rgw * TPW + t) * 16 + r;
     const int row = r0 + lrow;
-    aoff[t] = sel_off(row < d, dn_c + (uint32_t)row * (uint32_t)(f / 2));
+    aoff[t] = sel_off(row < d, dn_c + code_off(src, row, r, q, f));
     srow[t] = lds + lrow * sc_pitch(f);
   }
   f32x4 acc[TPW][NCBW];
@@ -886,9 +900,9 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
   const int smax = (f - (q << 5) + 127) >> 7;
   u32x4 ring[PF][TPW];
   u32x4 hst[PF][SPTA];
+  const uint32_t cstep = code_step(src);
   auto issue = [&](int s, int p) {
-    const int kq = (s << 7) + (q << 5);
-    const uint32_t ka = s < smax ? (uint32_t)(kq >> 1) : kDead;
+    const uint32_t ka = s < smax ? (uint32_t)s * cstep : kDead;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) ring[p][t] = buf_load16(wr, aoff[t] + ka);
 #pragma unroll
@@ -1111,7 +1125,7 @@ static int launch_down(int d, int f, int T, const uint8_t *experts, int64_t stri
 int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *experts, int64_t stride, int d, int f,
                int n_routed, int n_shared, const int32_t *offsets, const int32_t *perm, const int32_t *active,
                const int32_t *n_active, float *y, void *workspace, int stages, const int32_t *slot_map,
-               int n_records, int64_t max_active, hipStream_t stream) {
+               int n_records, int64_t max_active, int tiled, hipStream_t stream) {
   const int S = n_shared;
   const int kps = k + S;
   const int64_t T = M * kps;
@@ -1139,7 +1153,7 @@ int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *exper
 
   GroupSrc src[kGroupClasses];
   for (int c = 0; c < kGroupClasses; ++c)
-    src[c] = GroupSrc{offsets, active, n_active, nullptr, nullptr, slot_map, n_records};
+    src[c] = GroupSrc{offsets, active, n_active, nullptr, nullptr, slot_map, n_records, tiled};
   if (many) {
     // the group plan lives in the workspace and serves both stages
     if (stages & kStageGateUp) {

@@ -21,11 +21,18 @@ bool ffn_shape_ok(int64_t M, int k, int S, int d, int f, int64_t stride);
 constexpr int kStageGateUp = 1, kStageDown = 2;
 // slot_map (device, [n_routed + n_shared], or null): expert e's record is
 // slot_map[e] of the n_records at `experts` (null: record e).  max_active > 0:
-// *n_active never exceeds it (sizes the grids with few rows).
+// *n_active never exceeds it (sizes the grids with few rows).  tiled: the
+// records' codes planes are in tile order (pack_launch).
 int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *experts, int64_t stride, int d, int f,
                int n_routed, int n_shared, const int32_t *offsets, const int32_t *perm, const int32_t *active,
                const int32_t *n_active, float *y, void *workspace, int stages, const int32_t *slot_map,
-               int n_records, int64_t max_active, hipStream_t stream);
+               int n_records, int64_t max_active, int tiled, hipStream_t stream);
+
+// Copies n_records expert records from src to dst (distinct buffers), the
+// codes planes permuted from row to tile order (to_tiles) or back; every
+// other byte of a record is copied as is.
+int pack_launch(const uint8_t *src, uint8_t *dst, int64_t n_records, int64_t stride, int d, int f, int to_tiles,
+                hipStream_t stream);
 
 int combine_launch(const float *y, const float *w, int M, int k, int S, int d, float *out, hipStream_t stream);
 

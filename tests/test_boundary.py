@@ -85,9 +85,9 @@ def test_bucket_validation():
 
 def _experts(**kw):
     import router_top_bucket_amd as moe
-    v = dict(base=FAKE, stride=52224, d=256, f=128, n_routed=16, n_shared=0)
+    v = dict(base=FAKE, stride=52224, d=256, f=128, n_routed=16, n_shared=0, layout=0)
     v.update(kw)
-    return moe._Experts(v["base"], v["stride"], v["d"], v["f"], v["n_routed"], v["n_shared"])
+    return moe._Experts(v["base"], v["stride"], v["d"], v["f"], v["n_routed"], v["n_shared"], v["layout"])
 
 
 def test_ffn_validation_and_workspace_query():
@@ -97,7 +97,7 @@ def test_ffn_validation_and_workspace_query():
     ok = _experts()
     assert lib.moe_workspace_bytes(1, 2, ctypes.byref(ok)) > 0
     for bad in (_experts(d=100), _experts(f=50), _experts(stride=1000), _experts(base=0), _experts(n_routed=0),
-                _experts(base=FAKE + 4)):
+                _experts(base=FAKE + 4), _experts(layout=2), _experts(layout=-1)):
         assert lib.moe_workspace_bytes(1, 2, ctypes.byref(bad)) == 0
         assert lib.moe_expert_ffn_mxfp4(FAKE, 0, 1, 2, ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                         1 << 20, None) == EINVAL
@@ -195,7 +195,7 @@ def test_cache_and_streamed_layer_validation():
 
     def cfg(**kw):
         v = dict(device_pool=FAKE, n_slots=20, host_pool=FAKE, n_layers=2, n_routed=16, n_shared=1, d=256, f=128,
-                 stride=52224, n_upload_streams=4, upload_groups=2, admit_min_rows=0, n_transient=2)
+                 stride=52224, n_upload_streams=4, upload_groups=2, admit_min_rows=0, n_transient=2, layout=0)
         v.update(kw)
         return moe._CacheConfig(*[v[name] for name, _ in moe._CacheConfig._fields_])
 
@@ -204,7 +204,7 @@ def test_cache_and_streamed_layer_validation():
     for bad in (dict(device_pool=0), dict(host_pool=0), dict(n_layers=0), dict(d=100), dict(f=50),
                 dict(stride=1000), dict(stride=52224 + 8), dict(device_pool=FAKE + 4), dict(n_upload_streams=0),
                 dict(n_upload_streams=9), dict(upload_groups=0), dict(upload_groups=17), dict(admit_min_rows=-1),
-                dict(n_transient=-1), dict(n_slots=2 * 1 + 2)):  # no cached slot left
+                dict(n_transient=-1), dict(layout=2), dict(n_slots=2 * 1 + 2)):  # (last: no cached slot left)
         c = cfg(**bad)
         assert lib.moe_cache_create(ctypes.byref(c), ctypes.byref(h)) == EINVAL, bad
     assert lib.moe_cache_destroy(None) == EINVAL
@@ -247,3 +247,17 @@ def test_verify_helpers_validation():
     assert lib.moe_fnv1a_rows(FAKE, 1, 8, FAKE + 4, None) == EINVAL
     assert lib.moe_fnv1a_rows(FAKE, 1, 0, FAKE, None) == EINVAL
     assert lib.moe_fnv1a_rows(FAKE, 0, 8, FAKE, None) == moe.MOE_OK
+
+
+def test_pack_experts_validation():
+    import router_top_bucket_amd as moe
+    lib = moe.raw_library()
+    EINVAL = moe.MOE_EINVAL
+    B = FAKE * 16
+    assert lib.moe_pack_experts(None, B, 1, 52224, 256, 128, 1, None) == EINVAL
+    assert lib.moe_pack_experts(FAKE, B, 1, 52224, 256, 128, 2, None) == EINVAL     # layout
+    assert lib.moe_pack_experts(FAKE, B, 1, 52224, 100, 128, 1, None) == EINVAL     # d % 32
+    assert lib.moe_pack_experts(FAKE, B, 1, 1000, 256, 128, 1, None) == EINVAL      # stride too small
+    assert lib.moe_pack_experts(FAKE, FAKE + 16, 1, 52224, 256, 128, 1, None) == EINVAL  # overlap
+    assert lib.moe_pack_experts(FAKE + 8, B, 1, 52224, 256, 128, 1, None) == EINVAL  # alignment
+    assert lib.moe_pack_experts(FAKE, B, 0, 52224, 256, 128, 1, None) == moe.MOE_OK
