@@ -218,7 +218,7 @@ def run_stream(torch, moe, synth, shp, layers, stream, dev):
 
     def run(name, M, xfn, admit, warm, n):
         cache = moe.ExpertCache(pool, host, L, E, S, shp.d, shp.f, shp.stride, n_upload_streams=8, upload_groups=4,
-                                admit_min_rows=admit, n_transient=n_transient)
+                                admit_min_rows=admit, n_transient=n_transient, layout=layers[0][0].layout)
         ml = moe.MoELayer(cache.descriptor(), shp.k, M)
         xs = [xfn(i) for i in range(warm + n)]
 
@@ -298,11 +298,14 @@ def main():
     t0 = time.time()
     layers = []
     for seed in range(L):
-        base = synth.device_experts(shp, seed, device=dev)
-        layers.append((moe.Experts(base, shp.stride, shp.d, shp.f, shp.n_routed, shp.n_shared),
-                       torch.from_numpy(synth.router_weight(shp, seed)).to(dev)))
+        # records are generated in row order, then packed to tile order (the
+        # order the kernels read fastest; outputs are the same bits)
+        rows = moe.Experts(synth.device_experts(shp, seed, device=dev), shp.stride, shp.d, shp.f, shp.n_routed,
+                           shp.n_shared)
+        layers.append((moe.tile_experts(rows), torch.from_numpy(synth.router_weight(shp, seed)).to(dev)))
+        del rows
     log(f"[bench] {L} layers resident: {L * shp.n_experts} experts, {L * shp.n_experts * shp.stride / 1e9:.1f} GB "
-        f"in {time.time() - t0:.1f}s")
+        f"in {time.time() - t0:.1f}s (codes planes in tile order)")
     results = {}
     gu_bytes_per_expert = 2 * shp.f * shp.d * 17 // 32  # gate + up, codes and scales
 
@@ -513,7 +516,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "kimi_moe_layer_decode_1row", "d": shp.d, "f": shp.f, "routed_experts": shp.n_routed,
-                   "shared_experts": shp.n_shared, "top_k": shp.k, "rows": 1, "weights": "mxfp4",
+                   "shared_experts": shp.n_shared, "top_k": shp.k, "rows": 1,
+                   "weights": "mxfp4, codes planes in tile order (moe_pack_experts)",
                    "x": "bf16", "router": "fp32",
                    "timing": f"{N_LAYERS} resident layers in rotation, back-to-back steps between two HIP events"},
         "roofline": roof,

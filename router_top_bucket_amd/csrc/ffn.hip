@@ -1182,20 +1182,22 @@ int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *exper
         : launch_down<T, D, P, C, false, R, CS>(d, f, T_, experts, stride, src[CL], perm, cap[CL], h_ws, y, stream))
   // few rows: each group's B operand (x or h) stays resident in LDS for the
   // whole reduction; more rows: B is staged step by step through a ring.
-  // Launch shapes (measured at the Kimi shape): gate/up 2 waves each with
-  // the W_gate and W_up tiles of 16 rows (32 rows of f) and a 4-step ring at
-  // 1-2 rows, 8 waves (4 W_gate + 4 W_up) with a 4-step ring beyond, and
-  // the wide kernel (8 waves x 32 rows) for the 32- and 64-slot groups; down
-  // 4 waves x 1 tile (64 rows of d) at up to 4 rows, 8 waves x 2 tiles beyond
-  // (fewer workgroups per group re-stage its h).  A resident B is used only
-  // where the LDS it takes still lets two or more workgroups share a CU.
+  // Launch shapes (measured at the Kimi shape on tile-ordered records):
+  // gate/up 4 waves each with the W_gate and W_up tiles of 16 rows (64 rows
+  // of f) and a 4-step ring at 1-2 rows, 4 (5-8 rows) or 8 waves (half
+  // W_gate, half W_up) with a 4-step ring beyond, and the wide kernel (8
+  // waves x 32 rows) for the 32- and 64-slot groups; down 8 waves x 2 tiles
+  // (256 rows of d) at 1 row, 8 waves x 1 tile at 2-4 rows, 8 waves x 2 tiles
+  // beyond.  A resident B is used only where the LDS it takes still lets two
+  // or more workgroups share a CU.
   int rc = 0;
   if (stages & kStageGateUp) {
     const int np = x_bf16 ? 1 : 3;
     const size_t half = (size_t)kMaxLds / 2;
     if (x_bf16) {
-      if (M == 1 && gateup_lds_bytes(d, 4, np, 1, true, 32) <= half) rc = MOE_GU(1, 1, 2, 4, 1, true, true);
-      else if (M == 2 && gateup_lds_bytes(d, 4, np, 2, true, 32) <= half) rc = MOE_GU(1, 1, 2, 4, 2, true, true);
+      if (M == 1 && gateup_lds_bytes(d, 4, np, 1, true, 64) <= half) rc = MOE_GU(1, 1, 4, 4, 1, true, true);
+      else if (M == 2 && gateup_lds_bytes(d, 4, np, 2, true, 64) <= half) rc = MOE_GU(1, 1, 4, 4, 2, true, true);
+      else if (M >= 5 && M <= 8) rc = MOE_GU(1, 1, 4, 4, 16, false, false);
       else rc = MOE_GU(1, 1, 8, 4, 16, false, false);
       if (!rc && wide) rc = MOE_GUW(1, 8, 4, 2, 1);
       if (!rc && wide) rc = MOE_GUW(1, 8, 4, 4, 2);
@@ -1209,8 +1211,8 @@ int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *exper
   }
   if (stages & kStageDown) {
     const size_t half = (size_t)kMaxLds / 2;
-    if (M == 1 && down_lds_bytes(f, 4, 1, true, 64) <= half) rc = MOE_DN(1, 4, 4, 1, true, 0, 1);
-    else if (M <= 4 && down_lds_bytes(f, 4, 4, true, 64) <= half) rc = MOE_DN(1, 4, 4, 4, true, 0, 1);
+    if (M == 1 && down_lds_bytes(f, 4, 1, true, 256) <= half) rc = MOE_DN(2, 8, 4, 1, true, 0, 1);
+    else if (M <= 4 && down_lds_bytes(f, 4, 4, true, 128) <= half) rc = MOE_DN(1, 8, 4, 4, true, 0, 1);
     else rc = MOE_DN(2, 8, 4, 16, false, 0, 1);
     if (!rc && wide) rc = MOE_DN(4, 8, 4, 32, false, 1, 2);
     if (!rc && wide) rc = MOE_DN(4, 8, 2, 64, false, 2, 2);
