@@ -279,6 +279,18 @@ int moe_cache_simulate(int32_t n_layers, int32_t n_routed, int32_t n_cache, int3
 int q8_0_matmul(const float *X, int32_t M, int32_t K, const int8_t *Wq, const uint16_t *Ws, int32_t N, float *Y,
                 void *stream);
 
+/* q8_0_matmul with Wq in the given order.  MOE_LAYOUT_TILES (N % 16 == 0):
+ * block b (32 bytes) of weight row n sits at ((n/16)*(K/32) + b)*512 +
+ * (n%16)*32, so one step of a 16-row tile is one contiguous kilobyte; the
+ * results are bit-identical to row order.  q8_0_pack converts Wq. */
+int q8_0_matmul_layout(const float *X, int32_t M, int32_t K, const int8_t *Wq, const uint16_t *Ws, int32_t N,
+                       float *Y, moe_layout layout, void *stream);
+
+/* dst = the int8 plane [N x K] of src in order `to_layout` (src holds the
+ * other order); N % 16 == 0, K % 32 == 0, distinct 16-byte aligned device
+ * buffers.  The fp16 scales plane is the same in both orders. */
+int q8_0_pack(const int8_t *src, int8_t *dst, int32_t N, int32_t K, moe_layout to_layout, void *stream);
+
 /* ------------------------------------------------------------------------
  * Block verification ("A drafter that leaves the answer unchanged": a block
  * of up to 16 rows, the current token plus drafts, runs the same arithmetic
@@ -289,9 +301,10 @@ int q8_0_matmul(const float *X, int32_t M, int32_t K, const int8_t *Wq, const ui
 
 /* Rows of a Q8_0 matrix as fp32 (an embedding lookup):
  * X[m, c] = Wq[ids[m], c] * Ws[ids[m], c/32]; an id outside [0, N) gives a zero
- * row.  X [M x K] 16-byte aligned, Wq [N x K] 4-byte aligned, K % 32 == 0. */
+ * row.  Wq in either order (tiles: N % 16 == 0).  X [M x K] 16-byte aligned,
+ * Wq [N x K] 4-byte aligned, K % 32 == 0. */
 int q8_0_rows(const int32_t *ids, int32_t M, int32_t K, const int8_t *Wq, const uint16_t *Ws, int32_t N, float *X,
-              void *stream);
+              moe_layout layout, void *stream);
 
 /* Residual update: if a != NULL, h[i] += a[i] (fp32); then, if h_bf16 != NULL,
  * h_bf16[i] = bf16 bits of h[i], rounded to nearest even.  n >= 0 elements. */

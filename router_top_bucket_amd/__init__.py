@@ -24,7 +24,7 @@ MOE_LAYOUT_ROWS, MOE_LAYOUT_TILES = 0, 1
 # names exported by include/moe.h
 ABI_FUNCTIONS = ("moe_route", "moe_bucket", "moe_expert_ffn_mxfp4", "moe_ffn_gateup_mxfp4", "moe_ffn_down_mxfp4",
                  "moe_workspace_bytes", "moe_pack_experts", "moe_combine", "moe_layer_mxfp4", "moe_cache_create", "moe_cache_destroy",
-                 "moe_cache_get_stats", "moe_layer_streamed", "moe_cache_simulate", "q8_0_matmul", "q8_0_rows",
+                 "moe_cache_get_stats", "moe_layer_streamed", "moe_cache_simulate", "q8_0_matmul", "q8_0_matmul_layout", "q8_0_pack", "q8_0_rows",
                  "moe_residual_bf16", "moe_rmsnorm", "moe_argmax_rows", "moe_fnv1a_rows", "moe_status_str")
 
 
@@ -78,7 +78,9 @@ def _load() -> ctypes.CDLL:
                                               sz, P]),
         "moe_cache_simulate": (ctypes.c_int, [i32, i32, i32, i32, i32, i32, P, P, P, P, P, P, P]),
         "q8_0_matmul": (ctypes.c_int, [P, i32, i32, P, P, i32, P, P]),
-        "q8_0_rows": (ctypes.c_int, [P, i32, i32, P, P, i32, P, P]),
+        "q8_0_matmul_layout": (ctypes.c_int, [P, i32, i32, P, P, i32, P, ctypes.c_int, P]),
+        "q8_0_pack": (ctypes.c_int, [P, P, i32, i32, ctypes.c_int, P]),
+        "q8_0_rows": (ctypes.c_int, [P, i32, i32, P, P, i32, P, ctypes.c_int, P]),
         "moe_residual_bf16": (ctypes.c_int, [P, P, i64, P, P]),
         "moe_rmsnorm": (ctypes.c_int, [P, i32, i32, ctypes.c_float, P, P, P]),
         "moe_argmax_rows": (ctypes.c_int, [P, i32, i32, P, P]),
@@ -297,8 +299,17 @@ def moe_layer_mxfp4(x, w_router, logits, k, experts: Experts, topk_ids, topk_w, 
     _check("moe_layer_mxfp4", rc)
 
 
-def q8_0_matmul(X, Wq, Ws, Y, stream=None):
-    """Y[M x N] = X[M x K] . W^T with W in Q8_0 (int8 [N x K], fp16 bits [N x K/32])."""
+def q8_0_pack(src, dst, to_layout, stream=None):
+    """dst = the int8 plane src [N x K] in order ``to_layout`` (src in the other order)."""
+    N, K = src.shape
+    if src.dtype != torch.int8 or dst.dtype != torch.int8 or tuple(dst.shape) != (N, K):
+        raise ValueError("q8_0_pack: int8 [N x K] tensors")
+    _check("q8_0_pack", _lib.q8_0_pack(_ptr(src), _ptr(dst), N, K, to_layout, _stream(stream)))
+
+
+def q8_0_matmul(X, Wq, Ws, Y, stream=None, layout=MOE_LAYOUT_ROWS):
+    """Y[M x N] = X[M x K] . W^T with W in Q8_0 (int8 [N x K] in order ``layout``,
+    fp16 bits [N x K/32])."""
     M, K = X.shape
     N = Wq.shape[0]
     if X.dtype != torch.float32 or Wq.dtype != torch.int8 or Ws.dtype not in (torch.int16, torch.uint16,
@@ -306,20 +317,21 @@ def q8_0_matmul(X, Wq, Ws, Y, stream=None):
         raise ValueError("q8_0 dtypes: X float32, Wq int8, Ws fp16 bits")
     if tuple(Wq.shape) != (N, K) or tuple(Ws.shape) != (N, K // 32) or tuple(Y.shape) != (M, N):
         raise ValueError("q8_0 shapes")
-    rc = _lib.q8_0_matmul(_ptr(X), M, K, _ptr(Wq), _ptr(Ws), N, _ptr(Y), _stream(stream))
+    rc = _lib.q8_0_matmul_layout(_ptr(X), M, K, _ptr(Wq), _ptr(Ws), N, _ptr(Y), layout, _stream(stream))
     _check("q8_0_matmul", rc)
 
 
 # ----------------------------------------------------------------------------- block-verification helpers
-def q8_0_rows(ids, Wq, Ws, X, stream=None):
-    """X[m] = row ids[m] of the Q8_0 matrix (int8 [N x K], fp16 bits [N x K/32]) in fp32."""
+def q8_0_rows(ids, Wq, Ws, X, stream=None, layout=MOE_LAYOUT_ROWS):
+    """X[m] = row ids[m] of the Q8_0 matrix (int8 [N x K] in order ``layout``,
+    fp16 bits [N x K/32]) in fp32."""
     M, K = X.shape
     N = Wq.shape[0]
     if ids.dtype != torch.int32 or ids.numel() != M or X.dtype != torch.float32 or Wq.dtype != torch.int8:
         raise ValueError("q8_0_rows: ids int32 [M], X float32 [M x K], Wq int8 [N x K]")
     if tuple(Wq.shape) != (N, K) or tuple(Ws.shape) != (N, K // 32):
         raise ValueError("q8_0_rows shapes")
-    _check("q8_0_rows", _lib.q8_0_rows(_ptr(ids), M, K, _ptr(Wq), _ptr(Ws), N, _ptr(X), _stream(stream)))
+    _check("q8_0_rows", _lib.q8_0_rows(_ptr(ids), M, K, _ptr(Wq), _ptr(Ws), N, _ptr(X), layout, _stream(stream)))
 
 
 def moe_residual_bf16(h, a=None, h_bf16=None, stream=None):

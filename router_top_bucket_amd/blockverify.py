@@ -29,8 +29,8 @@ from dataclasses import dataclass
 
 import torch
 
-from . import (Experts, MoELayer, moe_argmax_rows, moe_fnv1a_rows, moe_residual_bf16, moe_rmsnorm, q8_0_matmul,
-               q8_0_rows)
+from . import (MOE_LAYOUT_ROWS, MOE_LAYOUT_TILES, Experts, MoELayer, moe_argmax_rows, moe_fnv1a_rows,
+               moe_residual_bf16, moe_rmsnorm, q8_0_matmul, q8_0_pack, q8_0_rows)
 
 Q8_ROWS = 8  # the Q8_0 matmul takes up to 8 rows per call
 EPS = 1e-6
@@ -40,6 +40,13 @@ EPS = 1e-6
 class Q8Matrix:
     wq: torch.Tensor  # int8 [N x K], device
     ws: torch.Tensor  # fp16 bits [N x K/32] (int16), device
+    layout: int = MOE_LAYOUT_ROWS  # order of wq (q8_0_pack converts)
+
+    def tiled(self) -> "Q8Matrix":
+        """A copy with wq in tile order (N % 16 == 0)."""
+        dst = torch.empty_like(self.wq)
+        q8_0_pack(self.wq, dst, MOE_LAYOUT_TILES)
+        return Q8Matrix(dst, self.ws, MOE_LAYOUT_TILES)
 
 
 class Stack:
@@ -63,7 +70,7 @@ class Stack:
 
     def _q8(self, X, m: Q8Matrix, Y):
         for r in range(0, X.shape[0], Q8_ROWS):
-            q8_0_matmul(X[r:r + Q8_ROWS], m.wq, m.ws, Y[r:r + Q8_ROWS])
+            q8_0_matmul(X[r:r + Q8_ROWS], m.wq, m.ws, Y[r:r + Q8_ROWS], layout=m.layout)
 
     def run(self, tokens: torch.Tensor) -> torch.Tensor:
         """Logits [M x vocab] of M rows, row m fed token tokens[m] (int32, on
@@ -73,7 +80,7 @@ class Stack:
             raise ValueError("1..max_rows rows")
         self.tok[:M].copy_(tokens)
         h, a, n, hb = self.h[:M], self.a[:M], self.n[:M], self.hb[:M]
-        q8_0_rows(self.tok[:M], self.head.wq, self.head.ws, h)
+        q8_0_rows(self.tok[:M], self.head.wq, self.head.ws, h, layout=self.head.layout)
         for ml, spine in zip(self.mls, self.spines):
             moe_rmsnorm(h, n, None, EPS)
             self._q8(n, spine, a)

@@ -198,26 +198,45 @@ int moe_layer_mxfp4(const void *x, moe_dtype x_dtype, const float *w_router, flo
   return status_of(moe::combine_launch(y_slots, topk_w, M, k, S, d, out, st));
 }
 
-int q8_0_matmul(const float *X, int32_t M, int32_t K, const int8_t *Wq, const uint16_t *Ws, int32_t N, float *Y,
-                void *stream) {
+int q8_0_matmul_layout(const float *X, int32_t M, int32_t K, const int8_t *Wq, const uint16_t *Ws, int32_t N,
+                       float *Y, moe_layout layout, void *stream) {
   if (M < 0 || K <= 0 || K % 32 || N <= 0) return MOE_EINVAL;
   if (!X || !Wq || !Ws || !Y) return MOE_EINVAL;
   if (reinterpret_cast<uintptr_t>(X) % 16 || reinterpret_cast<uintptr_t>(Wq) % 16) return MOE_EINVAL;
+  if (layout != MOE_LAYOUT_ROWS && layout != MOE_LAYOUT_TILES) return MOE_EINVAL;
+  if (layout == MOE_LAYOUT_TILES && N % 16) return MOE_EINVAL;
   if (M > 8) return MOE_EUNSUPPORTED;
   if ((int64_t)(K / 32 + 2) * 64 * 2 > 65536) return MOE_EUNSUPPORTED;
   if (M == 0) return MOE_OK;
-  return status_of(moe::q8_0_launch(X, M, K, Wq, Ws, N, Y, as_stream(stream)));
+  return status_of(moe::q8_0_launch(X, M, K, Wq, Ws, N, Y, layout == MOE_LAYOUT_TILES, as_stream(stream)));
+}
+
+int q8_0_matmul(const float *X, int32_t M, int32_t K, const int8_t *Wq, const uint16_t *Ws, int32_t N, float *Y,
+                void *stream) {
+  return q8_0_matmul_layout(X, M, K, Wq, Ws, N, Y, MOE_LAYOUT_ROWS, stream);
+}
+
+int q8_0_pack(const int8_t *src, int8_t *dst, int32_t N, int32_t K, moe_layout to_layout, void *stream) {
+  if (!src || !dst || N <= 0 || K <= 0 || K % 32 || N % 16) return MOE_EINVAL;
+  if (to_layout != MOE_LAYOUT_ROWS && to_layout != MOE_LAYOUT_TILES) return MOE_EINVAL;
+  if (reinterpret_cast<uintptr_t>(src) % 16 || reinterpret_cast<uintptr_t>(dst) % 16) return MOE_EINVAL;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  const uintptr_t n = (uintptr_t)((int64_t)N * K);
+  if (a < b + n && b < a + n) return MOE_EINVAL;  // overlapping buffers
+  return status_of(moe::q8_0_pack_launch(src, dst, N, K, to_layout == MOE_LAYOUT_TILES, as_stream(stream)));
 }
 
 int q8_0_rows(const int32_t *ids, int32_t M, int32_t K, const int8_t *Wq, const uint16_t *Ws, int32_t N, float *X,
-              void *stream) {
+              moe_layout layout, void *stream) {
   if (M < 0 || K <= 0 || K % 32 || N <= 0) return MOE_EINVAL;
   if (!ids || !Wq || !Ws || !X) return MOE_EINVAL;
   if (reinterpret_cast<uintptr_t>(X) % 16 || reinterpret_cast<uintptr_t>(Wq) % 4 ||
       reinterpret_cast<uintptr_t>(Ws) % 2)
     return MOE_EINVAL;
+  if (layout != MOE_LAYOUT_ROWS && layout != MOE_LAYOUT_TILES) return MOE_EINVAL;
+  if (layout == MOE_LAYOUT_TILES && N % 16) return MOE_EINVAL;
   if (M == 0) return MOE_OK;
-  return status_of(moe::q8_0_rows_launch(ids, M, K, Wq, Ws, N, X, as_stream(stream)));
+  return status_of(moe::q8_0_rows_launch(ids, M, K, Wq, Ws, N, X, layout == MOE_LAYOUT_TILES, as_stream(stream)));
 }
 
 int moe_residual_bf16(float *h, const float *a, int64_t n, uint16_t *h_bf16, void *stream) {

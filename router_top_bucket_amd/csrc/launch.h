@@ -36,12 +36,14 @@ int pack_launch(const uint8_t *src, uint8_t *dst, int64_t n_records, int64_t str
 
 int combine_launch(const float *y, const float *w, int M, int k, int S, int d, float *out, hipStream_t stream);
 
-int q8_0_launch(const float *X, int M, int K, const int8_t *wq, const uint16_t *ws, int N, float *Y,
+// tiled: Wq in tile order (N % 16 == 0; q8_0_pack_launch)
+int q8_0_launch(const float *X, int M, int K, const int8_t *wq, const uint16_t *ws, int N, float *Y, int tiled,
                 hipStream_t stream);
+int q8_0_pack_launch(const int8_t *src, int8_t *dst, int N, int K, int to_tiles, hipStream_t stream);
 
 // block-verification harness (verify.hip)
 int q8_0_rows_launch(const int32_t *ids, int M, int K, const int8_t *wq, const uint16_t *ws, int N, float *X,
-                     hipStream_t stream);
+                     int tiled, hipStream_t stream);
 int residual_bf16_launch(float *h, const float *a, int64_t n, uint16_t *hb, hipStream_t stream);
 int rmsnorm_launch(const float *h, int M, int d, float eps, float *out, uint16_t *outb, hipStream_t stream);
 int argmax_rows_launch(const float *X, int M, int N, int32_t *idx, hipStream_t stream);

@@ -53,4 +53,27 @@ int pack_launch(const uint8_t *src, uint8_t *dst, int64_t n_records, int64_t str
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
+// Q8_0 int8 plane [N x K] (N % 16 == 0): block b (32 bytes) of row n at
+// n*K + 32b in row order and at ((n/16)*(K/32) + b)*512 + (n%16)*32 in tile
+// order.  One thread per 16-byte piece.
+__global__ void q8_0_pack_kernel(const int8_t *__restrict__ src, int8_t *__restrict__ dst, int N, int K,
+                                 int to_tiles) {
+  const int64_t per_row = K / 16, total = (int64_t)N * per_row, nb = K / 32;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t n = i / per_row, c = i - n * per_row;  // row-order piece: row n, piece c
+    const int64_t rows_off = n * K + c * 16;
+    const int64_t tiles_off = ((n >> 4) * nb + (c >> 1)) * 512 + (n & 15) * 32 + (c & 1) * 16;
+    const int64_t so = to_tiles ? rows_off : tiles_off, dof = to_tiles ? tiles_off : rows_off;
+    *(u32x4 *)(dst + dof) = *(const u32x4 *)(src + so);
+  }
+}
+
+int q8_0_pack_launch(const int8_t *src, int8_t *dst, int N, int K, int to_tiles, hipStream_t stream) {
+  const int64_t total = (int64_t)N * (K / 16);
+  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 256 * 64);
+  hipLaunchKernelGGL(q8_0_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, src, dst, N, K, to_tiles);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
 }  // namespace moe

@@ -26,6 +26,12 @@
 // bpermute hands each lane the dword of output row 4q' + i for the step.
 // Every global load is an unconditional buffer load (dead steps and masked
 // lanes read past the resource and get zeros).
+//
+// Weight order: rows (row n's K bytes contiguous) or tiles (N % 16 == 0:
+// block b of row n at ((n/16)*(K/32) + b)*512 + (n%16)*32, so the 16 rows of
+// a tile keep each block's 32-byte pieces side by side and one step of a
+// wave, 16 rows x 64 bytes, is one contiguous kilobyte).  Every lane loads the
+// same bytes in both orders, so the results are bit-identical.
 #include "common.h"
 #include "launch.h"
 
@@ -80,7 +86,7 @@ template <int RT, int PF, int EPL, int NMF, bool MASKED, int WPE>
 __global__ __launch_bounds__(Q8_MAX_WAVES * 64) __attribute__((amdgpu_waves_per_eu(WPE))) void q8_0_kernel(const float *__restrict__ X, int M, int K,
                                                                  const int8_t *__restrict__ wq,
                                                                  const uint16_t *__restrict__ ws, int N,
-                                                                 float *__restrict__ Y, int KS, int RG) {
+                                                                 float *__restrict__ Y, int KS, int RG, int tiled) {
   static_assert(kQ8Chunk % PF == 0, "ring depth divides the scale chunk");
   static_assert(EPL == 1 || EPL == 2 || EPL == 4 || EPL == 8, "X elements per lane");
   using L = Q8Lds<RT, NMF>;
@@ -111,7 +117,9 @@ __global__ __launch_bounds__(Q8_MAX_WAVES * 64) __attribute__((amdgpu_waves_per_
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const int rr = 16 * t + r < rows_here ? 16 * t + r : rows_here - 1;
-      woff[t] = (uint32_t)rr * (uint32_t)K + 16u * q;
+      woff[t] = tiled ? ((uint32_t)(rr >> 4) * (uint32_t)nb + (uint32_t)(q >> 1)) * 512u + (uint32_t)(rr & 15) * 32u +
+                            16u * (uint32_t)(q & 1)
+                      : (uint32_t)rr * (uint32_t)K + 16u * q;
       soff[t] = (uint32_t)rr * (uint32_t)nb * 2u;
     }
     // X: lane handles row xm, elements xk .. xk+EPL-1 of each step's 64
@@ -140,9 +148,10 @@ __global__ __launch_bounds__(Q8_MAX_WAVES * 64) __attribute__((amdgpu_waves_per_
     uint32_t xr[PF][EPL];
     uint32_t sc_cur[RT][4], sc_nxt[RT][4];
 
+    const uint32_t wsz = tiled ? 1024u : 64u;  // weight bytes a step advances by
     auto issue = [&](int s, int slot) {
       const bool live_step = s < s_end;  // uniform
-      const uint32_t wstep = live_step ? 64u * (uint32_t)s : kDead;
+      const uint32_t wstep = live_step ? wsz * (uint32_t)s : kDead;
       const uint32_t xstep = live_step ? 256u * (uint32_t)s : kDead;
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
@@ -323,7 +332,7 @@ __global__ __launch_bounds__(Q8_MAX_WAVES * 64) __attribute__((amdgpu_waves_per_
 // WPE is the register budget as a target of resident waves per SIMD.
 template <int RT, int PF, int EPL, int NMF, bool MASKED, int WPE>
 static int q8_run(const float *X, int M, int K, const int8_t *wq, const uint16_t *ws, int N, float *Y, int KS,
-                  int RG, hipStream_t stream) {
+                  int RG, int tiled, hipStream_t stream) {
   using L = Q8Lds<RT, NMF>;
   if (KS < 1 || RG < 1 || KS * RG > Q8_MAX_WAVES || M > EPL || 3 * M > 16 * NMF) return -3;
   const size_t smem = (size_t)KS * RG * L::kWave;
@@ -333,7 +342,8 @@ static int q8_run(const float *X, int M, int K, const int8_t *wq, const uint16_t
     return -3;
   const int64_t groups = ((int64_t)N + RT * 16 - 1) / (RT * 16);
   const int64_t grid = (groups + RG - 1) / RG;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * KS * RG), smem, stream, X, M, K, wq, ws, N, Y, KS, RG);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * KS * RG), smem, stream, X, M, K, wq, ws, N, Y, KS, RG,
+                     tiled);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
@@ -357,32 +367,32 @@ static bool q8_fast_path(int K, int KS, const uint16_t *ws) {
 
 // Launch shapes by X rows and weight size (measured on MI355X); none of them
 // changes the arithmetic, which depends on K and N only.
-int q8_0_launch(const float *X, int M, int K, const int8_t *wq, const uint16_t *ws, int N, float *Y,
+int q8_0_launch(const float *X, int M, int K, const int8_t *wq, const uint16_t *ws, int N, float *Y, int tiled,
                 hipStream_t stream) {
   const int KS = q8_k_parts(K, N);
   const int RG = Q8_MAX_WAVES / KS >= 4 ? 4 : 1;
   const bool big = ((int64_t)N + 15) / 16 >= 4096;
   if (!q8_fast_path(K, KS, ws)) {
-    if (M <= 1) return q8_run<2, 4, 1, 1, true, 1>(X, M, K, wq, ws, N, Y, KS, RG, stream);
-    if (M <= 2) return q8_run<2, 4, 2, 1, true, 1>(X, M, K, wq, ws, N, Y, KS, RG, stream);
-    if (M <= 4) return q8_run<2, 4, 4, 1, true, 1>(X, M, K, wq, ws, N, Y, KS, RG, stream);
-    if (M <= 5) return q8_run<2, 4, 8, 1, true, 1>(X, M, K, wq, ws, N, Y, KS, RG, stream);
-    return q8_run<2, 4, 8, 2, true, 1>(X, M, K, wq, ws, N, Y, KS, RG, stream);
+    if (M <= 1) return q8_run<2, 4, 1, 1, true, 1>(X, M, K, wq, ws, N, Y, KS, RG, tiled, stream);
+    if (M <= 2) return q8_run<2, 4, 2, 1, true, 1>(X, M, K, wq, ws, N, Y, KS, RG, tiled, stream);
+    if (M <= 4) return q8_run<2, 4, 4, 1, true, 1>(X, M, K, wq, ws, N, Y, KS, RG, tiled, stream);
+    if (M <= 5) return q8_run<2, 4, 8, 1, true, 1>(X, M, K, wq, ws, N, Y, KS, RG, tiled, stream);
+    return q8_run<2, 4, 8, 2, true, 1>(X, M, K, wq, ws, N, Y, KS, RG, tiled, stream);
   }
   if (M <= 1)
-    return big ? q8_run<2, 4, 1, 1, false, 1>(X, M, K, wq, ws, N, Y, KS, RG, stream)
-               : q8_run<1, 4, 1, 1, false, 6>(X, M, K, wq, ws, N, Y, KS, RG, stream);
+    return big ? q8_run<2, 4, 1, 1, false, 1>(X, M, K, wq, ws, N, Y, KS, RG, tiled, stream)
+               : q8_run<1, 4, 1, 1, false, 6>(X, M, K, wq, ws, N, Y, KS, RG, tiled, stream);
   if (M <= 2)
-    return big ? q8_run<2, 4, 2, 1, false, 1>(X, M, K, wq, ws, N, Y, KS, RG, stream)
-               : q8_run<1, 4, 2, 1, false, 1>(X, M, K, wq, ws, N, Y, KS, RG, stream);
+    return big ? q8_run<2, 4, 2, 1, false, 1>(X, M, K, wq, ws, N, Y, KS, RG, tiled, stream)
+               : q8_run<1, 4, 2, 1, false, 1>(X, M, K, wq, ws, N, Y, KS, RG, tiled, stream);
   if (M <= 4)
-    return big ? q8_run<2, 4, 4, 1, false, 1>(X, M, K, wq, ws, N, Y, KS, RG, stream)
-               : q8_run<2, 2, 4, 1, false, 5>(X, M, K, wq, ws, N, Y, KS, RG, stream);
+    return big ? q8_run<2, 4, 4, 1, false, 1>(X, M, K, wq, ws, N, Y, KS, RG, tiled, stream)
+               : q8_run<2, 2, 4, 1, false, 5>(X, M, K, wq, ws, N, Y, KS, RG, tiled, stream);
   if (M <= 5)
-    return big ? q8_run<2, 4, 8, 1, false, 1>(X, M, K, wq, ws, N, Y, KS, RG, stream)
-               : q8_run<2, 2, 8, 1, false, 4>(X, M, K, wq, ws, N, Y, KS, RG, stream);
-  return big ? q8_run<4, 2, 8, 2, false, 1>(X, M, K, wq, ws, N, Y, KS, RG, stream)
-             : q8_run<2, 2, 8, 2, false, 4>(X, M, K, wq, ws, N, Y, KS, RG, stream);
+    return big ? q8_run<2, 4, 8, 1, false, 1>(X, M, K, wq, ws, N, Y, KS, RG, tiled, stream)
+               : q8_run<2, 2, 8, 1, false, 4>(X, M, K, wq, ws, N, Y, KS, RG, tiled, stream);
+  return big ? q8_run<4, 2, 8, 2, false, 1>(X, M, K, wq, ws, N, Y, KS, RG, tiled, stream)
+             : q8_run<2, 2, 8, 2, false, 4>(X, M, K, wq, ws, N, Y, KS, RG, tiled, stream);
 }
 
 }  // namespace moe

@@ -11,10 +11,10 @@
 namespace moe {
 
 // ---- rows of a Q8_0 matrix as fp32: X[m, c] = Wq[ids[m], c] * Ws[ids[m], c/32]
-// (the product of an int8 and an fp16 is exact in fp32).  One thread per 4
-// consecutive c.  Ids outside [0, N) give a zero row.
+// (the product of an int8 and an fp16 is exact in fp32), Wq in row or tile
+// order.  One thread per 4 consecutive c.  Ids outside [0, N) give a zero row.
 __global__ void q8_0_rows_kernel(const int32_t *__restrict__ ids, int M, int K, const int8_t *__restrict__ wq,
-                                 const uint16_t *__restrict__ ws, int N, float *__restrict__ X) {
+                                 const uint16_t *__restrict__ ws, int N, float *__restrict__ X, int tiled) {
   const int K4 = K >> 2;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)M * K4) return;
@@ -22,7 +22,10 @@ __global__ void q8_0_rows_kernel(const int32_t *__restrict__ ids, int M, int K, 
   const int id = ids[m];
   f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
   if (id >= 0 && id < N) {
-    const uint32_t q = *(const uint32_t *)(wq + (int64_t)id * K + c);
+    // tile order (q8_0.hip): block c/32 of row id at ((id/16)*(K/32) + c/32)*512 + (id%16)*32
+    const int64_t off = tiled ? (((int64_t)(id >> 4) * (K >> 5) + (c >> 5)) * 512 + (id & 15) * 32 + (c & 31))
+                              : (int64_t)id * K + c;
+    const uint32_t q = *(const uint32_t *)(wq + off);
     const float s = (float)__builtin_bit_cast(_Float16, ws[(int64_t)id * (K >> 5) + (c >> 5)]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = (float)(int8_t)(q >> (8 * i)) * s;
@@ -172,10 +175,10 @@ __global__ void fnv1a_rows_kernel(const float *__restrict__ X, int M, int N, uin
 }
 
 int q8_0_rows_launch(const int32_t *ids, int M, int K, const int8_t *wq, const uint16_t *ws, int N, float *X,
-                     hipStream_t stream) {
+                     int tiled, hipStream_t stream) {
   const int64_t n = (int64_t)M * (K / 4);
   hipLaunchKernelGGL(q8_0_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, ids, M, K, wq, ws, N,
-                     X);
+                     X, tiled);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

@@ -228,10 +228,12 @@ def test_verify_helpers_validation():
     import router_top_bucket_amd as moe
     lib = moe.raw_library()
     EINVAL = moe.MOE_EINVAL
-    assert lib.q8_0_rows(FAKE, 1, 100, FAKE, FAKE, 10, FAKE, None) == EINVAL       # K % 32
-    assert lib.q8_0_rows(None, 1, 128, FAKE, FAKE, 10, FAKE, None) == EINVAL
-    assert lib.q8_0_rows(FAKE, 1, 128, FAKE, FAKE, 10, FAKE + 4, None) == EINVAL   # X alignment
-    assert lib.q8_0_rows(FAKE, 0, 128, FAKE, FAKE, 10, FAKE, None) == moe.MOE_OK
+    assert lib.q8_0_rows(FAKE, 1, 100, FAKE, FAKE, 10, FAKE, 0, None) == EINVAL       # K % 32
+    assert lib.q8_0_rows(None, 1, 128, FAKE, FAKE, 10, FAKE, 0, None) == EINVAL
+    assert lib.q8_0_rows(FAKE, 1, 128, FAKE, FAKE, 10, FAKE + 4, 0, None) == EINVAL   # X alignment
+    assert lib.q8_0_rows(FAKE, 1, 128, FAKE, FAKE, 10, FAKE, 1, None) == EINVAL       # tiles need N % 16
+    assert lib.q8_0_rows(FAKE, 1, 128, FAKE, FAKE, 16, FAKE, 2, None) == EINVAL       # layout
+    assert lib.q8_0_rows(FAKE, 0, 128, FAKE, FAKE, 10, FAKE, 0, None) == moe.MOE_OK
     assert lib.moe_residual_bf16(None, FAKE, 10, None, None) == EINVAL
     assert lib.moe_residual_bf16(FAKE, None, 10, None, None) == EINVAL             # nothing to do
     assert lib.moe_residual_bf16(FAKE, FAKE, -1, None, None) == EINVAL
@@ -261,3 +263,18 @@ def test_pack_experts_validation():
     assert lib.moe_pack_experts(FAKE, FAKE + 16, 1, 52224, 256, 128, 1, None) == EINVAL  # overlap
     assert lib.moe_pack_experts(FAKE + 8, B, 1, 52224, 256, 128, 1, None) == EINVAL  # alignment
     assert lib.moe_pack_experts(FAKE, B, 0, 52224, 256, 128, 1, None) == moe.MOE_OK
+
+
+def test_q8_0_layout_and_pack_validation():
+    import router_top_bucket_amd as moe
+    lib = moe.raw_library()
+    EINVAL = moe.MOE_EINVAL
+    assert lib.q8_0_matmul_layout(FAKE, 1, 128, FAKE, FAKE, 10, FAKE, 1, None) == EINVAL  # tiles need N % 16
+    assert lib.q8_0_matmul_layout(FAKE, 1, 128, FAKE, FAKE, 16, FAKE, 2, None) == EINVAL  # layout
+    assert lib.q8_0_matmul_layout(FAKE, 0, 128, FAKE, FAKE, 16, FAKE, 1, None) == moe.MOE_OK
+    B = FAKE * 16
+    assert lib.q8_0_pack(FAKE, B, 10, 128, 1, None) == EINVAL          # N % 16
+    assert lib.q8_0_pack(FAKE, B, 16, 100, 1, None) == EINVAL          # K % 32
+    assert lib.q8_0_pack(FAKE, B, 16, 128, 3, None) == EINVAL          # layout
+    assert lib.q8_0_pack(FAKE, FAKE + 64, 16, 128, 1, None) == EINVAL  # overlap
+    assert lib.q8_0_pack(None, B, 16, 128, 1, None) == EINVAL

@@ -27,13 +27,20 @@ def _dev(a):
 
 
 # ----------------------------------------------------------------------------- kernels
-def test_q8_0_rows_exact():
+@pytest.mark.parametrize("tiles", [False, True])
+def test_q8_0_rows_exact(tiles):
     moe = _moe()
-    K, N = 416, 300
+    K, N = 416, 304
     wq, ws = synth.q8_0_weight(9, K, N)
-    ids = np.array([0, 299, 17, 17, -1, 300, 5], dtype=np.int32)
+    ids = np.array([0, 303, 17, 17, -1, 304, 5], dtype=np.int32)
     X = torch.empty((len(ids), K), dtype=torch.float32, device="cuda")
-    moe.q8_0_rows(_dev(ids), _dev(wq), _dev(ws.view(np.int16)), X)
+    dwq = _dev(wq)
+    if tiles:
+        t = torch.empty_like(dwq)
+        moe.q8_0_pack(dwq, t, moe.MOE_LAYOUT_TILES)
+        dwq = t
+    moe.q8_0_rows(_dev(ids), dwq, _dev(ws.view(np.int16)), X,
+                  layout=moe.MOE_LAYOUT_TILES if tiles else moe.MOE_LAYOUT_ROWS)
     sc = ws.view(np.float16).astype(np.float32)
     ref = np.zeros((len(ids), K), dtype=np.float32)
     for m, i in enumerate(ids):
@@ -111,7 +118,7 @@ def test_fnv1a_rows_match_reference():
 
 # ----------------------------------------------------------------------------- the stack
 SMALL = synth.LayerShape("s3", 416, 224, 9, 2, 4, -7, -3, 0.05, "bf16")
-VOCAB = 1000
+VOCAB = 1008  # a multiple of 16, so the head can be tile-ordered
 
 
 def _small_stack(moe, n_layers=3):
@@ -169,7 +176,7 @@ def test_stack_composition_against_oracle():
     logits = stack.logits[:M].cpu().numpy()
     # replay on the GPU stage by stage, checking each against the oracle
     h = torch.empty((M, shape.d), dtype=torch.float32, device="cuda")
-    moe.q8_0_rows(_dev(tokens), stack.head.wq, stack.head.ws, h)
+    moe.q8_0_rows(_dev(tokens), stack.head.wq, stack.head.ws, h, layout=stack.head.layout)
     emb = hq[tokens].astype(np.float32) * np.repeat(hs.view(np.float16).astype(np.float32)[tokens], 32, axis=1)
     assert np.array_equal(h.cpu().numpy(), emb)
 
@@ -184,7 +191,7 @@ def test_stack_composition_against_oracle():
         hh = h.cpu().numpy()
         moe.moe_rmsnorm(h, n, None, EPS)
         assert_close(n.cpu().numpy(), norm(hh), f"layer {l} norm 1")
-        moe.q8_0_matmul(n, stack.spines[l].wq, stack.spines[l].ws, a)
+        moe.q8_0_matmul(n, stack.spines[l].wq, stack.spines[l].ws, a, layout=stack.spines[l].layout)
         assert_close(a.cpu().numpy(), oracle.q8_0_matmul(n.cpu().numpy(), host[l]["wq"], host[l]["ws"]),
                      f"layer {l} spine")
         a_h = a.cpu().numpy()
@@ -203,3 +210,15 @@ def test_stack_composition_against_oracle():
     moe.moe_rmsnorm(h, n, None, EPS)
     assert_close(logits, oracle.q8_0_matmul(n.cpu().numpy(), hq, hs), "head logits")
     assert np.array_equal(stack.next[:M].cpu().numpy(), logits.argmax(axis=1))
+
+
+def test_stack_with_tiled_weights_equals_row_order():
+    """Tile-ordered expert records and Q8_0 spines/head: the same logits bits."""
+    moe = _moe()
+    from router_top_bucket_amd.blockverify import Stack, plain_steps
+    stack, _, _ = _small_stack(moe)
+    tiled = Stack([(moe.tile_experts(ml.experts), ml.w_router) for ml in stack.mls],
+                  [sp.tiled() for sp in stack.spines], stack.head.tiled(), stack.k, 16)
+    a_tok, a_hash = plain_steps(stack, 11, 6)
+    b_tok, b_hash = plain_steps(tiled, 11, 6)
+    assert a_tok == b_tok and a_hash == b_hash

@@ -144,3 +144,46 @@ def test_streamed_tiles_equal_resident_rows():
         b = _outputs(st.forward_streamed(cache, layer, x), M, k, S)
         _same(a, b, f"streamed call {i}")
     cache.close()
+
+
+# ----------------------------------------------------------------------------- Q8_0 weights
+def _q8_tiles_ref(wq: np.ndarray) -> np.ndarray:
+    """Tile order of an int8 plane [N x K]: block b of row n goes to
+    ((n/16)*(K/32) + b)*512 + (n%16)*32."""
+    N, K = wq.shape
+    return wq.reshape(N // 16, 16, K // 32, 32).transpose(0, 2, 1, 3).reshape(-1)
+
+
+@pytest.mark.parametrize("N,K", [(48, 96), (7168, 7168), (160, 416)])
+def test_q8_0_pack_rule_and_round_trip(N, K):
+    moe = _moe()
+    wq, _ = synth.q8_0_weight(5, K, N)
+    src = torch.from_numpy(wq).cuda()
+    t = torch.empty_like(src)
+    back = torch.empty_like(src)
+    moe.q8_0_pack(src, t, moe.MOE_LAYOUT_TILES)
+    moe.q8_0_pack(t, back, moe.MOE_LAYOUT_ROWS)
+    torch.cuda.synchronize()
+    assert torch.equal(back, src)
+    assert np.array_equal(t.cpu().numpy().reshape(-1), _q8_tiles_ref(wq))
+
+
+@pytest.mark.parametrize("K,N", [(7168, 7168), (7168, 18432), (256, 96), (96, 48), (416, 160)])
+def test_q8_0_tiles_equal_rows(K, N):
+    moe = _moe()
+    wq, ws = synth.q8_0_weight(6, K, N)
+    dwq = torch.from_numpy(wq).cuda()
+    tiles = torch.empty_like(dwq)
+    moe.q8_0_pack(dwq, tiles, moe.MOE_LAYOUT_TILES)
+    # aligned scales (fast path where K allows) and scales one element off
+    # 16-byte alignment (the masked path)
+    sbuf = torch.from_numpy(np.concatenate([np.zeros(1, np.uint16), ws.reshape(-1)]).view(np.int16)).cuda()
+    for dws in (torch.from_numpy(ws.view(np.int16)).cuda(), sbuf[1:].view(N, K // 32)):
+        for M in range(1, 9):
+            X = torch.from_numpy(synth.q8_0_x(7, M, K)).cuda()
+            Ya = torch.empty((M, N), dtype=torch.float32, device="cuda")
+            Yb = torch.empty_like(Ya)
+            moe.q8_0_matmul(X, dwq, dws, Ya)
+            moe.q8_0_matmul(X, tiles, dws, Yb, layout=moe.MOE_LAYOUT_TILES)
+            torch.cuda.synchronize()
+            assert torch.equal(Ya.view(torch.int32), Yb.view(torch.int32)), (K, N, M)
