@@ -10,10 +10,14 @@
 // e, and rank = base[e] + popcount(mask[e] & bits below m).
 #include "common.h"
 #include "launch.h"
+#include "topk.h"
 
 namespace moe {
 
 constexpr int BK_THREADS = 1024;
+// Dynamic LDS the fused top-k + bucket kernel may take: gfx950 gives a
+// workgroup 160 KB in all, and the kernel holds about 4 KB of static LDS.
+constexpr int kTbMaxLds = 152 * 1024;
 
 // Expert of slot t, or -1 for a routed id outside [0, E).
 __device__ __forceinline__ int slot_expert(const int32_t *ids, int t, int k, int kps, int E) {
@@ -117,42 +121,38 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(const int32_t *__res
   if (tid == 0) *dev_error = err;
 }
 
-// Small batches (T <= 1024 slots, M <= 64 rows): one thread per slot keeps
-// its expert in a register, so the ids are read once; the counts and the
-// 64-row occupancy masks are built in the same pass, and the arithmetic of
-// every output is the general kernel's.
-__global__ __launch_bounds__(BK_THREADS) void bucket_small_kernel(const int32_t *__restrict__ ids, int M, int k, int E,
-                                                                  int S, int32_t *__restrict__ offsets,
-                                                                  int32_t *__restrict__ perm,
-                                                                  int32_t *__restrict__ active,
-                                                                  int32_t *__restrict__ n_active,
-                                                                  int32_t *__restrict__ dev_error) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  const int NE = E + S;
+// Small batches (T <= threads of the workgroup, M <= 64 rows): one thread
+// per slot keeps its expert in a register (e_mine: the expert, -1 for a
+// routed id outside [0, E), -2 for a thread without a slot), so the ids are
+// read once; the counts and the 64-row occupancy masks are built in the same
+// pass, and the arithmetic of every output is the general kernel's.  Every
+// thread of the workgroup calls it (it has barriers).  smem: NE 64-bit masks
+// then NE int32 counts; wave_sum: one pair per wave.
+__device__ __forceinline__ void bucket_small_body(int e_mine, int M, int kps, int NE, int32_t *__restrict__ offsets,
+                                                  int32_t *__restrict__ perm, int32_t *__restrict__ active,
+                                                  int32_t *__restrict__ n_active, int32_t *__restrict__ dev_error,
+                                                  uint8_t *smem, int32_t (*wave_sum)[2], int32_t *err) {
   unsigned long long *mask = (unsigned long long *)smem;  // [NE]
   int32_t *base = (int32_t *)(mask + NE);                 // [NE] counts, then bases
-  __shared__ int32_t wave_sum[16][2];
-  __shared__ int32_t err;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int kps = k + S;
+  const int nth = blockDim.x, nw = nth >> 6;
   const int T = M * kps;
-  const int e_mine = tid < T ? slot_expert(ids, tid, k, kps, E) : -2;
-  for (int e = tid; e < NE; e += BK_THREADS) {
+  for (int e = tid; e < NE; e += nth) {
     base[e] = 0;
     mask[e] = 0ull;
   }
-  if (tid == 0) err = 0;
+  if (tid == 0) *err = 0;
   __syncthreads();
   const unsigned long long bit = 1ull << (tid < T ? tid / kps : 0);
-  if (e_mine == -1) err = 1;
+  if (e_mine == -1) *err = 1;
   if (e_mine >= 0) {
     atomicAdd(&base[e_mine], 1);
     const unsigned long long old = atomicOr(&mask[e_mine], bit);
-    if (old & bit) err = 1;  // a row names the same expert twice
+    if (old & bit) *err = 1;  // a row names the same expert twice
   }
   __syncthreads();
   // exclusive scans of the counts (offsets) and of the nonempty flags (active)
-  const int per = (NE + BK_THREADS - 1) / BK_THREADS;
+  const int per = (NE + nth - 1) / nth;
   const int e_beg = tid * per;
   int c_loc = 0, a_loc = 0;
   for (int i = 0; i < per; ++i) {
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_small_kernel(const int32_t 
   if (lane == 63) { wave_sum[wv][0] = cv; wave_sum[wv][1] = av; }
   __syncthreads();
   int c_ex = cv - c_loc, a_ex = av - a_loc, c_tot = 0, a_tot = 0;
-  for (int w2 = 0; w2 < BK_THREADS / 64; ++w2) {
+  for (int w2 = 0; w2 < nw; ++w2) {
     if (w2 < wv) { c_ex += wave_sum[w2][0]; a_ex += wave_sum[w2][1]; }
     c_tot += wave_sum[w2][0];
     a_tot += wave_sum[w2][1];
@@ -193,7 +193,83 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_small_kernel(const int32_t 
     if (rank < T) perm[rank] = tid;
   }
   __syncthreads();
-  if (tid == 0) *dev_error = err;
+  if (tid == 0) *dev_error = *err;
+}
+
+__global__ __launch_bounds__(BK_THREADS) void bucket_small_kernel(const int32_t *__restrict__ ids, int M, int k, int E,
+                                                                  int S, int32_t *__restrict__ offsets,
+                                                                  int32_t *__restrict__ perm,
+                                                                  int32_t *__restrict__ active,
+                                                                  int32_t *__restrict__ n_active,
+                                                                  int32_t *__restrict__ dev_error) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ int32_t wave_sum[BK_THREADS / 64][2];
+  __shared__ int32_t err;
+  const int tid = threadIdx.x, kps = k + S;
+  const int e_mine = tid < M * kps ? slot_expert(ids, tid, k, kps, E) : -2;
+  bucket_small_body(e_mine, M, kps, E + S, offsets, perm, active, n_active, dev_error, smem, wave_sum, &err);
+}
+
+// ------------------------------------------------------------------ top-k + bucket
+// A few rows (M <= 4, k + S <= 64): one workgroup of M waves; wave m ranks
+// row m (topk_row: the top-k kernel's arithmetic), the ids go to LDS, and
+// then every thread takes slot `tid` (T = M (k+S) <= 64 M) and the workgroup
+// buckets them (bucket_small_body).  Same results as topk_kernel followed by
+// bucket_small_kernel, in one launch.  Dynamic LDS: the ranking lists of the
+// M waves, then (reused) the bucket's masks and counts.  Measured on MI355X
+// at the Kimi shape: the 1- and 2-row layers gain about 1 us; at 16 rows the
+// 16 rankings on one CU take longer than the separate top-k kernel's 4 CUs
+// and the layer loses 5 us, hence the limit.
+constexpr int TB_MAX_ROWS = 4;
+
+template <int NPL>
+__global__ __launch_bounds__(TB_MAX_ROWS * 64) void topk_bucket_kernel(
+    const float *__restrict__ logits, int M, int E, int k, int S, int32_t *__restrict__ ids, float *__restrict__ w,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ perm, int32_t *__restrict__ active,
+    int32_t *__restrict__ n_active, int32_t *__restrict__ dev_error) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ int32_t wave_sum[TB_MAX_ROWS][2];
+  __shared__ int32_t err;
+  __shared__ int32_t sids[TB_MAX_ROWS * 64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int32_t id;
+  float wt;
+  topk_row<NPL>(logits + (int64_t)wv * E, E, k, (uint64_t(*)[64])(smem + (size_t)wv * topk_wave_lds(NPL)), lane, id,
+                wt);
+  if (lane < k) {
+    ids[(int64_t)wv * k + lane] = id;
+    w[(int64_t)wv * k + lane] = wt;
+    sids[wv * k + lane] = id;
+  }
+  __syncthreads();  // the ids are in LDS and every wave is done with its lists
+  const int kps = k + S;
+  int e_mine = -2;
+  if (tid < M * kps) {
+    const int m = tid / kps, j = tid - m * kps;
+    if (j >= k) {
+      e_mine = E + (j - k);
+    } else {
+      const int e = sids[m * k + j];
+      e_mine = (e >= 0 && e < E) ? e : -1;
+    }
+  }
+  bucket_small_body(e_mine, M, kps, E + S, offsets, perm, active, n_active, dev_error, smem, wave_sum, &err);
+}
+
+template <int NPL>
+static int launch_topk_bucket(const float *logits, int M, int E, int k, int S, int32_t *ids, float *w,
+                              int32_t *offsets, int32_t *perm, int32_t *active, int32_t *n_active,
+                              int32_t *dev_error, size_t smem, hipStream_t stream) {
+  static const bool lds_ok =
+      hipFuncSetAttribute(reinterpret_cast<const void *>(&topk_bucket_kernel<NPL>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kTbMaxLds) == hipSuccess;
+  if (!lds_ok) {
+    (void)hipGetLastError();  // leave no error behind for the next launch check
+    return -3;
+  }
+  hipLaunchKernelGGL(topk_bucket_kernel<NPL>, dim3(1), dim3(M * 64), smem, stream, logits, M, E, k, S, ids, w,
+                     offsets, perm, active, n_active, dev_error);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
 int bucket_launch(const int32_t *ids, int M, int k, int E, int S, int32_t *offsets, int32_t *perm, int32_t *active,
@@ -207,6 +283,26 @@ int bucket_launch(const int32_t *ids, int M, int k, int E, int S, int32_t *offse
     hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(BK_THREADS), smem, stream, ids, M, k, E, S, offsets, perm, active,
                        n_active, dev_error);
   return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+int route_bucket_launch(const void *x, int x_bf16, const float *w_router, float *logits, int M, int d, int E, int k,
+                        int S, int32_t *ids, float *w, int32_t *offsets, int32_t *perm, int32_t *active,
+                        int32_t *n_active, int32_t *dev_error, hipStream_t stream) {
+  if (w_router && logits_launch(x, x_bf16, w_router, logits, M, d, E, stream)) return -3;
+  const int npl = (E + 63) / 64;
+  const size_t lists = (size_t)M * topk_wave_lds(npl), bk = (size_t)(E + S) * (sizeof(unsigned long long) + 4);
+  const size_t smem = lists > bk ? lists : bk;
+  if (M <= TB_MAX_ROWS && k <= 64 && k + S <= 64 && smem <= (size_t)kTbMaxLds) {
+    if (npl <= 1) return launch_topk_bucket<1>(logits, M, E, k, S, ids, w, offsets, perm, active, n_active, dev_error, smem, stream);
+    if (npl <= 2) return launch_topk_bucket<2>(logits, M, E, k, S, ids, w, offsets, perm, active, n_active, dev_error, smem, stream);
+    if (npl <= 4) return launch_topk_bucket<4>(logits, M, E, k, S, ids, w, offsets, perm, active, n_active, dev_error, smem, stream);
+    if (npl <= 8) return launch_topk_bucket<8>(logits, M, E, k, S, ids, w, offsets, perm, active, n_active, dev_error, smem, stream);
+    if (npl <= 14) return launch_topk_bucket<14>(logits, M, E, k, S, ids, w, offsets, perm, active, n_active, dev_error, smem, stream);
+    if (npl <= 16) return launch_topk_bucket<16>(logits, M, E, k, S, ids, w, offsets, perm, active, n_active, dev_error, smem, stream);
+    if (npl <= 32) return launch_topk_bucket<32>(logits, M, E, k, S, ids, w, offsets, perm, active, n_active, dev_error, smem, stream);
+  }
+  if (topk_launch(logits, M, E, k, ids, w, stream)) return -3;
+  return bucket_launch(ids, M, k, E, S, offsets, perm, active, n_active, dev_error, stream);
 }
 
 // ------------------------------------------------------------------ combine

@@ -175,8 +175,9 @@ int moe_layer_streamed(moe_expert_cache *cache, int32_t layer, const void *x, mo
 
   const hipStream_t st = as_stream(stream);
   const int bf = x_dtype == MOE_BF16;
-  if (moe::route_launch(x, bf, w_router, logits, M, cf.d, E, k, topk_ids, topk_w, st)) return MOE_EHIP;
-  if (moe::bucket_launch(topk_ids, M, k, E, S, offsets, perm, active, n_active, dev_error, st)) return MOE_EHIP;
+  if (moe::route_bucket_launch(x, bf, w_router, logits, M, cf.d, E, k, S, topk_ids, topk_w, offsets, perm, active,
+                                n_active, dev_error, st))
+    return MOE_EHIP;
   int32_t *h_off = c.h_route, *h_act = c.h_route + NE + 1, *h_na = c.h_route + 2 * NE + 1;
   if (hipMemcpyAsync(h_off, offsets, sizeof(int32_t) * (NE + 1), hipMemcpyDeviceToHost, st) != hipSuccess ||
       hipMemcpyAsync(h_act, active, sizeof(int32_t) * NE, hipMemcpyDeviceToHost, st) != hipSuccess ||

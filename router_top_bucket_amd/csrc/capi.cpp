@@ -190,8 +190,9 @@ int moe_layer_mxfp4(const void *x, moe_dtype x_dtype, const float *w_router, flo
   const int E = W->n_routed, S = W->n_shared, d = W->d;
   const hipStream_t st = as_stream(stream);
   const int bf = x_dtype == MOE_BF16;
-  if (moe::route_launch(x, bf, w_router, logits, M, d, E, k, topk_ids, topk_w, st)) return MOE_EHIP;
-  if (moe::bucket_launch(topk_ids, M, k, E, S, offsets, perm, active, n_active, dev_error, st)) return MOE_EHIP;
+  if (moe::route_bucket_launch(x, bf, w_router, logits, M, d, E, k, S, topk_ids, topk_w, offsets, perm, active,
+                                n_active, dev_error, st))
+    return MOE_EHIP;
   if (run_ffn(x, x_dtype, M, k, W, offsets, perm, active, n_active, y_slots, workspace,
               moe::kStageGateUp | moe::kStageDown, stream) != MOE_OK)
     return MOE_EHIP;

@@ -9,9 +9,18 @@ namespace moe {
 
 int route_launch(const void *x, int x_bf16, const float *w_router, float *logits, int M, int d, int E, int k,
                  int32_t *ids, float *w, hipStream_t stream);
+// the two halves of route_launch: router logits, then top-k + weights
+int logits_launch(const void *x, int x_bf16, const float *w_router, float *logits, int M, int d, int E,
+                  hipStream_t stream);
+int topk_launch(const float *logits, int M, int E, int k, int32_t *ids, float *w, hipStream_t stream);
 
 int bucket_launch(const int32_t *ids, int M, int k, int E, int S, int32_t *offsets, int32_t *perm, int32_t *active,
                   int32_t *n_active, int32_t *dev_error, hipStream_t stream);
+// route_launch followed by bucket_launch, with the same results; for up to
+// 4 rows the top-k and the bucketing run as one kernel.
+int route_bucket_launch(const void *x, int x_bf16, const float *w_router, float *logits, int M, int d, int E, int k,
+                        int S, int32_t *ids, float *w, int32_t *offsets, int32_t *perm, int32_t *active,
+                        int32_t *n_active, int32_t *dev_error, hipStream_t stream);
 
 int64_t ffn_max_groups(int64_t M, int k, int S, int n_experts);
 size_t ffn_workspace_bytes(int64_t M, int k, int S, int d, int f, int n_experts);

@@ -3,6 +3,7 @@
 // Kimi 3.1 locally on one GPU": the router picks 16 of 896 experts per token).
 #include "common.h"
 #include "launch.h"
+#include "topk.h"
 
 #include <type_traits>
 
@@ -105,126 +106,24 @@ __global__ __launch_bounds__(LG_THREADS) void router_logits_kernel(const void *_
 }
 
 // ------------------------------------------------------------------ top-k
-// One wave per row, the row's logits in registers (NPL per lane).  Each entry
-// becomes a 64-bit key: high word = the logit's bits mapped to an unsigned
-// order (NaN as -inf, -0 as +0), low word = ~index, so a larger key is a
-// larger logit or, on equal logits, a lower index.  k rounds take the wave
-// maximum (a total order: every lane agrees) and retire it.
+// One wave per row (topk_row), TK_WAVES rows per workgroup.
 constexpr int TK_WAVES = 4;
 
-__device__ __forceinline__ uint32_t order_bits(float v) {
-  if (v != v) v = -INFINITY;
-  if (v == 0.0f) v = 0.0f;
-  const uint32_t b = __float_as_uint(v);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-__device__ __forceinline__ float from_order_bits(uint32_t o) {
-  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
-}
-
-// Batcher's odd-even merge sort of N keys in registers, largest first
-// (compile-time network; every index is a constant).
-__device__ __forceinline__ void cmpx_desc(uint64_t &a, uint64_t &b) {
-  const uint64_t hi = max_u64(a, b), lo = a ^ b ^ hi;
-  a = hi;
-  b = lo;
-}
-template <int LO, int HI, int R>  // merge the sorted halves of a[LO..HI] (inclusive), stride R
-__device__ __forceinline__ void oem_merge(uint64_t *a) {
-  constexpr int STEP = R * 2;
-  if constexpr (STEP < HI - LO) {
-    oem_merge<LO, HI, STEP>(a);
-    oem_merge<LO + R, HI, STEP>(a);
-#pragma unroll
-    for (int i = LO + R; i < HI - R; i += STEP) cmpx_desc(a[i], a[i + R]);
-  } else {
-    cmpx_desc(a[LO], a[LO + R]);
-  }
-}
-template <int LO, int HI>  // sort a[LO..HI] (inclusive)
-__device__ __forceinline__ void oem_sort(uint64_t *a) {
-  if constexpr (HI - LO >= 1) {
-    constexpr int MID = LO + (HI - LO) / 2;
-    oem_sort<LO, MID>(a);
-    oem_sort<MID + 1, HI>(a);
-    oem_merge<LO, HI, 1>(a);
-  }
-}
-
-// Maximum of a 32-bit value over the wave (uniform result): DPP inside each
-// 16-lane row, then the four row results.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-  v = max(v, dpp_u32<MOE_DPP_QUAD_1032>(v));
-  v = max(v, dpp_u32<MOE_DPP_QUAD_2301>(v));
-  v = max(v, dpp_u32<MOE_DPP_ROW_HALF_MIRROR>(v));
-  v = max(v, dpp_u32<MOE_DPP_ROW_MIRROR>(v));
-  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
-  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
-  return max(max(r0, r1), max(r2, r3));
-}
-
-// One wave per row.  Lane l sorts the keys of entries l, l+64, ... largest
-// first (P = NPL rounded up to a power of two, padded with key 0, which is
-// below every real key) and parks the sorted list in LDS, keeping only its
-// head in registers.  Each round takes the largest head over the wave; the
-// owning lane (keys are distinct: the index is part of the key) reads its
-// next key, and the lane of rank j keeps the round's logit and id.
 template <int NPL>
 __global__ __launch_bounds__(TK_WAVES * 64) void topk_kernel(const float *__restrict__ logits, int M, int E, int k,
                                                              int32_t *__restrict__ ids, float *__restrict__ w) {
-  constexpr int P = NPL <= 1 ? 1 : NPL <= 2 ? 2 : NPL <= 4 ? 4 : NPL <= 8 ? 8 : NPL <= 16 ? 16 : NPL <= 32 ? 32 : 64;
+  constexpr int P = topk_list_len(NPL);
   __shared__ uint64_t lists[TK_WAVES][P + 1][64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int m = blockIdx.x * TK_WAVES + wv;
   if (m >= M) return;  // whole wave; the LDS lists are per wave, no barrier
-  const float *row = logits + (int64_t)m * E;
-  // all loads first, from a clamped (always valid) index, so none waits on
-  // another; entries past E then become key 0
-  float v[NPL];
-#pragma unroll
-  for (int i = 0; i < NPL; ++i) v[i] = row[min(lane + 64 * i, E - 1)];
-  uint64_t key[P];
-#pragma unroll
-  for (int i = 0; i < P; ++i) {
-    const int e = lane + 64 * i;
-    key[i] = (i < NPL && e < E) ? (((uint64_t)order_bits(v[i < NPL ? i : 0]) << 32) | (uint32_t)~(uint32_t)e) : 0ull;
+  int32_t id;
+  float wt;
+  topk_row<NPL>(logits + (int64_t)m * E, E, k, lists[wv], lane, id, wt);
+  if (lane < k) {
+    ids[(int64_t)m * k + lane] = id;
+    w[(int64_t)m * k + lane] = wt;
   }
-  oem_sort<0, P - 1>(key);
-  uint64_t(*mine)[64] = lists[wv];
-#pragma unroll
-  for (int i = 1; i < P; ++i) mine[i][lane] = key[i];
-  mine[P][lane] = 0ull;  // past the end of every list
-  uint64_t head = key[0];
-  int pos = 0;  // index of head in this lane's list
-  float my_l = 0.f;  // lane j keeps the logit and id of rank j
-  int32_t my_id = 0;
-  for (int j = 0; j < k; ++j) {
-    const uint32_t hi = (uint32_t)(head >> 32), lo = (uint32_t)head;
-    const uint32_t hmax = wave_max_u32(hi);
-    uint64_t cand = __ballot(hi == hmax);
-    uint32_t lmax;
-    if (__popcll(cand) == 1) {
-      lmax = (uint32_t)__builtin_amdgcn_readlane((int)lo, __ffsll((unsigned long long)cand) - 1);
-    } else {  // equal logits: the lower index (larger ~index) first
-      lmax = wave_max_u32(hi == hmax ? lo : 0u);
-      cand = __ballot(hi == hmax && lo == lmax);
-    }
-    if (lane == __ffsll((unsigned long long)cand) - 1) {
-      pos = pos < P ? pos + 1 : P;
-      head = mine[pos][lane];
-    }
-    if (lane == j) {
-      my_l = from_order_bits(hmax);
-      my_id = (int32_t)~lmax;
-    }
-  }
-  if (lane < k) ids[(int64_t)m * k + lane] = my_id;
-  // weights: exp(l_j - l_0) / sum_{i<k} exp(l_i - l_0), summed in rank order
-  const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_l), 0));
-  const float ej = (lane < k) ? expf(my_l - l0) : 0.f;
-  float z = 0.f;
-  for (int i = 0; i < k; ++i) z += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ej), i));
-  if (lane < k) w[(int64_t)m * k + lane] = ej / z;
 }
 
 // ------------------------------------------------------------------ host
@@ -252,13 +151,14 @@ static void launch_logits(const void *x, const float *w_router, float *logits, i
                        w_router, M, d, E, logits);
 }
 
-int route_launch(const void *x, int x_bf16, const float *w_router, float *logits, int M, int d, int E, int k,
-                 int32_t *ids, float *w, hipStream_t stream) {
-  if (w_router) {
-    if (x_bf16) launch_logits<1>(x, w_router, logits, M, d, E, stream);
-    else launch_logits<0>(x, w_router, logits, M, d, E, stream);
-    if (hipGetLastError() != hipSuccess) return -3;
-  }
+int logits_launch(const void *x, int x_bf16, const float *w_router, float *logits, int M, int d, int E,
+                  hipStream_t stream) {
+  if (x_bf16) launch_logits<1>(x, w_router, logits, M, d, E, stream);
+  else launch_logits<0>(x, w_router, logits, M, d, E, stream);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+int topk_launch(const float *logits, int M, int E, int k, int32_t *ids, float *w, hipStream_t stream) {
   const int npl = (E + 63) / 64;
   if (npl <= 1) launch_topk<1>(logits, M, E, k, ids, w, stream);
   else if (npl <= 2) launch_topk<2>(logits, M, E, k, ids, w, stream);
@@ -268,8 +168,13 @@ int route_launch(const void *x, int x_bf16, const float *w_router, float *logits
   else if (npl <= 16) launch_topk<16>(logits, M, E, k, ids, w, stream);
   else if (npl <= 32) launch_topk<32>(logits, M, E, k, ids, w, stream);
   else launch_topk<64>(logits, M, E, k, ids, w, stream);
-  if (hipGetLastError() != hipSuccess) return -3;
-  return 0;
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+int route_launch(const void *x, int x_bf16, const float *w_router, float *logits, int M, int d, int E, int k,
+                 int32_t *ids, float *w, hipStream_t stream) {
+  if (w_router && logits_launch(x, x_bf16, w_router, logits, M, d, E, stream)) return -3;
+  return topk_launch(logits, M, E, k, ids, w, stream);
 }
 
 }  // namespace moe

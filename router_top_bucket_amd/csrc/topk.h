@@ -1,0 +1,134 @@
+// Top-k of one row of router logits in one wave, with the renormalised
+// softmax weights of the selected experts ("Read the experts the router
+// needs", "Run Kimi 3.1 locally on one GPU": the router picks 16 of 896
+// experts per token).  Shared by the top-k kernel and the fused
+// top-k + bucket kernel, so both give the same bits.
+//
+// The row's logits sit in registers (NPL per lane).  Each entry becomes a
+// 64-bit key: high word = the logit's bits mapped to an unsigned order (NaN
+// as -inf, -0 as +0), low word = ~index, so a larger key is a larger logit or,
+// on equal logits, a lower index.  k rounds take the wave maximum (a total
+// order: every lane agrees) and retire it.
+#pragma once
+#include "common.h"
+
+namespace moe {
+
+__device__ __forceinline__ uint32_t order_bits(float v) {
+  if (v != v) v = -INFINITY;
+  if (v == 0.0f) v = 0.0f;
+  const uint32_t b = __float_as_uint(v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float from_order_bits(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+// Batcher's odd-even merge sort of N keys in registers, largest first
+// (compile-time network; every index is a constant).
+__device__ __forceinline__ void cmpx_desc(uint64_t &a, uint64_t &b) {
+  const uint64_t hi = max_u64(a, b), lo = a ^ b ^ hi;
+  a = hi;
+  b = lo;
+}
+template <int LO, int HI, int R>  // merge the sorted halves of a[LO..HI] (inclusive), stride R
+__device__ __forceinline__ void oem_merge(uint64_t *a) {
+  constexpr int STEP = R * 2;
+  if constexpr (STEP < HI - LO) {
+    oem_merge<LO, HI, STEP>(a);
+    oem_merge<LO + R, HI, STEP>(a);
+#pragma unroll
+    for (int i = LO + R; i < HI - R; i += STEP) cmpx_desc(a[i], a[i + R]);
+  } else {
+    cmpx_desc(a[LO], a[LO + R]);
+  }
+}
+template <int LO, int HI>  // sort a[LO..HI] (inclusive)
+__device__ __forceinline__ void oem_sort(uint64_t *a) {
+  if constexpr (HI - LO >= 1) {
+    constexpr int MID = LO + (HI - LO) / 2;
+    oem_sort<LO, MID>(a);
+    oem_sort<MID + 1, HI>(a);
+    oem_merge<LO, HI, 1>(a);
+  }
+}
+
+// Maximum of a 32-bit value over the wave (uniform result): DPP inside each
+// 16-lane row, then the four row results.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<MOE_DPP_QUAD_1032>(v));
+  v = max(v, dpp_u32<MOE_DPP_QUAD_2301>(v));
+  v = max(v, dpp_u32<MOE_DPP_ROW_HALF_MIRROR>(v));
+  v = max(v, dpp_u32<MOE_DPP_ROW_MIRROR>(v));
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
+// Keys per lane list: NPL rounded up to a power of two.
+__host__ __device__ constexpr int topk_list_len(int npl) {
+  return npl <= 1 ? 1 : npl <= 2 ? 2 : npl <= 4 ? 4 : npl <= 8 ? 8 : npl <= 16 ? 16 : npl <= 32 ? 32 : 64;
+}
+// LDS of one ranking wave: (P + 1) x 64 keys.
+__host__ __device__ constexpr size_t topk_wave_lds(int npl) { return (size_t)(topk_list_len(npl) + 1) * 64 * 8; }
+
+// Ranks row `row` (E logits) in the calling wave.  Lane l sorts the keys of
+// entries l, l+64, ... largest first (P = topk_list_len(NPL), padded with key
+// 0, which is below every real key) and parks the sorted list in `lists`
+// (this wave's [P + 1][64] keys), keeping only its head in registers.  Each
+// round takes the largest head over the wave; the owning lane (keys are
+// distinct: the index is part of the key) reads its next key.  Lane j < k
+// gets the expert of rank j and its weight exp(l_j - l_0) / sum_{i<k}
+// exp(l_i - l_0), the normaliser summed in rank order.
+template <int NPL>
+__device__ __forceinline__ void topk_row(const float *__restrict__ row, int E, int k, uint64_t (*lists)[64], int lane,
+                                         int32_t &id_out, float &w_out) {
+  constexpr int P = topk_list_len(NPL);
+  // all loads first, from a clamped (always valid) index, so none waits on
+  // another; entries past E then become key 0
+  float v[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) v[i] = row[min(lane + 64 * i, E - 1)];
+  uint64_t key[P];
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = (i < NPL && e < E) ? (((uint64_t)order_bits(v[i < NPL ? i : 0]) << 32) | (uint32_t)~(uint32_t)e) : 0ull;
+  }
+  oem_sort<0, P - 1>(key);
+#pragma unroll
+  for (int i = 1; i < P; ++i) lists[i][lane] = key[i];
+  lists[P][lane] = 0ull;  // past the end of every list
+  uint64_t head = key[0];
+  int pos = 0;  // index of head in this lane's list
+  float my_l = 0.f;  // lane j keeps the logit and id of rank j
+  int32_t my_id = 0;
+  for (int j = 0; j < k; ++j) {
+    const uint32_t hi = (uint32_t)(head >> 32), lo = (uint32_t)head;
+    const uint32_t hmax = wave_max_u32(hi);
+    uint64_t cand = __ballot(hi == hmax);
+    uint32_t lmax;
+    if (__popcll(cand) == 1) {
+      lmax = (uint32_t)__builtin_amdgcn_readlane((int)lo, __ffsll((unsigned long long)cand) - 1);
+    } else {  // equal logits: the lower index (larger ~index) first
+      lmax = wave_max_u32(hi == hmax ? lo : 0u);
+      cand = __ballot(hi == hmax && lo == lmax);
+    }
+    if (lane == __ffsll((unsigned long long)cand) - 1) {
+      pos = pos < P ? pos + 1 : P;
+      head = lists[pos][lane];
+    }
+    if (lane == j) {
+      my_l = from_order_bits(hmax);
+      my_id = (int32_t)~lmax;
+    }
+  }
+  const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_l), 0));
+  const float ej = (lane < k) ? expf(my_l - l0) : 0.f;
+  float z = 0.f;
+  for (int i = 0; i < k; ++i) z += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ej), i));
+  id_out = my_id;
+  w_out = ej / z;
+}
+
+}  // namespace moe

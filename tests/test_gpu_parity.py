@@ -174,6 +174,49 @@ def test_bucket_flags_bad_ids_in_bounds():
     assert err == 0  # the flag is cleared by a clean call
 
 
+ROUTE_SHAPES = [
+    synth.LayerShape("e896", 64, 32, 896, 2, 16, -6, -2, 0.05, "bf16"),
+    synth.LayerShape("e16", 64, 32, 16, 0, 2, -6, -2, 0.05, "f32"),
+    synth.LayerShape("e64k64", 64, 32, 64, 0, 64, -6, -2, 0.05, "f32"),
+    synth.LayerShape("e100s3", 64, 32, 100, 3, 1, -6, -2, 0.05, "bf16"),
+    synth.LayerShape("e2000", 64, 32, 2000, 1, 8, -6, -2, 0.05, "bf16"),
+]
+
+
+@pytest.mark.parametrize("shape", ROUTE_SHAPES, ids=lambda s: s.name)
+def test_layer_routing_exact_adversarial_logits(shape):
+    """The layer call routes and buckets (for a few rows: one top-k + bucket
+    kernel) exactly as the oracle and as moe_route + moe_bucket do, on given
+    logits with ties, NaN and an all-equal row."""
+    moe = _moe()
+    ex, _ = _small_layer(shape, 51)
+    E, S, k = shape.n_routed, shape.n_shared, shape.k
+    for M in (1, 2, 4, 5, 16):
+        lg = synth.random_logits(E + M, M, E)
+        lg[::2] = np.round(lg[::2] * 2) / 2
+        lg[:, ::11] = np.nan
+        lg[-1] = 0.5
+        ids_ref, w_ref = oracle.topk(lg, k)
+        r_off, r_perm, r_act, r_na = oracle.bucket(ids_ref, E, S)
+        x = synth.rows_x(shape, 52 + M, M)
+        layer = moe.MoELayer(ex, k, M)
+        layer.dev_error.fill_(-7)
+        layer.offsets.fill_(-7)
+        layer.perm.fill_(-7)
+        res = layer.forward(_x_dev(shape, x), logits=_dev(lg))
+        got = _layer_outputs(res, M, k, S)
+        what = (shape.name, M)
+        assert np.array_equal(got["ids"], ids_ref), what
+        assert np.array_equal(got["offsets"], r_off) and np.array_equal(got["perm"], r_perm), what
+        assert got["n_active"][0] == r_na and np.array_equal(got["active"], r_act), what
+        assert int(got["dev_error"][0]) == 0, what
+        assert_close(got["w"], w_ref, f"routing weights {what}")
+        ids2 = torch.empty((M, k), dtype=torch.int32, device="cuda")
+        w2 = torch.empty((M, k), dtype=torch.float32, device="cuda")
+        moe.moe_route(None, None, _dev(lg), k, ids2, w2)
+        assert np.array_equal(_host(w2).view(np.uint8), got["w"].view(np.uint8)), what
+
+
 # ----------------------------------------------------------------------------- combine
 @pytest.mark.parametrize("M,k,S,d", [(1, 16, 2, 7168), (16, 16, 2, 7168), (5, 2, 0, 256), (3, 4, 3, 8)])
 def test_combine_parity(M, k, S, d):
