@@ -351,7 +351,9 @@ def main():
         routes = []
         for i in range(P):
             v = fwd(i)
-            routes.append({k: v[k].clone() for k in ("offsets", "perm", "active", "n_active")})
+            # the copies go on the layer's stream, after the pass that writes them
+            with torch.cuda.stream(stream):
+                routes.append({k: v[k].clone() for k in ("offsets", "perm", "active", "n_active")})
         stream.synchronize()
         na = np.array([int(r["n_active"].item()) for r in routes], dtype=np.float64)
 
@@ -437,6 +439,7 @@ def main():
             # copies at distinct addresses so the rotation spans >= 1 GB
             ncopy = max(2, -(-(1 << 30) // dwq.numel()))
             copies = [(dwq, dws)] + [(dwq.clone(), dws.clone()) for _ in range(ncopy - 1)]
+            torch.cuda.synchronize()  # the copies are made on torch's stream, read on `stream`
             for Mq in (1, 2, 4, 8):
                 X = torch.from_numpy(synth.q8_0_x(3, Mq, K)).to(dev)
                 Y = torch.empty((Mq, N), dtype=torch.float32, device=dev)

@@ -1148,6 +1148,11 @@ int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *exper
       off += align_up((size_t)cap[c] * sizeof(int4), 256);
     }
     if (!wide) cap[1] = cap[2] = 0;
+    // grids (not list capacities): with wide groups every active expert has
+    // at most one narrow group (itself, or the remainder of its 64s), so the
+    // narrow kernels need not launch ceil(T/16) + E groups' workgroups, most
+    // of which would find no group
+    if (wide) cap[0] = std::min<int64_t>(cap[0], std::min<int64_t>(n_experts, T));
   }
   int32_t *n_groups = (int32_t *)(ws + off);
 
