@@ -239,10 +239,39 @@ __global__ __launch_bounds__(TB_MAX_ROWS * 64) void topk_bucket_kernel(
   if (lane < k) {
     ids[(int64_t)wv * k + lane] = id;
     w[(int64_t)wv * k + lane] = wt;
-    sids[wv * k + lane] = id;
   }
+  const int kps = k + S, NE = E + S;
+  // One row (the workgroup is one wave): its k routed and S shared experts
+  // are distinct, so lane t's slot has rank = the number of experts below
+  // its own, and offsets[e] = the number of experts below e.  Lane l writes
+  // offsets[l*C .. l*C+C) from that count at l*C and a mask of the experts
+  // inside its range.  Same results as the general path below.
+  if (M == 1 && NE + 1 <= 64 * 64 && __ballot(lane < k && (id < 0 || id >= E)) == 0ull) {
+    const int e_t = lane < k ? id : (lane < kps ? E + (lane - k) : 0x7FFFFFFF);
+    const int C = (NE + 1 + 63) >> 6, e0 = lane * C;
+    int rank = 0, below = 0;
+    uint64_t inside = 0ull;
+    for (int u = 0; u < kps; ++u) {
+      const int eu = __builtin_amdgcn_readlane(e_t, u);
+      rank += eu < e_t;
+      below += eu < e0;
+      const int rel = eu - e0;
+      if (rel >= 0 && rel < C) inside |= 1ull << rel;
+    }
+    if (lane < kps) {
+      perm[rank] = lane;
+      active[rank] = e_t;
+    }
+    for (int i = 0; i < C; ++i)
+      if (e0 + i <= NE) offsets[e0 + i] = below + __popcll(inside & ((1ull << i) - 1ull));
+    if (lane == 0) {
+      *n_active = kps;
+      *dev_error = 0;
+    }
+    return;
+  }
+  if (lane < k) sids[wv * k + lane] = id;
   __syncthreads();  // the ids are in LDS and every wave is done with its lists
-  const int kps = k + S;
   int e_mine = -2;
   if (tid < M * kps) {
     const int m = tid / kps, j = tid - m * kps;
@@ -253,7 +282,7 @@ __global__ __launch_bounds__(TB_MAX_ROWS * 64) void topk_bucket_kernel(
       e_mine = (e >= 0 && e < E) ? e : -1;
     }
   }
-  bucket_small_body(e_mine, M, kps, E + S, offsets, perm, active, n_active, dev_error, smem, wave_sum, &err);
+  bucket_small_body(e_mine, M, kps, NE, offsets, perm, active, n_active, dev_error, smem, wave_sum, &err);
 }
 
 template <int NPL>

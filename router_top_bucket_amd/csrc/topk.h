@@ -75,9 +75,9 @@ __host__ __device__ constexpr size_t topk_wave_lds(int npl) { return (size_t)(to
 // Ranks row `row` (E logits) in the calling wave.  Lane l sorts the keys of
 // entries l, l+64, ... largest first (P = topk_list_len(NPL), padded with key
 // 0, which is below every real key) and parks the sorted list in `lists`
-// (this wave's [P + 1][64] keys), keeping only its head in registers.  Each
-// round takes the largest head over the wave; the owning lane (keys are
-// distinct: the index is part of the key) reads its next key.  Lane j < k
+// (this wave's [P + 1][64] keys), keeping its first two keys in registers.
+// Each round takes the largest head over the wave; the owning lane (keys are
+// distinct: the index is part of the key) moves on to its next key.  Lane j < k
 // gets the expert of rank j and its weight exp(l_j - l_0) / sum_{i<k}
 // exp(l_i - l_0), the normaliser summed in rank order.
 template <int NPL>
@@ -97,10 +97,13 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ row, int E, i
   }
   oem_sort<0, P - 1>(key);
 #pragma unroll
-  for (int i = 1; i < P; ++i) lists[i][lane] = key[i];
+  for (int i = 2; i < P; ++i) lists[i][lane] = key[i];
   lists[P][lane] = 0ull;  // past the end of every list
-  uint64_t head = key[0];
-  int pos = 0;  // index of head in this lane's list
+  // the head and the key after it stay in registers: a lane that wins a
+  // round promotes its next key and starts the LDS read of the one after,
+  // which is needed a round later at the earliest
+  uint64_t head = key[0], nxt = P > 1 ? key[P > 1 ? 1 : 0] : 0ull;
+  int pos = P > 1 ? 1 : P;  // index of nxt in this lane's list
   float my_l = 0.f;  // lane j keeps the logit and id of rank j
   int32_t my_id = 0;
   for (int j = 0; j < k; ++j) {
@@ -115,8 +118,9 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ row, int E, i
       cand = __ballot(hi == hmax && lo == lmax);
     }
     if (lane == __ffsll((unsigned long long)cand) - 1) {
+      head = nxt;
       pos = pos < P ? pos + 1 : P;
-      head = lists[pos][lane];
+      nxt = lists[pos][lane];
     }
     if (lane == j) {
       my_l = from_order_bits(hmax);

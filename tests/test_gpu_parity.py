@@ -180,6 +180,8 @@ ROUTE_SHAPES = [
     synth.LayerShape("e64k64", 64, 32, 64, 0, 64, -6, -2, 0.05, "f32"),
     synth.LayerShape("e100s3", 64, 32, 100, 3, 1, -6, -2, 0.05, "bf16"),
     synth.LayerShape("e2000", 64, 32, 2000, 1, 8, -6, -2, 0.05, "bf16"),
+    synth.LayerShape("e4000s40", 64, 32, 4000, 40, 16, -6, -2, 0.05, "bf16"),
+    synth.LayerShape("e4090s6", 64, 32, 4090, 6, 8, -6, -2, 0.05, "f32"),
 ]
 
 
