@@ -337,11 +337,12 @@ int route_bucket_launch(const void *x, int x_bf16, const float *w_router, float 
 // ------------------------------------------------------------------ combine
 // out[m,r] = sum_{j<k} w[m,j] y[m*(k+S)+j, r] + sum_{s<S} y[m*(k+S)+k+s, r],
 // fp32, in slot order.  One thread per 4 consecutive r; the slot rows are
-// loaded CH at a time before their (ordered) accumulation.
+// loaded CH at a time before their (ordered) accumulation, CH chosen so that
+// k + S slots take one round of loads where it fits (18 at the Kimi shape).
 constexpr int CB_THREADS = 64;
+template <int CH>
 __global__ __launch_bounds__(CB_THREADS) void combine_kernel(const float *__restrict__ y, const float *__restrict__ w,
                                                              int M, int k, int S, int d, float *__restrict__ out) {
-  constexpr int CH = 9;
   const int d4 = d >> 2;
   const int64_t idx = (int64_t)blockIdx.x * CB_THREADS + threadIdx.x;
   if (idx >= (int64_t)M * d4) return;
@@ -378,7 +379,13 @@ __global__ __launch_bounds__(CB_THREADS) void combine_kernel(const float *__rest
 int combine_launch(const float *y, const float *w, int M, int k, int S, int d, float *out, hipStream_t stream) {
   const int64_t n = (int64_t)M * (d / 4);
   const int64_t grid = (n + CB_THREADS - 1) / CB_THREADS;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)grid), dim3(CB_THREADS), 0, stream, y, w, M, k, S, d, out);
+  const int kps = k + S;
+  if (kps <= 4)
+    hipLaunchKernelGGL(combine_kernel<4>, dim3((unsigned)grid), dim3(CB_THREADS), 0, stream, y, w, M, k, S, d, out);
+  else if (kps <= 9)
+    hipLaunchKernelGGL(combine_kernel<9>, dim3((unsigned)grid), dim3(CB_THREADS), 0, stream, y, w, M, k, S, d, out);
+  else
+    hipLaunchKernelGGL(combine_kernel<18>, dim3((unsigned)grid), dim3(CB_THREADS), 0, stream, y, w, M, k, S, d, out);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
