@@ -1193,7 +1193,8 @@ int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *exper
   // W_gate, half W_up) with a 4-step ring beyond, and the wide kernel (8
   // waves x 32 rows) for the 32- and 64-slot groups; down 8 waves x 2 tiles
   // (256 rows of d) at 1 row, 8 waves x 1 tile at 2-4 rows, 8 waves x 2 tiles
-  // beyond.  A resident B is used only where the LDS it takes still lets two
+  // and a 4-step ring up to 16 rows, and for the narrow groups of more rows
+  // 8 waves x 4 tiles (512 rows) with a 2-step ring.  A resident B is used only where the LDS it takes still lets two
   // or more workgroups share a CU.
   int rc = 0;
   if (stages & kStageGateUp) {
@@ -1218,7 +1219,8 @@ int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *exper
     const size_t half = (size_t)kMaxLds / 2;
     if (M == 1 && down_lds_bytes(f, 4, 1, true, 256) <= half) rc = MOE_DN(2, 8, 4, 1, true, 0, 1);
     else if (M <= 4 && down_lds_bytes(f, 4, 4, true, 128) <= half) rc = MOE_DN(1, 8, 4, 4, true, 0, 1);
-    else rc = MOE_DN(2, 8, 4, 16, false, 0, 1);
+    else if (M <= kGroupCols) rc = MOE_DN(2, 8, 4, 16, false, 0, 1);
+    else rc = MOE_DN(4, 8, 2, 16, false, 0, 1);
     if (!rc && wide) rc = MOE_DN(4, 8, 4, 32, false, 1, 2);
     if (!rc && wide) rc = MOE_DN(4, 8, 2, 64, false, 2, 2);
   }
