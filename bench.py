@@ -53,7 +53,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-extra", action="store_true", help="skip the 16-row, prefill and Q8_0 results")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-rows", type=int, default=10)
+    p.add_argument("--cpu-sample-rows", type=int, default=25)
     p.add_argument("--only", default="",
                    help="comma list of workloads: decode1,block16,prefill,q8_0,stream,verify (copy = the copy "
                         "kernel that calibrates the HBM counters, run alone)")
