@@ -397,7 +397,7 @@ def test_kimi_block_rows_equal_single_rows(kimi_layer, B):
     shp = L["shape"]
     blk = moe.MoELayer(L["experts"], shp.k, B, w_router=L["wr_dev"])
     one = moe.MoELayer(L["experts"], shp.k, 1, w_router=L["wr_dev"])
-    for seed in range(20 if B == 16 else 6):
+    for seed in range(20):  # 20 seeded blocks per block size
         x = synth.block_x(shp, seed, B)
         xd = _x_dev(shp, x)
         rb = blk.forward(xd)
@@ -409,16 +409,17 @@ def test_kimi_block_rows_equal_single_rows(kimi_layer, B):
                 assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), (B, seed, m, key)
 
 
-def test_kimi_block16_parity(kimi_layer):
+@pytest.mark.parametrize("B,seed", [(16, 0), (8, 3), (2, 5)])
+def test_kimi_block16_parity(kimi_layer, B, seed):
     moe = _moe()
     L = kimi_layer
     shp = L["shape"]
-    x = synth.block_x(shp, 0, 16)
-    layer = moe.MoELayer(L["experts"], shp.k, 16, w_router=L["wr_dev"])
+    x = synth.block_x(shp, seed, B)
+    layer = moe.MoELayer(L["experts"], shp.k, B, w_router=L["wr_dev"])
     res = layer.forward(_x_dev(shp, x))
     ref = oracle.layer(x, shp.k, shp.n_routed, shp.n_shared, shp.d, shp.f, L["rec"], w_r=L["wr"])
-    print(f"block of 16: {ref['n_active'] - shp.n_shared} unique routed experts", flush=True)
-    _compare_layer(res, ref, "kimi block 16", shp.k, shp.n_shared)
+    print(f"block of {B}: {ref['n_active'] - shp.n_shared} unique routed experts", flush=True)
+    _compare_layer(res, ref, f"kimi block {B}", shp.k, shp.n_shared)
 
 
 def test_kimi_expert_order_independence(kimi_layer):
