@@ -58,6 +58,14 @@ __device__ __forceinline__ void split3_bf16(float v, uint32_t &hi, uint32_t &mid
   lo = f32_to_bf16_bits(r2);
 }
 
+// Split a finite fp32 value into two bf16 parts: hi is v to the nearest bf16
+// and lo the remainder (an exact fp32 difference) to the nearest bf16, so
+// |v - hi - lo| <= 2^-18 |v|.
+__device__ __forceinline__ void split2_bf16(float v, uint32_t &hi, uint32_t &lo) {
+  hi = f32_to_bf16_bits(v);
+  lo = f32_to_bf16_bits(v - bf16_bits_to_f32(hi));
+}
+
 __device__ __forceinline__ bf16x8 bits_to_bf16x8(u32x4 v) {
   bf16x8 r;
   __builtin_memcpy(&r, &v, sizeof(r));

@@ -12,9 +12,11 @@
 // column) or on how many there are.
 //
 // Arithmetic: weights are decoded exactly to bf16 (E2M1 x 2^k) with gfx950's
-// scaled FP4 convert; x in bf16 is used as is, fp32 x and the fp32 hidden h
-// are split exactly into three bf16 parts (hi + mid + lo), so every MFMA
-// product is exact and only fp32 accumulation rounds.  Every accumulation
+// scaled FP4 convert; x in bf16 is used as is and fp32 x is split exactly
+// into three bf16 parts (hi + mid + lo), so every gate/up product is exact
+// and only fp32 accumulation rounds.  The fp32 hidden h goes to the down pass
+// as two bf16 parts (split2_bf16: |h - hi - lo| <= 2^-18 |h|), so each of its
+// products is exact on those parts.  Every accumulation
 // walks K in 128-element steps, step by step and within a step in 32-element
 // MFMA slices, in ascending order: the order is fixed by d and f alone, for
 // every launch shape and every M.
@@ -32,6 +34,9 @@
 namespace moe {
 
 constexpr int kGroupCols = 16;
+// bf16 parts of h per slot in the workspace and per slot in the down pass's
+// B operand (MFMA columns)
+constexpr int kHParts = 2;
 
 // ------------------------------------------------------------------ groups
 struct GroupSrc {
@@ -236,19 +241,20 @@ __host__ __device__ __forceinline__ size_t gateup_lds_bytes(int d, int pf, int n
 // main loop is done, then the dummy area.
 __host__ __device__ __forceinline__ size_t down_b_off(int f, int rows) { return lds_align16((size_t)rows * sc_pitch(f)); }
 __host__ __device__ __forceinline__ size_t down_b_bytes(int f, int pf, int maxc, bool bres) {
-  return bres ? (size_t)3 * maxc * bres_row_bytes(f) : (size_t)pf * 3 * maxc * kBRow;
+  return bres ? (size_t)kHParts * maxc * bres_row_bytes(f) : (size_t)pf * kHParts * maxc * kBRow;
 }
 __host__ __device__ __forceinline__ size_t down_y_off(int f, int pf, int maxc, bool bres, int rows) {
   return down_b_off(f, rows);
 }
 // Columns of the epilogue's per-(row, column) sums held at a time: all of
 // them for up to 16 slots (or a resident B), else as many whole 16-slot
-// blocks (48 columns) as the ring slots' bytes hold.
+// blocks (16 kHParts columns) as the ring slots' bytes hold.
 __host__ __device__ constexpr int down_yc(int pf, int maxc, bool bres, int rows) {
-  const int nc = 3 * maxc;
+  constexpr int blk = 16 * kHParts;  // the columns of 16 slots
+  const int nc = kHParts * maxc;
   const int avail = (int)((size_t)pf * nc * kBRow / ((size_t)rows * 4)) - 1;
-  const int yc = avail / 48 * 48;
-  return (bres || nc <= 48) ? nc : (yc < 48 ? 48 : (yc > nc ? nc : yc));
+  const int yc = avail / blk * blk;
+  return (bres || nc <= blk) ? nc : (yc < blk ? blk : (yc > nc ? nc : yc));
 }
 __host__ __device__ __forceinline__ size_t down_dummy_off(int f, int pf, int maxc, bool bres, int rows) {
   const int yc = down_yc(pf, maxc, bres, rows);
@@ -355,8 +361,8 @@ __device__ __forceinline__ float lds_scale(const uint8_t *row, int s, int q) {
 // columns past the group's slots read column 0: an MFMA output column
 // depends only on its own B column, and those columns are never stored.
 //
-// Epilogue: h = silu(g) * u for every slot, split exactly into three bf16
-// parts.
+// Epilogue: h = silu(g) * u for every slot, split into kHParts bf16 parts
+// (split2_bf16).
 //
 // x staging (ring mode): piece i of a step (i < MAXC*16) is column i/16,
 // elements 8*(i%16)..+8 of the step; thread t stages pieces t, t+GW*64, ...
@@ -608,16 +614,15 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
       const int lrow = (rw * TPW + t) * 16 + 4 * q;
       const int row = i0 + lrow;
       if (row < f) {
-        uint32_t hi[4], mi[4], lo[4];
+        uint32_t hi[4], lo[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float gv = acc[t][i], uv = PAIR ? acc[(t + TPW) % NT][i] : ut[(lrow + i) * 17 + r];
-          split3_bf16((gv / (1.0f + expf(-gv))) * uv, hi[i], mi[i], lo[i]);
+          split2_bf16((gv / (1.0f + expf(-gv))) * uv, hi[i], lo[i]);
         }
-        uint16_t *hp = h_ws + (int64_t)(start + r) * 3 * f + row;
+        uint16_t *hp = h_ws + (int64_t)(start + r) * kHParts * f + row;
         *(uint2 *)(hp) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
-        *(uint2 *)(hp + f) = make_uint2(mi[0] | (mi[1] << 16), mi[2] | (mi[3] << 16));
-        *(uint2 *)(hp + 2 * f) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+        *(uint2 *)(hp + f) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
       }
     }
   }
@@ -790,7 +795,7 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_wide_kernel(
     for (int t = 0; t < NT; ++t) sc_cur[t] = sc_nxt[t];
   } while (++j < ngroups);
 
-  // SwiGLU and the exact three-part split of h, as in ffn_gateup_kernel
+  // SwiGLU and the split of h into kHParts parts, as in ffn_gateup_kernel
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     const int col = 16 * cb + r;
@@ -799,16 +804,15 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_wide_kernel(
       for (int t = 0; t < 2; ++t) {
         const int row = i0 + wv * 32 + 16 * t + 4 * q;
         if (row < f) {
-          uint32_t hi[4], mi[4], lo[4];
+          uint32_t hi[4], lo[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float gv = acc[t][cb][i], uv = acc[t + 2][cb][i];
-            split3_bf16((gv / (1.0f + expf(-gv))) * uv, hi[i], mi[i], lo[i]);
+            split2_bf16((gv / (1.0f + expf(-gv))) * uv, hi[i], lo[i]);
           }
-          uint16_t *hp = h_ws + (int64_t)(start + col) * 3 * f + row;
+          uint16_t *hp = h_ws + (int64_t)(start + col) * kHParts * f + row;
           *(uint2 *)(hp) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
-          *(uint2 *)(hp + f) = make_uint2(mi[0] | (mi[1] << 16), mi[2] | (mi[3] << 16));
-          *(uint2 *)(hp + 2 * f) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+          *(uint2 *)(hp + f) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
         }
       }
     }
@@ -817,22 +821,22 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_wide_kernel(
 
 // ------------------------------------------------------------------ down
 // Workgroup = (group, DW*TPW*16 rows of d); each wave owns TPW row tiles and
-// the whole f reduction.  B = the group's h in three exact bf16 parts, three
-// MFMA columns per slot: B row (global column) 3*j + p holds part p of slot j.
-// Those are rows start*3 + 3*j + p of the workspace's h, one contiguous
+// the whole f reduction.  B = the group's h in kHParts = 2 bf16 parts, two
+// MFMA columns per slot: B row (global column) 2*j + p holds part p of slot j.
+// Those are rows start*2 + 2*j + p of the workspace's h, one contiguous
 // block for the group.  Columns come in blocks of 16, so a group of c slots
-// takes ceil(3c/16) MFMAs per 32-element slice (one for up to 5 slots).
+// takes ceil(2c/16) MFMAs per 32-element slice (one for up to 8 slots).
 // Every column accumulates one (slot, part) over the whole reduction in a
 // fixed order, independent of the column's position; the epilogue adds a
-// slot's three part sums, hi + mid, then + lo.  Lanes of columns past the
-// group's read B row 0 (those columns are never used).
+// slot's two part sums, hi + lo.  Lanes of columns past the group's read B
+// row 0 (those columns are never used).
 template <int TPW, int DW, int PF, int MAXC, bool SX4, bool BRES, int CS>
 __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
     int d, int f, int n_slots, const uint8_t *__restrict__ experts, int64_t stride, GroupSrc src,
     const int32_t *__restrict__ perm, int n_dtiles, const uint16_t *__restrict__ h_ws, float *__restrict__ y) {
   constexpr int ROWS = DW / CS * TPW * 16;
   constexpr int NTH = DW * 64;
-  constexpr int NC = 3 * MAXC;        // B rows at most
+  constexpr int NC = kHParts * MAXC;  // B rows at most
   constexpr int NCB = (NC + 15) / 16;  // column blocks at most
   static_assert(DW % CS == 0 && NCB % CS == 0, "column split");
   constexpr int NCBW = NCB / CS;       // column blocks per wave
@@ -840,7 +844,7 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
   constexpr int SPT = BRES ? 0 : (NPIECE + NTH - 1) / NTH;
   constexpr int SPTA = SPT > 0 ? SPT : 1;
   constexpr int YC = down_yc(PF, MAXC, BRES, ROWS);  // epilogue columns per phase
-  constexpr int SPP = YC / 3;                         // slots per phase
+  constexpr int SPP = YC / kHParts;                   // slots per phase
   constexpr int NPH = (MAXC + SPP - 1) / SPP;         // epilogue phases
   constexpr int YP = YC + 1;                          // epilogue row pitch (floats)
   extern __shared__ __align__(16) uint8_t lds[];
@@ -854,12 +858,12 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = lane & 15, q = lane >> 4;
   const int cs = wv % CS, rgw = wv / CS;  // column part and row group of this wave
-  const int nc = 3 * count, ncb = (nc + 15) >> 4;
+  const int nc = kHParts * count, ncb = (nc + 15) >> 4;
   const uint32_t plane = (uint32_t)((int64_t)f * d / 2 + (int64_t)f * d / 32);
   const uint32_t dn_c = 2 * plane, dn_s = dn_c + (uint32_t)((int64_t)d * f / 2);
   const rsrc_t wr = expert_rsrc(src, experts, stride, expert);
-  const rsrc_t hr = make_rsrc(h_ws, (uint32_t)((int64_t)n_slots * 3 * f * 2));
-  const uint32_t hbase = (uint32_t)start * (uint32_t)(3 * f * 2);  // the group's first h row
+  const rsrc_t hr = make_rsrc(h_ws, (uint32_t)((int64_t)n_slots * kHParts * f * 2));
+  const uint32_t hbase = (uint32_t)start * (uint32_t)(kHParts * f * 2);  // the group's first h row
   const int r0 = dt * ROWS;
   const uint32_t brow = bres_row_bytes(f);
   const uint32_t dummy = (uint32_t)down_dummy_off(f, PF, MAXC, BRES, ROWS);
@@ -989,7 +993,7 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
 
   // every (row, column) sum goes through LDS (in the B area: all waves are
   // past their last B read at the first barrier), SPP slots (YC columns) per
-  // phase; each slot's three part sums are added in a fixed order and its
+  // phase; each slot's part sums are added in a fixed order and its
   // rows written as float4
   float *ys = (float *)(lds + down_y_off(f, PF, MAXC, BRES, ROWS));
 #pragma unroll
@@ -1015,8 +1019,8 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
         f32x4 v;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float *yr = ys + (lrow + i) * YP + 3 * jl;
-          v[i] = (yr[0] + yr[1]) + yr[2];
+          const float *yr = ys + (lrow + i) * YP + kHParts * jl;
+          v[i] = yr[0] + yr[1];
         }
         *(f32x4 *)(y + (int64_t)t_slot * d + row) = v;
       }
@@ -1047,7 +1051,7 @@ int64_t ffn_max_groups(int64_t M, int k, int S, int n_experts) {
 
 size_t ffn_workspace_bytes(int64_t M, int k, int S, int d, int f, int n_experts) {
   const int64_t T = M * (k + S);
-  size_t b = align_up((size_t)T * 3 * f * sizeof(uint16_t), 256);
+  size_t b = align_up((size_t)T * kHParts * f * sizeof(uint16_t), 256);
   if (M > kGroupCols) {
     int64_t cap[kGroupClasses];
     group_caps(M, k, S, n_experts, cap);
@@ -1071,7 +1075,7 @@ bool ffn_shape_ok(int64_t M, int k, int S, int d, int f, int64_t stride) {
   (void)d;
   (void)f;
   return stride < lim &&
-         M * (int64_t)d * 4 < lim && T * 3 * f * 2 < lim;
+         M * (int64_t)d * 4 < lim && T * kHParts * f * 2 < lim;
 }
 
 template <int XBF16, int TPW, int GW, int PF, int MAXC, bool SX4, bool BRES, bool PAIR>
@@ -1132,7 +1136,7 @@ int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *exper
   const int n_experts = n_routed + n_shared;
   uint8_t *ws = (uint8_t *)workspace;
   uint16_t *h_ws = (uint16_t *)ws;
-  size_t off = align_up((size_t)T * 3 * f * sizeof(uint16_t), 256);
+  size_t off = align_up((size_t)T * kHParts * f * sizeof(uint16_t), 256);
   const bool many = M > kGroupCols;
   // with many rows: groups of up to 64 slots where the wide gate/up kernel
   // applies (dword-aligned scale rows)
