@@ -116,10 +116,12 @@ def run_verify(torch, moe, synth, shp, layers, stream, dev, timer):
     spines = []
     for l in range(len(layers)):
         wq, ws = synth.q8_0_weight(400 + l, shp.d, shp.d)
-        spines.append(Q8Matrix(torch.from_numpy(wq).to(dev), torch.from_numpy(ws.view(np.int16)).to(dev)))
+        # the spine and head weights in tile order (q8_0_pack), as the experts
+        spines.append(Q8Matrix(torch.from_numpy(wq).to(dev), torch.from_numpy(ws.view(np.int16)).to(dev)).tiled())
     hq, hs = synth.q8_0_weight(500, shp.d, V)
-    head = Q8Matrix(torch.from_numpy(hq).to(dev), torch.from_numpy(hs.view(np.int16)).to(dev))
+    head = Q8Matrix(torch.from_numpy(hq).to(dev), torch.from_numpy(hs.view(np.int16)).to(dev)).tiled()
     del hq, hs
+    torch.cuda.synchronize()
     stack = Stack(layers, spines, head, shp.k, 16, device=dev)
     t0 = 1234
     with torch.cuda.stream(stream):
@@ -463,9 +465,13 @@ def main():
             dwq = torch.from_numpy(wq).to(dev)
             dws = torch.from_numpy(ws.view(np.int16)).to(dev)
             del wq, ws
+            # int8 plane in tile order (q8_0_pack; the same bits as row order)
+            twq = torch.empty_like(dwq)
+            moe.q8_0_pack(dwq, twq, moe.MOE_LAYOUT_TILES)
+            del dwq
             # copies at distinct addresses so the rotation spans >= 1 GB
-            ncopy = max(2, -(-(1 << 30) // dwq.numel()))
-            copies = [(dwq, dws)] + [(dwq.clone(), dws.clone()) for _ in range(ncopy - 1)]
+            ncopy = max(2, -(-(1 << 30) // twq.numel()))
+            copies = [(twq, dws)] + [(twq.clone(), dws.clone()) for _ in range(ncopy - 1)]
             torch.cuda.synchronize()  # the copies are made on torch's stream, read on `stream`
             for Mq in (1, 2, 4, 8):
                 X = torch.from_numpy(synth.q8_0_x(3, Mq, K)).to(dev)
@@ -473,7 +479,7 @@ def main():
 
                 def q(i):
                     a, b = copies[i % ncopy]
-                    moe.q8_0_matmul(X, a, b, Y, stream=stream)
+                    moe.q8_0_matmul(X, a, b, Y, stream=stream, layout=moe.MOE_LAYOUT_TILES)
 
                 for i in range(5):
                     q(i)
@@ -482,7 +488,7 @@ def main():
                 gbs = (wbytes + Mq * (K + N) * 4) / (ms / 1e3) / 1e9
                 q8[f"K{K}_N{N}_M{Mq}"] = dict(us=ms * 1e3, GBps=gbs, hbm_frac=gbs / HBM_PEAK_GBS)
                 log(f"[bench] q8_0 K={K} N={N} M={Mq}: {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
-            del dwq, dws, copies
+            del twq, dws, copies
         results["q8_0"] = q8
 
     # ------------------------------------------------------------ block verification over a layer stack

@@ -6,19 +6,20 @@
 // Arithmetic (fixed for a given K and N, independent of M and of the launch
 // shape below): for output row n and X row m, each 32-block b contributes
 //   P_p = sum_{c in b} q[n,c] * x_p[m,c]        (one MFMA column, fresh C = 0)
-// for the three parts x = x_0 + x_1 + x_2 of an exact bf16 truncation split
-// (int8 is exact in bf16, so every product is exact), and
+// for the two bf16 parts of x (q8_split2: x_0 = x to the nearest bf16, x_1 =
+// the remainder to the nearest bf16, |x - x_0 - x_1| <= 2^-18 |x|; int8 is
+// exact in bf16, so every product is exact on those parts), and
 //   A_p <- fma(P_p, s[n,b], A_p)                 (v_fma_mix: fp16 scale, one rounding)
 // runs over the blocks of a K part in ascending order.  The KS K parts are
-// summed in part order per p, and y = (A_0 + A_1) + A_2.
+// summed in part order per p, and y = A_0 + A_1.
 //
 // Mapping.  A wave owns RT tiles of 16 weight rows and one K part; a step is
 // 64 K (two blocks).  Lane (r, q) loads 16 bytes of row r at K offset
 // 64s + 16q, so lanes q < 2 hold block 2s and q >= 2 block 2s+1; one
 // v_permlane32_swap per dword pair regroups them so each block's 32 values
 // sit 8 per lane group in the order {0, 16, 8, 24} + 0..7, the MFMA A layout.
-// The MFMA B operand has one column per (m, p): column 3m + p, so M <= 5 needs
-// one 16-column MFMA per block and M <= 8 two.  The wave splits X for the step
+// The MFMA B operand has one column per (m, p): column 2m + p, so M <= 8 needs
+// one 16-column MFMA per block.  The wave splits X for the step
 // once (EPL elements per lane) into its own LDS area in that layout, and every
 // tile of the wave reads it back.  Scales: once per 16 steps lane (r, q)
 // loads the 8 fp16 scales of row r for blocks 2 s0 + 8q .. +7 of the chunk
@@ -53,17 +54,18 @@ __device__ __forceinline__ u32x2 q8_i8x4_to_bf16(uint32_t w) {
                q8_pack_hi16(__float_as_uint(f2), __float_as_uint(f3))};
 }
 
-// v == hi + mid + lo exactly; each part is the upper 16 bits of the returned
-// fp32 pattern (truncation: hi keeps the top 8 significant bits of v, mid the
-// top 8 of the remainder, lo the at most 8 bits left).
-__device__ __forceinline__ void q8_split3(float v, uint32_t &hi, uint32_t &mid, uint32_t &lo) {
-  const uint32_t u = __float_as_uint(v);
-  const float r1 = v - __uint_as_float(u & 0xFFFF0000u);
-  const uint32_t u1 = __float_as_uint(r1);
-  const float r2 = r1 - __uint_as_float(u1 & 0xFFFF0000u);
-  hi = u;
-  mid = u1;
-  lo = __float_as_uint(r2);
+// Round-to-nearest-even of an fp32 pattern to bf16, returned as the fp32
+// pattern of that bf16 value (upper 16 bits; finite inputs).
+__device__ __forceinline__ uint32_t q8_round_bf16(uint32_t u) {
+  return ((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16) << 16;
+}
+
+// v ~= hi + lo: hi is v to the nearest bf16 and lo the remainder (an exact
+// fp32 difference) to the nearest bf16, so |v - hi - lo| <= 2^-18 |v|; each
+// part is the upper 16 bits of the returned fp32 pattern.
+__device__ __forceinline__ void q8_split2(float v, uint32_t &hi, uint32_t &lo) {
+  hi = q8_round_bf16(__float_as_uint(v));
+  lo = q8_round_bf16(__float_as_uint(v - __uint_as_float(hi)));
 }
 
 __device__ __forceinline__ float q8_f16_lo(uint32_t v) {
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(Q8_MAX_WAVES * 64) __attribute__((amdgpu_waves_per_
     // where this lane's split goes: block j, lane group g, column 3 xm + p
     const int xj = xk >> 5, xg8 = (xk & 31) >> 3, xe = xk & 7;
     const int xg = ((xg8 & 1) << 1) | (xg8 >> 1);
-    const uint32_t xdst = xm < M ? (uint32_t)(((xj * 4 + xg) * L::kCols + 3 * xm) * 16 + 2 * xe) : (uint32_t)L::kFrag;
+    const uint32_t xdst = xm < M ? (uint32_t)(((xj * 4 + xg) * L::kCols + 2 * xm) * 16 + 2 * xe) : (uint32_t)L::kFrag;
     const uint32_t xpstep = xm < M ? 16u : 0u;  // next part's column (dummy stays put)
     // fragment reads: lane (r, q) reads column 16 mf + r of lane group q
     const uint32_t frd = (uint32_t)((q * L::kCols + r) * 16);
@@ -230,13 +232,13 @@ __global__ __launch_bounds__(Q8_MAX_WAVES * 64) __attribute__((amdgpu_waves_per_
         const int slot = u % PF;
         // 1. split this step's X into the fragment area
         {
-          uint32_t hp[EPL], mp[EPL], lp[EPL];
+          uint32_t hp[EPL], lp[EPL];
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) q8_split3(__uint_as_float(xr[slot][e]), hp[e], mp[e], lp[e]);
+          for (int e = 0; e < EPL; ++e) q8_split2(__uint_as_float(xr[slot][e]), hp[e], lp[e]);
           uint32_t d = xdst;
 #pragma unroll
-          for (int p = 0; p < 3; ++p) {
-            const uint32_t *src = p == 0 ? hp : (p == 1 ? mp : lp);
+          for (int p = 0; p < 2; ++p) {
+            const uint32_t *src = p == 0 ? hp : lp;
             if constexpr (EPL == 8) {
               *(u32x4 *)(wl + d) = u32x4{q8_pack_hi16(src[0], src[1]), q8_pack_hi16(src[2], src[3]),
                                          q8_pack_hi16(src[4], src[5]), q8_pack_hi16(src[6], src[7])};
@@ -315,16 +317,16 @@ __global__ __launch_bounds__(Q8_MAX_WAVES * 64) __attribute__((amdgpu_waves_per_
     const int n = (blockIdx.x * RG + g) * RT * 16 + row;
     if (n >= N) continue;
     const int t = row >> 4, qq = (row >> 2) & 3, i = row & 3;
-    float part_sum[3];
+    float part_sum[2];
 #pragma unroll
-    for (int p = 0; p < 3; ++p) {
-      const int col = 3 * m + p, mf = col >> 4, c = col & 15;
+    for (int p = 0; p < 2; ++p) {
+      const int col = 2 * m + p, mf = col >> 4, c = col & 15;
       const int idx = ((t * NMF + mf) * 4 + i) * 65 + 16 * qq + c;
       float v = ((const float *)(smem + (g * KS) * L::kWave))[idx];
       for (int w = 1; w < KS; ++w) v += ((const float *)(smem + (g * KS + w) * L::kWave))[idx];
       part_sum[p] = v;
     }
-    Y[(int64_t)m * N + n] = (part_sum[0] + part_sum[1]) + part_sum[2];
+    Y[(int64_t)m * N + n] = part_sum[0] + part_sum[1];
   }
 }
 
@@ -334,7 +336,7 @@ template <int RT, int PF, int EPL, int NMF, bool MASKED, int WPE>
 static int q8_run(const float *X, int M, int K, const int8_t *wq, const uint16_t *ws, int N, float *Y, int KS,
                   int RG, int tiled, hipStream_t stream) {
   using L = Q8Lds<RT, NMF>;
-  if (KS < 1 || RG < 1 || KS * RG > Q8_MAX_WAVES || M > EPL || 3 * M > 16 * NMF) return -3;
+  if (KS < 1 || RG < 1 || KS * RG > Q8_MAX_WAVES || M > EPL || 2 * M > 16 * NMF) return -3;
   const size_t smem = (size_t)KS * RG * L::kWave;
   auto kern = q8_0_kernel<RT, PF, EPL, NMF, MASKED, WPE>;
   if (smem > 65536 &&
@@ -377,7 +379,7 @@ int q8_0_launch(const float *X, int M, int K, const int8_t *wq, const uint16_t *
     if (M <= 2) return q8_run<2, 4, 2, 1, true, 1>(X, M, K, wq, ws, N, Y, KS, RG, tiled, stream);
     if (M <= 4) return q8_run<2, 4, 4, 1, true, 1>(X, M, K, wq, ws, N, Y, KS, RG, tiled, stream);
     if (M <= 5) return q8_run<2, 4, 8, 1, true, 1>(X, M, K, wq, ws, N, Y, KS, RG, tiled, stream);
-    return q8_run<2, 4, 8, 2, true, 1>(X, M, K, wq, ws, N, Y, KS, RG, tiled, stream);
+    return q8_run<2, 4, 8, 1, true, 1>(X, M, K, wq, ws, N, Y, KS, RG, tiled, stream);
   }
   if (M <= 1)
     return big ? q8_run<2, 4, 1, 1, false, 1>(X, M, K, wq, ws, N, Y, KS, RG, tiled, stream)
@@ -391,8 +393,8 @@ int q8_0_launch(const float *X, int M, int K, const int8_t *wq, const uint16_t *
   if (M <= 5)
     return big ? q8_run<2, 4, 8, 1, false, 1>(X, M, K, wq, ws, N, Y, KS, RG, tiled, stream)
                : q8_run<2, 2, 8, 1, false, 4>(X, M, K, wq, ws, N, Y, KS, RG, tiled, stream);
-  return big ? q8_run<4, 2, 8, 2, false, 1>(X, M, K, wq, ws, N, Y, KS, RG, tiled, stream)
-             : q8_run<2, 2, 8, 2, false, 4>(X, M, K, wq, ws, N, Y, KS, RG, tiled, stream);
+  return big ? q8_run<4, 2, 8, 1, false, 1>(X, M, K, wq, ws, N, Y, KS, RG, tiled, stream)
+             : q8_run<2, 2, 8, 1, false, 4>(X, M, K, wq, ws, N, Y, KS, RG, tiled, stream);
 }
 
 }  // namespace moe
