@@ -716,8 +716,12 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_wide_kernel(
       for (int h = 0; h < EL / 2; ++h) xst[p][i][h] = buf_load16(xr, pbase[i] + kx + 16 * h);
     }
   };
+  // lane q loads the scale dword of step 4j + q; the dword of a padding step
+  // (past d) would lie past the row's d/32 scale bytes, in the next row or
+  // plane, where a 0xFF byte would make the scale infinite and its zero codes
+  // NaN, so such lanes read past the resource (zero bytes) instead
   auto load_sc = [&](int j, uint32_t (&sc)[NT]) {
-    const uint32_t js = j < ngroups ? 16u * (uint32_t)j : kDead;
+    const uint32_t js = (j < ngroups && 4 * j + q < nsteps) ? 16u * (uint32_t)j : kDead;
 #pragma unroll
     for (int t = 0; t < NT; ++t) sc[t] = buf_load4(wr, soff[t] + js);
   };

@@ -370,6 +370,34 @@ def test_layer_call_back_to_back_and_given_logits():
     _compare_layer(res, ref, "given logits", shape.k, shape.n_shared)
 
 
+def test_wide_groups_scale_bytes_after_the_plane():
+    """The wide gate/up kernel reads a scale dword per lane for each step of a
+    4-step group; with d/128 not a multiple of 4 the last group has padding
+    steps, whose dwords lie past a row's scale bytes.  Codes bytes of 0xFF
+    right after the W_gate and W_up scale planes (the first bytes of the
+    W_up and W_down codes planes: valid E2M1 data) must not reach the
+    arithmetic as scales: the layer still matches the oracle."""
+    moe = _moe()
+    shape = synth.LayerShape("pad", 384, 32, 3, 1, 2, -6, -2, 0.05, "bf16")
+    seed, M = 7, 24  # the shared expert's 24 slots form a 32-wide group
+    c, sc = shape.f * shape.d // 2, shape.f * shape.d // 32
+    recs = {}
+    for e in range(shape.n_experts):
+        r = synth.expert_record(shape, seed, e).copy()
+        r[c + sc:c + sc + 16] = 0xFF              # first bytes of W_up codes
+        r[2 * (c + sc):2 * (c + sc) + 16] = 0xFF  # first bytes of W_down codes
+        recs[e] = r
+    base = torch.from_numpy(np.concatenate([recs[e] for e in range(shape.n_experts)])).cuda()
+    ex = moe.Experts(base, shape.stride, shape.d, shape.f, shape.n_routed, shape.n_shared)
+    wr = synth.router_weight(shape, seed)
+    x = synth.rows_x(shape, seed, M)
+    layer = moe.MoELayer(ex, shape.k, M, w_router=_dev(wr))
+    layer.workspace.fill_(0xFF)
+    res = layer.forward(_x_dev(shape, x))
+    ref = oracle.layer(x, shape.k, shape.n_routed, shape.n_shared, shape.d, shape.f, recs.__getitem__, w_r=wr)
+    _compare_layer(res, ref, "scale bytes after the plane", shape.k, shape.n_shared)
+
+
 # ----------------------------------------------------------------------------- Kimi decode
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_kimi_one_row_parity(kimi_layer, seed):

@@ -1,0 +1,95 @@
+"""Seeded random layer shapes through the whole layer call on the GPU, each
+against the oracle, with row 0 of every block checked bit for bit against
+the same row run alone, and the tile-ordered records against row order.
+d and f come from sizes the fixed-shape tests already cover; E, k, S, M and
+the x dtype vary around them (M on both sides of the 16-row switch to the
+grouped prefill path).  Needs an MI355X."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from conftest import assert_close
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 30
+D_CHOICES = (96, 128, 160, 256, 384, 416, 512)
+F_CHOICES = (32, 96, 128, 160, 224)
+E_CHOICES = (1, 2, 3, 5, 9, 16, 33, 100)
+M_CHOICES = (1, 2, 3, 5, 8, 13, 16, 17, 24, 40, 64)
+
+
+def _moe():
+    import router_top_bucket_amd as moe
+    return moe
+
+
+def _cases():
+    g = np.random.default_rng(20261202)
+    out = []
+    for i in range(N_CASES):
+        d = int(g.choice(D_CHOICES))
+        f = int(g.choice(F_CHOICES))
+        E = int(g.choice(E_CHOICES))
+        k = int(g.integers(1, min(E, 16) + 1))
+        S = int(g.integers(0, 4))
+        M = int(g.choice(M_CHOICES))
+        dt = "bf16" if g.integers(0, 2) else "f32"
+        out.append((synth.LayerShape(f"rnd{i}", d, f, E, S, k, -6, -2, 0.05, dt), M, 1000 + i))
+    return out
+
+
+def _host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _x_dev(shape, x):
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    return (t.view(torch.bfloat16) if shape.x_dtype == "bf16" else t).cuda()
+
+
+def _outputs(res, M, k, S):
+    kps = k + S
+    na = int(_host(res["n_active"])[0])
+    return dict(logits=_host(res["logits"][:M]), ids=_host(res["topk_ids"][:M]), w=_host(res["topk_w"][:M]),
+                offsets=_host(res["offsets"]), perm=_host(res["perm"][:M * kps]), active=_host(res["active"])[:na],
+                y=_host(res["y_slots"][:M * kps]), out=_host(res["out"][:M]), dev_error=_host(res["dev_error"]))
+
+
+@pytest.mark.parametrize("shape,M,seed", _cases(), ids=lambda v: v.name if hasattr(v, "name") else str(v))
+def test_random_shape_layer(shape, M, seed):
+    moe = _moe()
+    k, S = shape.k, shape.n_shared
+    base = synth.device_experts(shape, seed)
+    ex = moe.Experts(base, shape.stride, shape.d, shape.f, shape.n_routed, shape.n_shared)
+    recs = {e: synth.expert_record(shape, seed, e) for e in range(shape.n_experts)}
+    wr = synth.router_weight(shape, seed)
+    wr_d = torch.from_numpy(wr).cuda()
+    x = synth.rows_x(shape, seed, M)
+    what = f"{shape} M={M}"
+
+    res = moe.MoELayer(ex, k, M, w_router=wr_d).forward(_x_dev(shape, x))
+    got = _outputs(res, M, k, S)
+    ref = oracle.layer(x, k, shape.n_routed, S, shape.d, shape.f, recs.__getitem__, w_r=wr)
+    assert_close(got["logits"], ref["logits"], what + " logits")
+    assert np.array_equal(got["ids"], ref["ids"]), what + " ids"
+    assert_close(got["w"], ref["w"], what + " w")
+    assert np.array_equal(got["offsets"], ref["offsets"]) and np.array_equal(got["perm"], ref["perm"]), what
+    assert np.array_equal(got["active"], ref["active"]) and int(got["dev_error"][0]) == 0, what
+    assert_close(got["y"], ref["y_slots"], what + " y_slots")
+    assert_close(got["out"], ref["out"], what + " out")
+
+    if M > 1:  # row 0 of the block against the row alone, bit for bit
+        one = _outputs(moe.MoELayer(ex, k, 1, w_router=wr_d).forward(_x_dev(shape, x[:1])), 1, k, S)
+        for key in ("logits", "ids", "w", "out"):
+            assert np.array_equal(got[key][:1].view(np.uint8), one[key].view(np.uint8)), (what, key)
+        assert np.array_equal(got["y"][:k + S].view(np.uint8), one["y"].view(np.uint8)), (what, "y")
+
+    # tile-ordered records give the same bits
+    tiles = moe.tile_experts(ex)
+    got_t = _outputs(moe.MoELayer(tiles, k, M, w_router=wr_d).forward(_x_dev(shape, x)), M, k, S)
+    for key in ("y", "out"):
+        assert np.array_equal(got_t[key].view(np.uint8), got[key].view(np.uint8)), (what, "tiles", key)
