@@ -14,11 +14,11 @@ from conftest import assert_close
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 30
-D_CHOICES = (96, 128, 160, 256, 384, 416, 512)
-F_CHOICES = (32, 96, 128, 160, 224)
-E_CHOICES = (1, 2, 3, 5, 9, 16, 33, 100)
-M_CHOICES = (1, 2, 3, 5, 8, 13, 16, 17, 24, 40, 64)
+N_CASES = 60
+D_CHOICES = (96, 128, 160, 256, 384, 416, 512, 640, 768)
+F_CHOICES = (32, 96, 128, 160, 224, 256, 288)
+E_CHOICES = (1, 2, 3, 5, 9, 16, 33, 100, 300)
+M_CHOICES = (1, 2, 3, 4, 5, 8, 13, 16, 17, 24, 40, 64, 130)
 
 
 def _moe():
@@ -93,3 +93,39 @@ def test_random_shape_layer(shape, M, seed):
     got_t = _outputs(moe.MoELayer(tiles, k, M, w_router=wr_d).forward(_x_dev(shape, x)), M, k, S)
     for key in ("y", "out"):
         assert np.array_equal(got_t[key].view(np.uint8), got[key].view(np.uint8)), (what, "tiles", key)
+
+
+# ----------------------------------------------------------------------------- Q8_0
+def _q8_cases():
+    g = np.random.default_rng(4242)
+    out = []
+    for i in range(24):
+        K = int(g.choice((32, 64, 96, 160, 224, 512, 1024, 2080)))
+        N = int(g.choice((1, 5, 16, 17, 100, 256, 1000, 4096)))
+        M = int(g.integers(1, 9))
+        out.append((K, N, M, 7000 + i))
+    return out
+
+
+@pytest.mark.parametrize("K,N,M,seed", _q8_cases())
+def test_random_shape_q8_0(K, N, M, seed):
+    """Q8_0 against the oracle; row 0 of M rows equals the row alone bit for
+    bit; the tile-ordered plane (N % 16 == 0) gives the same bits."""
+    moe = _moe()
+    wq, ws = synth.q8_0_weight(seed, K, N)
+    X = synth.q8_0_x(seed, M, K)
+    dwq = torch.from_numpy(wq).cuda()
+    dws = torch.from_numpy(ws.view(np.int16)).cuda()
+    Y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    moe.q8_0_matmul(torch.from_numpy(X).cuda(), dwq, dws, Y)
+    got = _host(Y)
+    assert_close(got, oracle.q8_0_matmul(X, wq, ws), f"q8_0 K={K} N={N} M={M}")
+    Y1 = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    moe.q8_0_matmul(torch.from_numpy(X[:1].copy()).cuda(), dwq, dws, Y1)
+    assert np.array_equal(_host(Y1).view(np.uint32), got[:1].view(np.uint32)), (K, N, M)
+    if N % 16 == 0:
+        tq = torch.empty_like(dwq)
+        moe.q8_0_pack(dwq, tq, moe.MOE_LAYOUT_TILES)
+        Yt = torch.empty_like(Y)
+        moe.q8_0_matmul(torch.from_numpy(X).cuda(), tq, dws, Yt, layout=moe.MOE_LAYOUT_TILES)
+        assert np.array_equal(_host(Yt).view(np.uint32), got.view(np.uint32)), (K, N, M, "tiles")
