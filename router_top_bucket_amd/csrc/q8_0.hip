@@ -68,6 +68,18 @@ __device__ __forceinline__ void q8_split2(float v, uint32_t &hi, uint32_t &lo) {
   lo = q8_round_bf16(__float_as_uint(v - __uint_as_float(hi)));
 }
 
+// The same split for two values at once with the paired round-to-nearest-even
+// convert (v_cvt_pk_bf16_f32): hi and lo each hold the two parts packed
+// (x0's in the low half), bit for bit the parts q8_split2 gives.
+typedef float q8_f32x2 __attribute__((__vector_size__(2 * sizeof(float))));
+__device__ __forceinline__ uint32_t q8_pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((q8_f32x2){a, b}, bf16x2));
+}
+__device__ __forceinline__ void q8_split2_pk(float x0, float x1, uint32_t &hi, uint32_t &lo) {
+  hi = q8_pk_bf16(x0, x1);
+  lo = q8_pk_bf16(x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xFFFF0000u));
+}
+
 __device__ __forceinline__ float q8_f16_lo(uint32_t v) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
 }
@@ -232,24 +244,29 @@ __global__ __launch_bounds__(Q8_MAX_WAVES * 64) __attribute__((amdgpu_waves_per_
         const int slot = u % PF;
         // 1. split this step's X into the fragment area
         {
-          uint32_t hp[EPL], lp[EPL];
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) q8_split2(__uint_as_float(xr[slot][e]), hp[e], lp[e]);
           uint32_t d = xdst;
+          if constexpr (EPL == 1) {
+            uint32_t hp, lp;
+            q8_split2(__uint_as_float(xr[slot][0]), hp, lp);
+            *(uint16_t *)(wl + d) = (uint16_t)(hp >> 16);
+            *(uint16_t *)(wl + d + xpstep) = (uint16_t)(lp >> 16);
+          } else {
+            constexpr int NP = EPL / 2;  // packed pairs
+            uint32_t hp[NP], lp[NP];
 #pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            const uint32_t *src = p == 0 ? hp : lp;
-            if constexpr (EPL == 8) {
-              *(u32x4 *)(wl + d) = u32x4{q8_pack_hi16(src[0], src[1]), q8_pack_hi16(src[2], src[3]),
-                                         q8_pack_hi16(src[4], src[5]), q8_pack_hi16(src[6], src[7])};
-            } else if constexpr (EPL == 4) {
-              *(u32x2 *)(wl + d) = u32x2{q8_pack_hi16(src[0], src[1]), q8_pack_hi16(src[2], src[3])};
-            } else if constexpr (EPL == 2) {
-              *(uint32_t *)(wl + d) = q8_pack_hi16(src[0], src[1]);
-            } else {
-              *(uint16_t *)(wl + d) = (uint16_t)(src[0] >> 16);
+            for (int e = 0; e < NP; ++e)
+              q8_split2_pk(__uint_as_float(xr[slot][2 * e]), __uint_as_float(xr[slot][2 * e + 1]), hp[e], lp[e]);
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+              const uint32_t *src = p == 0 ? hp : lp;
+              if constexpr (EPL == 8)
+                *(u32x4 *)(wl + d) = u32x4{src[0], src[1], src[2], src[3]};
+              else if constexpr (EPL == 4)
+                *(u32x2 *)(wl + d) = u32x2{src[0], src[1]};
+              else
+                *(uint32_t *)(wl + d) = src[0];
+              d += xpstep;
             }
-            d += xpstep;
           }
         }
         // 2. weights of both blocks as bf16 A fragments
