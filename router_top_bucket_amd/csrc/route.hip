@@ -19,7 +19,8 @@ namespace moe {
 // Rows of x are taken MCH at a time and the reduction KC chunks at a time;
 // each pass issues all its loads (W and x, buffer loads: out-of-range chunks
 // read zero, and a zero term at the end of a chain leaves it unchanged)
-// before any arithmetic, so a thread waits for memory once per pass.
+// before any arithmetic; with single-chunk passes (KC = 1) the next pass's
+// loads are issued before this pass's arithmetic.
 constexpr int LG_THREADS = 256;
 
 template <int XBF16, int RW, int MCH, int KC>
@@ -31,7 +32,12 @@ __global__ __launch_bounds__(LG_THREADS) void router_logits_kernel(const void *_
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int nchunk = d >> 2;
   constexpr int EL = XBF16 ? 2 : 4;
+  constexpr int STEP = LG_THREADS * KC;  // chunks per pass
   typedef typename std::conditional<XBF16 != 0, u32x2, u32x4>::type xraw_t;
+  struct Pass {
+    f32x4 w[KC][RW];
+    xraw_t x[MCH][KC];
+  };
   const rsrc_t wres = make_rsrc(w, (uint32_t)((int64_t)E * d * 4));
   const rsrc_t xres = make_rsrc(x, (uint32_t)((int64_t)M * d * EL));
   for (int mc = 0; mc < M; mc += MCH) {
@@ -41,46 +47,71 @@ __global__ __launch_bounds__(LG_THREADS) void router_logits_kernel(const void *_
     for (int m = 0; m < MCH; ++m)
 #pragma unroll
       for (int rr = 0; rr < RW; ++rr) acc[m][rr] = 0.f;
-    for (int cb = 0; cb < nchunk; cb += LG_THREADS * KC) {
-      f32x4 wr[KC][RW];
-      xraw_t xr[MCH][KC];
+    // every load of the pass at chunk base cb (out-of-range chunks read zero)
+    auto load = [&](int cb, Pass &ps) {
 #pragma unroll
       for (int i = 0; i < KC; ++i) {
         const int c = cb + tid + i * LG_THREADS;
 #pragma unroll
         for (int rr = 0; rr < RW; ++rr)
-          wr[i][rr] = __builtin_bit_cast(
+          ps.w[i][rr] = __builtin_bit_cast(
               f32x4, buf_load16(wres, (c < nchunk && e0 + rr < E) ? (uint32_t)(((e0 + rr) * d + 4 * c) * 4) : kOOB));
 #pragma unroll
         for (int m = 0; m < MCH; ++m) {
           const uint32_t off = (c < nchunk && m < mn) ? (uint32_t)(((mc + m) * d + 4 * c) * EL) : kOOB;
-          if constexpr (XBF16) xr[m][i] = buf_load8(xres, off);
-          else xr[m][i] = buf_load16(xres, off);
+          if constexpr (XBF16) ps.x[m][i] = buf_load8(xres, off);
+          else ps.x[m][i] = buf_load16(xres, off);
         }
       }
+    };
+    auto compute = [&](const Pass &ps) {
 #pragma unroll
       for (int i = 0; i < KC; ++i) {
 #pragma unroll
         for (int m = 0; m < MCH; ++m) {
           f32x4 xv;
           if constexpr (XBF16) {
-            xv[0] = __uint_as_float(xr[m][i][0] << 16);
-            xv[1] = __uint_as_float(xr[m][i][0] & 0xFFFF0000u);
-            xv[2] = __uint_as_float(xr[m][i][1] << 16);
-            xv[3] = __uint_as_float(xr[m][i][1] & 0xFFFF0000u);
+            xv[0] = __uint_as_float(ps.x[m][i][0] << 16);
+            xv[1] = __uint_as_float(ps.x[m][i][0] & 0xFFFF0000u);
+            xv[2] = __uint_as_float(ps.x[m][i][1] << 16);
+            xv[3] = __uint_as_float(ps.x[m][i][1] & 0xFFFF0000u);
           } else {
-            xv = __builtin_bit_cast(f32x4, xr[m][i]);
+            xv = __builtin_bit_cast(f32x4, ps.x[m][i]);
           }
 #pragma unroll
           for (int rr = 0; rr < RW; ++rr) {
             float a = acc[m][rr];
-            a = __builtin_fmaf(wr[i][rr][0], xv[0], a);
-            a = __builtin_fmaf(wr[i][rr][1], xv[1], a);
-            a = __builtin_fmaf(wr[i][rr][2], xv[2], a);
-            a = __builtin_fmaf(wr[i][rr][3], xv[3], a);
+            a = __builtin_fmaf(ps.w[i][rr][0], xv[0], a);
+            a = __builtin_fmaf(ps.w[i][rr][1], xv[1], a);
+            a = __builtin_fmaf(ps.w[i][rr][2], xv[2], a);
+            a = __builtin_fmaf(ps.w[i][rr][3], xv[3], a);
             acc[m][rr] = a;
           }
         }
+      }
+    };
+    if (KC > 1 || nchunk <= STEP) {  // one pass at a time
+      for (int cb = 0; cb < nchunk; cb += STEP) {
+        Pass a;
+        load(cb, a);
+        compute(a);
+      }
+    } else {
+      // single-chunk passes (the many-row shape): two register sets, so the
+      // next pass's loads are in flight while this pass computes (its wait
+      // covers only its own, older loads); the chain order of every logit is
+      // the same as one pass at a time
+      Pass a, b;
+      load(0, a);
+      for (int cb = 0;;) {
+        load(cb + STEP, b);
+        compute(a);
+        cb += STEP;
+        if (cb >= nchunk) break;
+        load(cb + STEP, a);
+        compute(b);
+        cb += STEP;
+        if (cb >= nchunk) break;
       }
     }
 #pragma unroll
