@@ -3,7 +3,10 @@ against the oracle, with row 0 of every block checked bit for bit against
 the same row run alone, and the tile-ordered records against row order.
 d and f come from sizes the fixed-shape tests already cover; E, k, S, M and
 the x dtype vary around them (M on both sides of the 16-row switch to the
-grouped prefill path).  Needs an MI355X."""
+grouped prefill path).  MOE_RANDOM_SEED and MOE_RANDOM_CASES (layer cases;
+the Q8_0 cases are a third of that) draw another set.  Needs an MI355X."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -14,11 +17,12 @@ from conftest import assert_close
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 60
-D_CHOICES = (96, 128, 160, 256, 384, 416, 512, 640, 768)
-F_CHOICES = (32, 96, 128, 160, 224, 256, 288)
-E_CHOICES = (1, 2, 3, 5, 9, 16, 33, 100, 300)
-M_CHOICES = (1, 2, 3, 4, 5, 8, 13, 16, 17, 24, 40, 64, 130)
+SEED = int(os.environ.get("MOE_RANDOM_SEED", "20261202"))
+N_CASES = int(os.environ.get("MOE_RANDOM_CASES", "60"))
+D_CHOICES = (32, 64, 96, 128, 160, 256, 384, 416, 512, 640, 768, 1024)
+F_CHOICES = (32, 64, 96, 128, 160, 224, 256, 288, 352, 512)
+E_CHOICES = (1, 2, 3, 4, 5, 9, 16, 33, 64, 100, 300, 896)
+M_CHOICES = (1, 2, 3, 4, 5, 6, 8, 13, 15, 16, 17, 24, 33, 40, 64, 65, 130, 200, 333)
 
 
 def _moe():
@@ -27,7 +31,7 @@ def _moe():
 
 
 def _cases():
-    g = np.random.default_rng(20261202)
+    g = np.random.default_rng(SEED)
     out = []
     for i in range(N_CASES):
         d = int(g.choice(D_CHOICES))
@@ -73,8 +77,11 @@ def test_random_shape_layer(shape, M, seed):
 
     res = moe.MoELayer(ex, k, M, w_router=wr_d).forward(_x_dev(shape, x))
     got = _outputs(res, M, k, S)
-    ref = oracle.layer(x, k, shape.n_routed, S, shape.d, shape.f, recs.__getitem__, w_r=wr)
-    assert_close(got["logits"], ref["logits"], what + " logits")
+    assert_close(got["logits"], oracle.router_logits(x, wr), what + " logits")
+    # The top-k decision and everything after it against the oracle on the
+    # same fp32 logits the GPU decided on: the two logit sums agree only to
+    # rounding, and two experts whose logits tie within it may rank either way.
+    ref = oracle.layer(x, k, shape.n_routed, S, shape.d, shape.f, recs.__getitem__, logits=got["logits"])
     assert np.array_equal(got["ids"], ref["ids"]), what + " ids"
     assert_close(got["w"], ref["w"], what + " w")
     assert np.array_equal(got["offsets"], ref["offsets"]) and np.array_equal(got["perm"], ref["perm"]), what
@@ -97,11 +104,11 @@ def test_random_shape_layer(shape, M, seed):
 
 # ----------------------------------------------------------------------------- Q8_0
 def _q8_cases():
-    g = np.random.default_rng(4242)
+    g = np.random.default_rng(SEED + 1)
     out = []
-    for i in range(24):
-        K = int(g.choice((32, 64, 96, 160, 224, 512, 1024, 2080)))
-        N = int(g.choice((1, 5, 16, 17, 100, 256, 1000, 4096)))
+    for i in range(max(1, N_CASES // 3)):
+        K = int(g.choice((32, 64, 96, 128, 160, 224, 512, 1024, 2048, 2080, 4096, 7168)))
+        N = int(g.choice((1, 2, 5, 15, 16, 17, 31, 48, 100, 256, 1000, 4096, 8192)))
         M = int(g.integers(1, 9))
         out.append((K, N, M, 7000 + i))
     return out
