@@ -88,6 +88,11 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// The same load marked non-temporal (nt): for a stream read once, so that
+// its lines leave the caches first and data that is re-read stays.
+__device__ __forceinline__ u32x4 buf_load16_stream(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
 __device__ __forceinline__ u32x2 buf_load8(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }

@@ -23,7 +23,10 @@
 //
 // Memory: every operand is read with buffer loads (an offset past the end
 // reads zero), so lanes of empty columns, rows past f or d and K past the
-// end need no branch.  Weight codes and the B operand of a step travel
+// end need no branch.  Weight codes are streamed with non-temporal loads
+// wherever a call reads an expert's codes once (every group of up to 16
+// slots); the 32- and 64-wide groups of one expert re-read its codes from
+// the caches and use ordinary loads.  Weight codes and the B operand of a step travel
 // together through a ring of PF steps and are consumed in issue order, which
 // is the order the vector-memory counter retires them in.
 #include "common.h"
@@ -442,7 +445,7 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
   auto issue = [&](int s, int p) {
     const uint32_t ka = s < smax ? (uint32_t)s * cstep : kDead;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) ring[p][t] = buf_load16(wr, aoff[t] + ka);
+    for (int t = 0; t < NT; ++t) ring[p][t] = buf_load16_stream(wr, aoff[t] + ka);
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
       const int k = (s << 7) + pel[i];
@@ -912,7 +915,7 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
   auto issue = [&](int s, int p) {
     const uint32_t ka = s < smax ? (uint32_t)s * cstep : kDead;
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) ring[p][t] = buf_load16(wr, aoff[t] + ka);
+    for (int t = 0; t < TPW; ++t) ring[p][t] = MAXC <= kGroupCols ? buf_load16_stream(wr, aoff[t] + ka) : buf_load16(wr, aoff[t] + ka);
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
       const int k = (s << 7) + pel[i];

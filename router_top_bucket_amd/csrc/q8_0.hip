@@ -171,7 +171,7 @@ __global__ __launch_bounds__(Q8_MAX_WAVES * 64) __attribute__((amdgpu_waves_per_
       for (int t = 0; t < RT; ++t) {
         uint32_t o = woff[t];
         if constexpr (MASKED) o = 2 * s + (q >> 1) < b_end ? o : kOOB;
-        wr[slot][t] = buf_load16(wrs, o + wstep);
+        wr[slot][t] = buf_load16_stream(wrs, o + wstep);
       }
       uint32_t xo = xoff;
       if constexpr (MASKED) xo = 2 * s + xj < b_end ? xo : kOOB;

@@ -54,8 +54,11 @@ __global__ __launch_bounds__(LG_THREADS) void router_logits_kernel(const void *_
         const int c = cb + tid + i * LG_THREADS;
 #pragma unroll
         for (int rr = 0; rr < RW; ++rr)
-          ps.w[i][rr] = __builtin_bit_cast(
-              f32x4, buf_load16(wres, (c < nchunk && e0 + rr < E) ? (uint32_t)(((e0 + rr) * d + 4 * c) * 4) : kOOB));
+        {
+          const uint32_t wo = (c < nchunk && e0 + rr < E) ? (uint32_t)(((e0 + rr) * d + 4 * c) * 4) : kOOB;
+          // W is read once when one pass takes every row: stream it
+          ps.w[i][rr] = __builtin_bit_cast(f32x4, M <= MCH ? buf_load16_stream(wres, wo) : buf_load16(wres, wo));
+        }
 #pragma unroll
         for (int m = 0; m < MCH; ++m) {
           const uint32_t off = (c < nchunk && m < mn) ? (uint32_t)(((mc + m) * d + 4 * c) * EL) : kOOB;
