@@ -282,8 +282,9 @@ __host__ __device__ __forceinline__ size_t down_lds_bytes(int f, int pf, int max
 // loads of the first round of pieces, end() stores them and stages any
 // further rounds (loads before stores), so that a kernel can issue begin()
 // before its ring prefill and let one wait cover both.  Every load is stored
-// (to `dummy` when out of range).
-template <bool W16>
+// (to `dummy` when out of range).  STREAM: wide loads carry the non-temporal
+// hint (the ring-mode kernels; measured faster there, slower at 1 row).
+template <bool W16, bool STREAM = false>
 struct ScaleStage {
   static constexpr int CH = W16 ? 4 : 8;  // pieces per thread per round
   u32x4 v16[W16 ? CH : 1];
@@ -299,9 +300,10 @@ struct ScaleStage {
       pr[c] = piece / per_row;
       pc[c] = piece - pr[c] * per_row;
       const bool ok = piece < npieces && pr[c] < rows_valid;
-      if (W16)
-        v16[c] = buf_load16(wr, ok ? plane + (uint32_t)(row0 + pr[c]) * (uint32_t)nb + 16u * pc[c] : kOOB);
-      else
+      if (W16) {
+        const uint32_t o = ok ? plane + (uint32_t)(row0 + pr[c]) * (uint32_t)nb + 16u * pc[c] : kOOB;
+        v16[c] = STREAM ? buf_load16_stream(wr, o) : buf_load16(wr, o);
+      } else
         v1[c] = buf_load1(wr, ok ? plane + (uint32_t)(row0 + pr[c]) * (uint32_t)nb + (uint32_t)pc[c] : kOOB);
     }
   }
@@ -459,7 +461,7 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
   // in flight at every loop iteration, instead of keeping the prefill's issue
   // order in mind at the loop head and waiting far deeper than the ring needs)
   const int rv = f - i0 < ROWS ? f - i0 : ROWS;
-  ScaleStage<SX4> sg, su;
+  ScaleStage<SX4, !BRES> sg, su;
   sg.begin(wr, plane_c, i0, rv, ROWS, d, tid, NTH);
   su.begin(wr, 2 * plane_c + plane_s, i0, rv, ROWS, d, tid, NTH);
 #pragma unroll
@@ -924,7 +926,7 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
   };
   // scale staging loads, then the ring prefill, one wait (see the gate/up kernel)
   const int rv = d - r0 < ROWS ? d - r0 : ROWS;
-  ScaleStage<SX4> ss;
+  ScaleStage<SX4, !BRES> ss;
   ss.begin(wr, dn_s, r0, rv, ROWS, f, tid, NTH);
 #pragma unroll
   for (int p = 0; p < PF; ++p) issue(p, p);
