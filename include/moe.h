@@ -20,8 +20,8 @@
  *  - M = 0 rows is valid and enqueues nothing.
  *  - Rows of one call never influence each other's results: the result of a
  *    row is bit-identical whether it is alone (M = 1) or inside a block of
- *    any M, for every function here ("A drafter that leaves the answer
- *    unchanged": a block's rows run the same arithmetic as plain steps).
+ *    any M, for every function here (the verification blocks of "A drafter
+ *    that leaves the answer unchanged" must reproduce one-row steps exactly).
  *
  * MXFP4 storage (OCP MX v1.0 elements; the byte layout is this library's
  * data contract, the pages give only the format name and the 17,547,264-byte
@@ -79,9 +79,10 @@ typedef struct {
   int32_t layout;      /* moe_layout of the codes planes */
 } moe_experts;
 
-/* Router ("Read the experts the router needs": the router picks 16 of 896
- * experts per token).  The router function is softmax over the E logits,
- * the k largest are kept and their probabilities renormalised to sum to 1.
+/* Router ("Read the experts the router needs": top-k routing, k = 16 of
+ * E = 896 in the Kimi layer).  The router function is softmax over the E
+ * logits; the k largest are kept and their probabilities renormalised to
+ * sum to 1.
  *
  *   x         [M x d] fp32 or bf16 (x_dtype), the layer input rows.
  *   w_router  [E x d] fp32.  If non-NULL, logits[m,e] = sum_c w_router[e,c]*x[m,c]
@@ -98,10 +99,10 @@ typedef struct {
 int moe_route(const void *x, moe_dtype x_dtype, const float *w_router, float *logits, int32_t M, int32_t d,
               int32_t E, int32_t k, int32_t *topk_ids, float *topk_w, void *stream);
 
-/* Bucketing: group the M*(k+S) slots by expert so each expert's rows are
- * found together and its weights are read once for all of them ("A drafter
- * that leaves the answer unchanged": a block reads each expert once for all
- * its rows).  Slot t = m*(k+S)+j is routed expert topk_ids[m,j] for j < k and
+/* Bucketing: group the M*(k+S) slots by expert so that one pass over an
+ * expert's weights serves every row of the call that selected it ("A drafter
+ * that leaves the answer unchanged": a block's weight traffic is one read per
+ * distinct expert).  Slot t = m*(k+S)+j is routed expert topk_ids[m,j] for j < k and
  * shared expert E+(j-k) for j >= k.
  *
  *   offsets   [E+S+1] int32 out: exclusive prefix sum of per-expert slot
@@ -121,8 +122,9 @@ int moe_bucket(const int32_t *topk_ids, int32_t M, int32_t k, int32_t E, int32_t
                int32_t *perm, int32_t *active, int32_t *n_active, int32_t *dev_error, void *stream);
 
 /* Expert FFN over the bucketed slots ("A drafter that leaves the answer
- * unchanged": each expert's weights are read once for all rows of the block;
- * experts are SwiGLU: y = W_down (silu(W_gate x) * (W_up x)), silu(z) = z/(1+e^-z)).
+ * unchanged": one pass over an expert's weights per call, whatever the number
+ * of its rows).  Experts are SwiGLU: y = W_down (silu(W_gate x) * (W_up x)),
+ * silu(z) = z/(1+e^-z).
  *
  *   x         [M x d] fp32 or bf16 (x_dtype).
  *   M, k      as given to moe_bucket; S = W->n_shared.
@@ -178,9 +180,8 @@ int moe_combine(const float *y_slots, const float *topk_w, int32_t M, int32_t k,
                 float *out, void *stream);
 
 /* One MoE layer in one call: moe_route, moe_bucket, moe_expert_ffn_mxfp4 and
- * moe_combine in that order ("Read the experts the router needs": router,
- * then the selected experts; "A drafter that leaves the answer unchanged":
- * rows bucketed per expert, each expert read once, outputs combined).  Every
+ * moe_combine in that order ("Read the experts the router needs" and "A
+ * drafter that leaves the answer unchanged").  Every
  * argument means what it means there, with E = W->n_routed and d = W->d, and
  * every output (logits when computed, topk_ids, topk_w, the bucketing
  * arrays, dev_error, y_slots, out) is bit-identical to what those four calls
@@ -195,10 +196,11 @@ int moe_layer_mxfp4(const void *x, moe_dtype x_dtype, const float *w_router, flo
                     void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
- * Expert streaming ("One GPU, three storage tiers": a device expert cache in
- * front of a pinned host pool; "Read the experts the router needs": a
- * device-cache hit computes at once, a host-pool hit is uploaded first on one
- * of several upload streams, and experts are computed as they arrive).
+ * Expert streaming ("One GPU, three storage tiers" and "Read the experts the
+ * router needs": a device expert cache in front of a pinned host pool).
+ * Experts in the device cache run immediately; the others are copied up from
+ * the host pool over several streams and computed group by group as the
+ * copies complete.
  * The disk tier of the pages is not modelled: the host pool holds every
  * expert of n_layers layers.
  *
@@ -208,8 +210,8 @@ int moe_layer_mxfp4(const void *x, moe_dtype x_dtype, const float *w_router, flo
  *   the rest (at least one)            cached experts, by (layer, expert)
  * Cache policy (also run on the host alone by moe_cache_simulate): the
  * experts of a call are taken in ascending id; those cached are hits.  With
- * admit_min_rows > 0 ("A drafter that leaves the answer unchanged": keep only
- * the experts that enough of a block's rows use), a miss used by fewer rows
+ * admit_min_rows > 0 (the row-count admission rule of "A drafter that leaves
+ * the answer unchanged"), a miss used by fewer rows
  * takes a transient slot while one is left.  Other misses are admitted into
  * the lowest free cached slot, else the least recently used cached slot
  * (lowest on equal age) not holding an expert of this call; with none left
@@ -269,9 +271,9 @@ int moe_cache_simulate(int32_t n_layers, int32_t n_routed, int32_t n_cache, int3
                        int32_t admit_min_rows, int32_t n_calls, const int32_t *call_layer, const int32_t *call_n,
                        const int32_t *experts, const int32_t *rows, int32_t *slot, int32_t *hit, int32_t *admitted);
 
-/* Q8_0 spine matmul ("A drafter that leaves the answer unchanged": the
- * spine's matrix multiplies load each weight once for up to eight rows;
- * "One GPU, three storage tiers": the spine's matrices are Q8_0):
+/* Q8_0 spine matmul ("A drafter that leaves the answer unchanged" and "One
+ * GPU, three storage tiers": the spine is stored as Q8_0, and a call with up
+ * to 8 rows reads each weight from HBM once rather than once per row):
  *   Y[m,n] = sum_c X[m,c] * Wq[n,c] * Ws[n, c/32]
  *   X  [M x K] fp32;  Wq [N x K] int8;  Ws [N x K/32] fp16 bit patterns;
  *   Y  [M x N] fp32 out.
@@ -292,12 +294,11 @@ int q8_0_matmul_layout(const float *X, int32_t M, int32_t K, const int8_t *Wq, c
 int q8_0_pack(const int8_t *src, int8_t *dst, int32_t N, int32_t K, moe_layout to_layout, void *stream);
 
 /* ------------------------------------------------------------------------
- * Block verification ("A drafter that leaves the answer unchanged": a block
- * of up to 16 rows, the current token plus drafts, runs the same arithmetic
- * as plain steps, and drafts are kept up to the first one the model
- * disagrees with; the run record compares FNV-1a hashes of every position's
- * logits between the paths, under greedy decoding).  Helpers of a harness
- * that stacks layers; every result is exact. */
+ * Block verification ("A drafter that leaves the answer unchanged" and the
+ * run record).  A harness over a stack of layers checks drafted tokens in one
+ * multi-row block: a draft is accepted while it equals the greedy choice,
+ * block rows must match one-row steps bit for bit, and every position's
+ * logits are FNV-1a hashed on both sides.  The helpers below are exact. */
 
 /* Rows of a Q8_0 matrix as fp32 (an embedding lookup):
  * X[m, c] = Wq[ids[m], c] * Ws[ids[m], c/32]; an id outside [0, N) gives a zero

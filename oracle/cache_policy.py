@@ -3,9 +3,9 @@
 TEST INFRASTRUCTURE ONLY, like the rest of ``oracle/``.  Written from
 "Run Kimi 3.1 locally on one GPU" (argonautlabs.ai): "One GPU, three storage
 tiers" (a device expert cache in front of a pinned host pool) and "A drafter
-that leaves the answer unchanged" (plain least-recently-used eviction got no
-hits for blocks touching more experts than the caches hold; keeping only the
-experts that enough of a block's rows use cut the reads).  The pages give no
+that leaves the answer unchanged" (LRU alone never hits once a block needs
+more experts than the cache has room for; admitting only experts with a
+minimum row count per block reduces the reads).  The pages give no
 slot-level rules; the ones below are this library's, stated in its header.
 
 Per call (one layer, its routed experts ascending, each with its row count):

@@ -8,13 +8,14 @@
  * GPU path: every value below is written out from its definition.
  *
  * Sources ("Run Kimi 3.1 locally on one GPU", argonautlabs.ai):
- *   - section "Read the experts the router needs": per MoE layer a router picks
- *     16 of 896 experts for each token;
- *   - section "A drafter that leaves the answer unchanged": a block of 1..16
- *     rows reads each expert once for all its rows, and a block's rows run the
- *     same arithmetic as plain steps;
- *   - section "One GPU, three storage tiers": experts are MXFP4 files of
- *     17,547,264 bytes; the spine's matrices are quantised to Q8_0.
+ *   - section "Read the experts the router needs": the Kimi layer routes each
+ *     token to k = 16 of its E = 896 experts;
+ *   - section "A drafter that leaves the answer unchanged": verification
+ *     blocks of up to 16 rows, whose per-row results must equal those of
+ *     one-row steps bit for bit (so each row's result here is computed on its
+ *     own, whatever block it sits in);
+ *   - section "One GPU, three storage tiers": each expert is an MXFP4 record
+ *     of 17,547,264 bytes, and the spine's matrices are stored as Q8_0.
  * The pages give neither the router function, the bit layout of MXFP4 or
  * Q8_0, nor any worked numeric example.  The readings used here (softmax,
  * top-k by logit with ties to the lower index, renormalised weights, SwiGLU

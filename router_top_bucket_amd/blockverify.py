@@ -1,12 +1,13 @@
 """Block verification over a stack of MoE layers ("A drafter that leaves the
 answer unchanged", "Run Kimi 3.1 locally on one GPU").
 
-The engine on the pages checks a proposal of drafted tokens in one block of up
-to 16 rows (the current token plus the drafts), keeps the drafts up to the
-first one the model disagrees with, and emits only the model's own greedy
-choices; a block reads each expert once for all its rows, and its rows run the
-same arithmetic as plain steps, checked by hashing every position's logits
-(FNV-1a) in both paths.
+The engine on the pages verifies drafted tokens in one multi-row pass (at
+most 16 rows: the token being decoded followed by the drafts).  A draft is
+accepted while it equals the model's greedy choice at its position; the
+output is always the model's own greedy sequence.  Experts are fetched once
+per block, and each block row must reproduce the one-row step exactly; the
+pages show this by FNV-1a hashing every position's logits on both sides,
+and this harness does the same.
 
 ``Stack`` is the harness's model: no attention, so a row depends only on its
 own token.  Per row, with h the fp32 residual stream and n(.) the RMS

@@ -1,7 +1,7 @@
-// Bucketing: stable counting sort of the M*(k+S) slots by expert, so each
-// expert's rows are found together and its weights are read once for all of
-// them ("A drafter that leaves the answer unchanged", "Run Kimi 3.1 locally on
-// one GPU").  One workgroup; every result is an integer and exact.
+// Bucketing: stable counting sort of the M*(k+S) slots by expert, so that
+// the slots of one expert are contiguous and the FFN can serve them all from
+// a single pass over that expert's weights ("Run Kimi 3.1 locally on one
+// GPU", section "A drafter that leaves the answer unchanged").  One workgroup; every result is an integer and exact.
 //
 // Stable rank without sorting: within a row the k routed experts and the S
 // shared experts are distinct, so the rank of slot (m, j) inside expert e's

@@ -1,9 +1,10 @@
-// Expert streaming from a pinned host pool into a device expert cache
-// ("One GPU, three storage tiers": a device expert cache and a pinned host
-// pool; "Read the experts the router needs": a device-cache hit computes at
-// once, a host-pool hit is uploaded first, uploads run on several streams and
-// experts are computed as they arrive).  The disk tier of the pages has no
-// counterpart here: the host pool holds every expert.
+// Expert streaming from a pinned host pool into a device expert cache ("Run
+// Kimi 3.1 locally on one GPU", sections "One GPU, three storage tiers" and
+// "Read the experts the router needs").  Experts found in the device cache
+// run immediately; the rest are copied up from the host pool over several
+// streams, and each group of copies is computed as soon as it lands.  The
+// disk tier of the pages has no counterpart here: the host pool holds every
+// expert.
 //
 // A call: route and bucket on the caller's stream, wait for the bucketing on
 // the host (the experts to fetch are known only then), plan slots

@@ -1,9 +1,10 @@
 // Which device-cache slot each expert of a call uses, and which experts are
-// kept there for later calls ("One GPU, three storage tiers": a device expert
-// cache in front of the host pool; "A drafter that leaves the answer
-// unchanged": with blocks touching more experts than the cache holds, plain
-// least-recently-used eviction got no hits, and keeping only the experts that
-// enough of the block's rows use cut the reads).  Host code only.
+// kept there for later calls ("Run Kimi 3.1 locally on one GPU", sections
+// "One GPU, three storage tiers" and "A drafter that leaves the answer
+// unchanged").  The pages report that LRU alone misses every time once a
+// block needs more experts than fit, and that admitting only experts with
+// a minimum number of rows in the block helps; admit_min_rows is that
+// threshold.  Host code only.
 //
 // Slots (numbered from 0 here; the device pool adds its own offset):
 //   [0, n_transient)                       transient: hold an expert for one

@@ -1,7 +1,8 @@
 // Expert FFN over bucketed slots: y = W_down (silu(W_gate x) * (W_up x)) with
-// MXFP4 weights, each expert's weights streamed once for all rows of its
-// bucket ("A drafter that leaves the answer unchanged", "Run Kimi 3.1 locally
-// on one GPU": a block reads each expert once for all its rows).
+// MXFP4 weights.  All slots of an expert are computed from one pass over its
+// weights, so a multi-row block costs one weight read per distinct expert
+// ("Run Kimi 3.1 locally on one GPU", section "A drafter that leaves the
+// answer unchanged").
 //
 // Work unit: a "group" = one expert and up to 16 of its slots (a bucket
 // segment of <= 16 positions of perm).  With M <= 16 rows every active expert

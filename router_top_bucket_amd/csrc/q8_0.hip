@@ -1,7 +1,8 @@
 // Q8_0 spine matmul Y[M x N] = X[M x K] . W^T, W stored as int8 [N x K] and
-// one fp16 scale per 32 consecutive K ("A drafter that leaves the answer
-// unchanged", "Run Kimi 3.1 locally on one GPU": the spine's matrix multiplies
-// load each weight once for up to eight rows).
+// one fp16 scale per 32 consecutive K.  Up to 8 rows of X share one pass
+// over W, so each weight byte leaves HBM once per call, not once per row
+// ("Run Kimi 3.1 locally on one GPU", sections "A drafter that leaves the
+// answer unchanged" and "One GPU, three storage tiers").
 //
 // Arithmetic (fixed for a given K and N, independent of M and of the launch
 // shape below): for output row n and X row m, each 32-block b contributes

@@ -1,6 +1,6 @@
 // Router: logits = x . W_r^T, then per row the top-k experts and their
-// renormalised softmax weights ("Read the experts the router needs", "Run
-// Kimi 3.1 locally on one GPU": the router picks 16 of 896 experts per token).
+// renormalised softmax weights ("Run Kimi 3.1 locally on one GPU", section
+// "Read the experts the router needs": k = 16 of E = 896 in the Kimi layer).
 #include "common.h"
 #include "launch.h"
 #include "topk.h"

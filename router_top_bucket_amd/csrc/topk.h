@@ -1,7 +1,7 @@
 // Top-k of one row of router logits in one wave, with the renormalised
-// softmax weights of the selected experts ("Read the experts the router
-// needs", "Run Kimi 3.1 locally on one GPU": the router picks 16 of 896
-// experts per token).  Shared by the top-k kernel and the fused
+// softmax weights of the selected experts ("Run Kimi 3.1 locally on one
+// GPU", section "Read the experts the router needs": k = 16 routed experts
+// out of E = 896 per token in the Kimi layer).  Shared by the top-k kernel and the fused
 // top-k + bucket kernel, so both give the same bits.
 //
 // The row's logits sit in registers (NPL per lane).  Each entry becomes a

@@ -1,9 +1,9 @@
-// Small kernels of the block-verification harness ("A drafter that leaves the
-// answer unchanged": a block of up to 16 rows runs the same arithmetic as
-// plain steps, drafts are kept up to the first one the model disagrees with,
-// and the logits of every position are hashed in both paths; "Run Kimi 3.1
-// locally on one GPU", run record: FNV-1a hashes of every position's logits,
-// greedy decoding).  The lookups, adds, casts, argmax and hashes are exact;
+// Small kernels of the block-verification harness ("Run Kimi 3.1 locally on
+// one GPU", section "A drafter that leaves the answer unchanged", and its run
+// record).  The harness compares a multi-row verification block with one-row
+// steps: block outputs must match bit for bit, a draft is accepted only while
+// it equals the greedy choice, and every position's logits are FNV-1a
+// hashed on both sides.  The lookups, adds, casts, argmax and hashes are exact;
 // the RMS normalisation is fp32 in an order fixed by the row length.
 #include "common.h"
 #include "launch.h"

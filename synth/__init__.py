@@ -7,7 +7,7 @@ numbers and packs them into the storage formats; it contains none of the
 layer's arithmetic (no dequantisation, routing, bucketing, FFN or combine).
 
 Workloads (shapes from "Run Kimi 3.1 locally on one GPU", argonautlabs.ai:
-16 of 896 experts per token, section "Read the experts the router needs";
+top-16 routing over 896 experts, section "Read the experts the router needs";
 blocks of 2..16 rows, section "A drafter that leaves the answer unchanged";
 270- and 1,533-token prompt passes, section "Decode and prefill are different
 measurements"; 17,547,264-byte MXFP4 experts, section "One GPU, three storage

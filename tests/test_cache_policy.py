@@ -1,7 +1,7 @@
-"""The device expert cache's policy ("One GPU, three storage tiers"; "A
-drafter that leaves the answer unchanged": plain LRU got no hits for blocks
-wider than the cache, keeping only the experts that enough of a block's rows
-use helped).  The reference in oracle/cache_policy.py is pinned to closed
+"""The device expert cache's policy ("Run Kimi 3.1 locally on one GPU",
+sections "One GPU, three storage tiers" and "A drafter that leaves the answer
+unchanged": with blocks wider than the cache LRU never hits, and a row-count
+threshold for admission helps).  The reference in oracle/cache_policy.py is pinned to closed
 forms first, then the library's policy (moe_cache_simulate, host code only,
 no device call) must match it decision for decision on random traces."""
 import numpy as np

@@ -1,7 +1,8 @@
 """GPU parity: every C-ABI call against the CPU oracle on the same seeded
-inputs, plus the pages' invariants on the GPU path ("A drafter that leaves
-the answer unchanged": block rows equal plain steps bit for bit; outputs are
-unchanged by the order experts are computed in).  Needs an MI355X."""
+inputs, plus the pages' invariants on the GPU path ("Run Kimi 3.1 locally on
+one GPU", section "A drafter that leaves the answer unchanged": a row's
+results inside a multi-row block are bit-identical to a one-row call, and do
+not depend on the order in which experts are computed).  Needs an MI355X."""
 import numpy as np
 import pytest
 
@@ -439,7 +440,7 @@ def _row_outputs(res, m, k, S):
 
 @pytest.mark.parametrize("B", [2, 8, 16])
 def test_kimi_block_rows_equal_single_rows(kimi_layer, B):
-    """Block rows run the same arithmetic as plain steps: bit-identical."""
+    """Every row of a block is bit-identical to the same row called alone."""
     moe = _moe()
     L = kimi_layer
     shp = L["shape"]
