@@ -2,8 +2,18 @@
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by the
 benchmark's CPU-baseline leg, never by the product package.  The arithmetic
-lives in ``oracle.c`` (plain C, fp64 accumulation, one thread per output
-element); this module only marshals numpy arrays through ctypes.
+lives in ``oracle.c`` (plain C, one thread per output element); this module
+only marshals numpy arrays through ctypes.
+
+Two accumulation readings, chosen per call with ``accum``:
+  "f64" (default) every sum in double precision, rounded once when stored;
+  "f32" every sum in fp32, a reduction over K as ascending 32-element blocks
+        (terms added one by one inside a block, then the block partials in
+        order), silu and the softmax with the fp32 expf.
+The layer's tolerance is stated against an fp32-accumulating reference; the
+fp64 reading is the stricter one (its only rounding is the final store) and
+is the one the parity tests use.  A CPU test checks that the two agree far
+inside that tolerance at the Kimi shape.
 
 Each function names the passage of "Run Kimi 3.1 locally on one GPU"
 (argonautlabs.ai) it follows in ``oracle.c``.
@@ -42,6 +52,11 @@ def _load():
             "orc_expert_ffn": (ctypes.c_int, [P, i32, P, i32, i32, P]),
             "orc_combine": (ctypes.c_int, [P, P, i32, i32, i32, i32, P]),
             "orc_q8_0_matmul": (ctypes.c_int, [P, i32, i32, P, P, i32, P]),
+            "orc_router_logits_f32": (ctypes.c_int, [P, P, i32, i32, i32, P]),
+            "orc_topk_f32": (ctypes.c_int, [P, i32, i32, i32, P, P]),
+            "orc_expert_ffn_f32": (ctypes.c_int, [P, i32, P, i32, i32, P]),
+            "orc_combine_f32": (ctypes.c_int, [P, P, i32, i32, i32, i32, P]),
+            "orc_q8_0_matmul_f32": (ctypes.c_int, [P, i32, i32, P, P, i32, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(lib, name)
@@ -59,6 +74,13 @@ def _ptr(a: np.ndarray):
 def _check(rc: int, what: str):
     if rc != 0:
         raise ValueError(f"oracle {what}: invalid arguments (rc={rc})")
+
+
+def _fn(name: str, accum: str):
+    """The C function of one step for an accumulation reading."""
+    if accum not in ("f64", "f32"):
+        raise ValueError(f"accum must be 'f64' or 'f32', not {accum!r}")
+    return getattr(_load(), name + ("_f32" if accum == "f32" else ""))
 
 
 # --------------------------------------------------------------------------- formats
@@ -116,25 +138,26 @@ def as_f32_rows(x: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(x, dtype=np.float32)
 
 
-def router_logits(x: np.ndarray, w_r: np.ndarray) -> np.ndarray:
-    """logits[M x E] = x[M x d] . W_r[E x d]^T, fp64 sums rounded to fp32."""
+def router_logits(x: np.ndarray, w_r: np.ndarray, accum: str = "f64") -> np.ndarray:
+    """logits[M x E] = x[M x d] . W_r[E x d]^T, rounded to fp32 ("Run Kimi 3.1
+    locally on one GPU", section "Read the experts the router needs")."""
     xf = as_f32_rows(x)
     w_r = np.ascontiguousarray(w_r, dtype=np.float32)
     M, d = xf.shape
     E = w_r.shape[0]
     out = np.empty((M, E), dtype=np.float32)
-    _check(_load().orc_router_logits(_ptr(xf), _ptr(w_r), M, d, E, _ptr(out)), "router_logits")
+    _check(_fn("orc_router_logits", accum)(_ptr(xf), _ptr(w_r), M, d, E, _ptr(out)), "router_logits")
     return out
 
 
-def topk(logits: np.ndarray, k: int) -> tuple[np.ndarray, np.ndarray]:
+def topk(logits: np.ndarray, k: int, accum: str = "f64") -> tuple[np.ndarray, np.ndarray]:
     """Top-k expert ids (rank order; ties to the lower index; NaN last) and
     renormalised softmax weights, per row."""
     logits = np.ascontiguousarray(logits, dtype=np.float32)
     M, E = logits.shape
     ids = np.empty((M, k), dtype=np.int32)
     w = np.empty((M, k), dtype=np.float32)
-    _check(_load().orc_topk(_ptr(logits), M, E, k, _ptr(ids), _ptr(w)), "topk")
+    _check(_fn("orc_topk", accum)(_ptr(logits), M, E, k, _ptr(ids), _ptr(w)), "topk")
     return ids, w
 
 
@@ -154,7 +177,7 @@ def bucket(ids: np.ndarray, E: int, n_shared: int):
     return offsets, perm[: M * (k + n_shared)], active[:n].copy(), n
 
 
-def expert_ffn(x_rows: np.ndarray, expert: np.ndarray, d: int, f: int) -> np.ndarray:
+def expert_ffn(x_rows: np.ndarray, expert: np.ndarray, d: int, f: int, accum: str = "f64") -> np.ndarray:
     """SwiGLU expert y = W_down (silu(W_gate x) * (W_up x)) for each row of
     x_rows [n x d] (float32 or bfloat16 bits) through one expert record."""
     xf = as_f32_rows(np.atleast_2d(x_rows))
@@ -162,11 +185,11 @@ def expert_ffn(x_rows: np.ndarray, expert: np.ndarray, d: int, f: int) -> np.nda
     n = xf.shape[0]
     assert xf.shape[1] == d and expert.size >= expert_layout(d, f)[6]
     y = np.empty((n, d), dtype=np.float32)
-    _check(_load().orc_expert_ffn(_ptr(xf), n, _ptr(expert), d, f, _ptr(y)), "expert_ffn")
+    _check(_fn("orc_expert_ffn", accum)(_ptr(xf), n, _ptr(expert), d, f, _ptr(y)), "expert_ffn")
     return y
 
 
-def combine(y_slots: np.ndarray, w: np.ndarray, k: int, n_shared: int) -> np.ndarray:
+def combine(y_slots: np.ndarray, w: np.ndarray, k: int, n_shared: int, accum: str = "f64") -> np.ndarray:
     """out[m] = sum_j w[m,j] y[m,j] + sum_s y_shared[m,s]."""
     y_slots = np.ascontiguousarray(y_slots, dtype=np.float32)
     w = np.ascontiguousarray(w, dtype=np.float32)
@@ -174,11 +197,11 @@ def combine(y_slots: np.ndarray, w: np.ndarray, k: int, n_shared: int) -> np.nda
     d = y_slots.shape[-1]
     assert y_slots.size == M * (k + n_shared) * d
     out = np.empty((M, d), dtype=np.float32)
-    _check(_load().orc_combine(_ptr(y_slots), _ptr(w), M, k, n_shared, d, _ptr(out)), "combine")
+    _check(_fn("orc_combine", accum)(_ptr(y_slots), _ptr(w), M, k, n_shared, d, _ptr(out)), "combine")
     return out
 
 
-def q8_0_matmul(X: np.ndarray, wq: np.ndarray, ws: np.ndarray) -> np.ndarray:
+def q8_0_matmul(X: np.ndarray, wq: np.ndarray, ws: np.ndarray, accum: str = "f64") -> np.ndarray:
     """Y[M x N] = X[M x K] . W^T with W in Q8_0 (int8 plane, fp16 scale per 32)."""
     X = np.ascontiguousarray(X, dtype=np.float32)
     wq = np.ascontiguousarray(wq, dtype=np.int8)
@@ -187,12 +210,12 @@ def q8_0_matmul(X: np.ndarray, wq: np.ndarray, ws: np.ndarray) -> np.ndarray:
     N = wq.shape[0]
     assert wq.shape == (N, K) and ws.shape == (N, K // 32)
     Y = np.empty((M, N), dtype=np.float32)
-    _check(_load().orc_q8_0_matmul(_ptr(X), M, K, _ptr(wq), _ptr(ws), N, _ptr(Y)), "q8_0_matmul")
+    _check(_fn("orc_q8_0_matmul", accum)(_ptr(X), M, K, _ptr(wq), _ptr(ws), N, _ptr(Y)), "q8_0_matmul")
     return Y
 
 
 def layer(x: np.ndarray, k: int, n_routed: int, n_shared: int, d: int, f: int, expert_bytes,
-          w_r: np.ndarray | None = None, logits: np.ndarray | None = None):
+          w_r: np.ndarray | None = None, logits: np.ndarray | None = None, accum: str = "f64"):
     """The whole MoE layer for rows x: router (or given logits) -> top-k ->
     every slot's expert FFN -> combine.  ``expert_bytes(e)`` returns expert e's
     record (shared expert s is e = n_routed + s).  Returns a dict of every
@@ -200,15 +223,15 @@ def layer(x: np.ndarray, k: int, n_routed: int, n_shared: int, d: int, f: int, e
     xf = as_f32_rows(np.atleast_2d(x))
     M = xf.shape[0]
     if logits is None:
-        logits = router_logits(xf, w_r)
-    ids, w = topk(logits, k)
+        logits = router_logits(xf, w_r, accum)
+    ids, w = topk(logits, k, accum)
     offsets, perm, active, n_active = bucket(ids, n_routed, n_shared)
     S = n_shared
     y_slots = np.zeros((M * (k + S), d), dtype=np.float32)
     for e in active:
         seg = perm[offsets[e]:offsets[e + 1]]
         rows = seg // (k + S)
-        y_slots[seg] = expert_ffn(xf[rows], expert_bytes(int(e)), d, f)
-    out = combine(y_slots, w, k, S)
+        y_slots[seg] = expert_ffn(xf[rows], expert_bytes(int(e)), d, f, accum)
+    out = combine(y_slots, w, k, S, accum)
     return dict(logits=logits, ids=ids, w=w, offsets=offsets, perm=perm, active=active, n_active=n_active,
                 y_slots=y_slots, out=out)

@@ -211,8 +211,8 @@ int orc_topk(const float *logits, int32_t M, int32_t E, int32_t k, int32_t *ids,
 
 /* Slots t = m*(k+S)+j of M rows: j<k is routed expert ids[m,j]; j>=k is shared
  * expert E+(j-k), applied to every row.  Group the slots by expert so that
- * each expert's rows are found together (the block "reads each expert once
- * for all its rows"): offsets[e]..offsets[e+1] is expert e's segment of perm,
+ * each expert's slots are contiguous (so one pass over its weights can serve
+ * all of them): offsets[e]..offsets[e+1] is expert e's segment of perm,
  * perm lists slot indices ordered by (expert, slot), active lists the experts
  * with a nonempty segment in ascending order.  Returns ORC_EINVAL (and writes
  * nothing) when an id is outside [0,E). */
@@ -333,6 +333,157 @@ int orc_q8_0_matmul(const float *X, int32_t M, int32_t K, const int8_t *wq, cons
     for (int64_t c = 0; c < K; ++c)
       s += (double)X[m * K + c] * ((double)wq[n * K + c] * orc_fp16(ws[n * (K / 32) + c / 32]));
     Y[i] = (float)s;
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* fp32-accumulation variants                                               */
+/* ------------------------------------------------------------------------ */
+/* The same definitions with every sum kept in fp32, in the order the layer's
+ * specification states for an fp32-accumulating reference: a reduction over K
+ * is cut into blocks of 32 consecutive indices; inside a block the terms are
+ * added one after another in fp32 (each product rounded to fp32, then the
+ * add), and the block partials are then added in ascending block order.
+ * silu and the routing softmax use the fp32 expf.  The fp64 functions above
+ * are the default reference (a tighter one: their only rounding is the final
+ * store); these exist so the two readings can be compared.  The product is
+ * compiled without contraction, so no multiply-add is fused. */
+
+static float blocked_dot_f32(const float *a, const float *b, int64_t K) {
+  float s = 0.0f;
+  for (int64_t c0 = 0; c0 < K; c0 += 32) {
+    float p = 0.0f;
+    int64_t c1 = c0 + 32 < K ? c0 + 32 : K;
+    for (int64_t c = c0; c < c1; ++c) {
+      float t = a[c] * b[c];
+      p = p + t;
+    }
+    s = s + p;
+  }
+  return s;
+}
+
+int orc_router_logits_f32(const float *x, const float *w_r, int32_t M, int32_t d, int32_t E, float *logits) {
+  if (M < 0 || d <= 0 || E <= 0) return ORC_EINVAL;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < (int64_t)M * E; ++i) {
+    int64_t m = i / E, e = i % E;
+    logits[i] = blocked_dot_f32(w_r + e * d, x + m * d, d);
+  }
+  return ORC_OK;
+}
+
+/* Top-k as orc_topk (same selection); weights w_j = expf(l_j - l_0) /
+ * sum_{i<k} expf(l_i - l_0) in fp32 with l_0 the top logit, the normaliser
+ * summed in rank order.  NaN logits are never selected before a number. */
+int orc_topk_f32(const float *logits, int32_t M, int32_t E, int32_t k, int32_t *ids, float *w) {
+  if (M < 0 || E <= 0 || k < 1 || k > E) return ORC_EINVAL;
+  int err = 0;
+#pragma omp parallel for schedule(static) reduction(| : err)
+  for (int64_t m = 0; m < M; ++m) {
+    const float *row = logits + m * E;
+    int32_t *id = ids + m * k;
+    char *taken = (char *)calloc((size_t)E, 1);
+    if (!taken) { err |= 1; continue; }
+    for (int j = 0; j < k; ++j) {
+      int best = -1;
+      for (int e = 0; e < E; ++e)
+        if (!taken[e] && (best < 0 || ranks_before(row, e, best))) best = e;
+      taken[best] = 1;
+      id[j] = best;
+    }
+    float l0 = row[id[0]];
+    float z = 0.0f;
+    for (int j = 0; j < k; ++j) z = z + expf(row[id[j]] - l0);
+    for (int j = 0; j < k; ++j) w[m * k + j] = expf(row[id[j]] - l0) / z;
+    free(taken);
+  }
+  return err ? ORC_EINVAL : ORC_OK;
+}
+
+/* One row of an MXFP4 matrix decoded to fp32 (exact: E2M1 times a power of
+ * two fits in fp32). */
+static void mx_row_f32(const uint8_t *codes, const uint8_t *scales, int64_t K, int64_t r, float *out) {
+  for (int64_t c = 0; c < K; ++c) out[c] = (float)mx_elem(codes, scales, K, r, c);
+}
+
+int orc_expert_ffn_f32(const float *x, int32_t nrows, const uint8_t *expert, int32_t d, int32_t f, float *y) {
+  int64_t off[7];
+  if (nrows < 0 || orc_expert_layout(d, f, off)) return ORC_EINVAL;
+  if (nrows == 0) return ORC_OK;
+  const uint8_t *gc = expert + off[0], *gs = expert + off[1];
+  const uint8_t *uc = expert + off[2], *us = expert + off[3];
+  const uint8_t *dc = expert + off[4], *ds = expert + off[5];
+  float *h = (float *)malloc(sizeof(float) * (size_t)f * (size_t)nrows);
+  if (!h) return ORC_EINVAL;
+  int err = 0;
+#pragma omp parallel for schedule(static) reduction(| : err)
+  for (int64_t i = 0; i < f; ++i) {
+    float *wg = (float *)malloc(sizeof(float) * (size_t)d * 2);
+    if (!wg) { err |= 1; continue; }
+    float *wu = wg + d;
+    mx_row_f32(gc, gs, d, i, wg);
+    mx_row_f32(uc, us, d, i, wu);
+    for (int64_t n = 0; n < nrows; ++n) {
+      float g = blocked_dot_f32(wg, x + n * d, d);
+      float u = blocked_dot_f32(wu, x + n * d, d);
+      float sg = g / (1.0f + expf(-g));
+      h[n * f + i] = sg * u;
+    }
+    free(wg);
+  }
+  if (err) { free(h); return ORC_EINVAL; }
+#pragma omp parallel for schedule(static) reduction(| : err)
+  for (int64_t r = 0; r < d; ++r) {
+    float *wd = (float *)malloc(sizeof(float) * (size_t)f);
+    if (!wd) { err |= 1; continue; }
+    mx_row_f32(dc, ds, f, r, wd);
+    for (int64_t n = 0; n < nrows; ++n) y[n * d + r] = blocked_dot_f32(wd, h + n * f, f);
+    free(wd);
+  }
+  free(h);
+  return err ? ORC_EINVAL : ORC_OK;
+}
+
+/* Combine in fp32, one term after another in slot order: routed slots as
+ * w * y (product rounded, then the add), shared slots added as they are. */
+int orc_combine_f32(const float *y_slots, const float *w, int32_t M, int32_t k, int32_t S, int32_t d, float *out) {
+  if (M < 0 || k < 1 || S < 0 || d <= 0) return ORC_EINVAL;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < (int64_t)M * d; ++i) {
+    int64_t m = i / d, r = i % d;
+    float s = 0.0f;
+    for (int64_t j = 0; j < k; ++j) {
+      float t = w[m * k + j] * y_slots[(m * (k + S) + j) * d + r];
+      s = s + t;
+    }
+    for (int64_t j = 0; j < S; ++j) s = s + y_slots[(m * (k + S) + k + j) * d + r];
+    out[i] = s;
+  }
+  return ORC_OK;
+}
+
+/* Q8_0 in fp32: per 32-block b the sum of q[n,c] * X[m,c] over the block in
+ * order, times the block's scale, the blocks added in ascending order. */
+int orc_q8_0_matmul_f32(const float *X, int32_t M, int32_t K, const int8_t *wq, const uint16_t *ws, int32_t N,
+                        float *Y) {
+  if (M < 0 || K <= 0 || K % 32 || N <= 0) return ORC_EINVAL;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < (int64_t)M * N; ++i) {
+    int64_t m = i / N, n = i % N;
+    float s = 0.0f;
+    for (int64_t b = 0; b < K / 32; ++b) {
+      float p = 0.0f;
+      for (int64_t c = 32 * b; c < 32 * b + 32; ++c) {
+        float t = (float)wq[n * K + c] * X[m * K + c];
+        p = p + t;
+      }
+      float sb = (float)orc_fp16(ws[n * (K / 32) + b]);
+      float t = sb * p;
+      s = s + t;
+    }
+    Y[i] = s;
   }
   return ORC_OK;
 }

@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import synth
-from conftest import ROOT, make_expert, read_golden
+from conftest import ROOT, make_expert, read_golden, rel_l2
 
 
 # ----------------------------------------------------------------------------- formats
@@ -432,3 +432,127 @@ def test_oracle_thread_count_invariance():
         outs.append(subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
                                    check=True).stdout)
     assert outs[0] == outs[1] and len(outs[0]) > 0
+
+
+# ----------------------------------------------------------------------------- fp32-accumulation reading
+# The oracle's second reading keeps every sum in fp32: a K reduction is cut
+# into ascending 32-element blocks, terms added one by one inside a block and
+# the block partials then added in order.  Pinned by closed forms that hold in
+# any fp32 order, by cases whose result only that order produces, and by its
+# agreement with the fp64 reading at the Kimi shape.
+def test_f32_router_closed_forms():
+    E, d, M = 7, 64, 3
+    w = np.zeros((E, d), dtype=np.float32)
+    for e in range(E):
+        w[e, 3 * e + 1] = 1.0
+    x = synth.rng(21, 1).standard_normal((M, d)).astype(np.float32)
+    assert np.array_equal(oracle.router_logits(x, w, accum="f32"), x[:, 1::3][:, :E])
+    g = synth.rng(21, 2)
+    xi = g.integers(-8, 9, size=(4, 96)).astype(np.float32)
+    wi = g.integers(-8, 9, size=(9, 96)).astype(np.float32)
+    ref = xi.astype(np.int64) @ wi.astype(np.int64).T
+    assert np.array_equal(oracle.router_logits(xi, wi, accum="f32"), ref.astype(np.float32))
+
+
+def test_f32_router_block_order():
+    # 2^24 + 1 rounds back to 2^24 in fp32 (ties to even).  One big term ahead
+    # of 31 ones inside a block swallows them one by one; the same ones
+    # summed in an earlier block arrive as one partial of 31 and survive.
+    d = 64
+    w = np.ones((2, d), np.float32)
+    x = np.zeros((2, d), np.float32)
+    x[0, 0], x[0, 1:32] = 2.0 ** 24, 1.0      # big term first, in block 0
+    x[1, 0:31], x[1, 32] = 1.0, 2.0 ** 24     # ones in block 0, big term in block 1
+    lg = oracle.router_logits(x, w[:1], accum="f32")
+    assert lg[0, 0] == np.float32(2.0 ** 24)
+    assert lg[1, 0] == np.float32(2.0 ** 24 + 32)    # 2^24 + 31 rounds to even
+    lg64 = oracle.router_logits(x, w[:1])
+    assert lg64[0, 0] == np.float32(2.0 ** 24 + 32)  # fp64 reading: exact sum, rounded once
+
+
+def test_f32_topk_weights_closed_forms():
+    g = synth.rng(22, 1)
+    lg = g.standard_normal((5, 40)).astype(np.float32)
+    ids, w = oracle.topk(lg, 1, accum="f32")
+    assert np.all(w == 1.0)
+    eq = np.full((2, 12), 0.375, np.float32)
+    ids, w = oracle.topk(eq, 4, accum="f32")
+    assert np.array_equal(ids, [[0, 1, 2, 3]] * 2) and np.all(w == np.float32(0.25))
+    ids64, _ = oracle.topk(lg, 6)
+    ids32, w32 = oracle.topk(lg, 6, accum="f32")
+    assert np.array_equal(ids32, ids64)  # the selection does not depend on the reading
+    assert np.allclose(w32.sum(1), 1.0, rtol=0, atol=6 * 2.0 ** -23)
+
+
+def test_f32_ffn_closed_forms():
+    x = synth.rng(23, 1).standard_normal((2, D)).astype(np.float32)
+    assert np.all(oracle.expert_ffn(x, make_expert(D, F), D, F, accum="f32") == 0)
+    for (i0, c0, c1, r0) in [(0, 0, 1, 0), (F - 1, D - 1, D - 2, D - 1), (5, 33, 40, 17)]:
+        rec = make_expert(D, F, gate=[(i0, c0, 5, 126)], up=[(i0, c1, 11, 128)], down=[(r0, i0, 7, 125)])
+        xx = synth.rng(24, i0).standard_normal((1, D)).astype(np.float32)
+        y = oracle.expert_ffn(xx, rec, D, F, accum="f32")
+        g_, u_ = 1.5 * float(xx[0, c0]), -3.0 * float(xx[0, c1])
+        ref = 1.5 * (g_ * _sigmoid(g_)) * u_
+        assert abs(float(y[0, r0]) - ref) <= abs(ref) * 2 ** -20  # fp32 expf, divide and products
+        mask = np.ones(D, bool)
+        mask[r0] = False
+        assert np.all(y[0, mask] == 0)
+    # gate and up are not interchangeable; down scales are linear
+    rec = make_expert(D, F, up=[(3, 4, 7, 127)], down=[(9, 3, 2, 127)])
+    assert np.all(oracle.expert_ffn(np.ones((1, D), np.float32), rec, D, F, accum="f32") == 0)
+    shp = synth.LayerShape("t", D, F, 1, 0, 1, -6, -2, 0.05, "f32")
+    rec = synth.expert_record(shp, 3, 0)
+    y = oracle.expert_ffn(x, rec, D, F, accum="f32")
+    rec2 = rec.copy()
+    off = oracle.expert_layout(D, F)
+    rec2[off[5]:off[6]] += 1
+    assert np.array_equal(oracle.expert_ffn(x, rec2, D, F, accum="f32"), 2 * y)
+
+
+def test_f32_combine_and_q8_0_closed_forms():
+    M, k, S, d = 4, 16, 2, 32
+    g = synth.rng(25, 1)
+    y = g.integers(-50, 51, size=(M * (k + S), d)).astype(np.float32)
+    w = (2.0 ** -g.integers(0, 6, size=(M, k))).astype(np.float32)
+    yy = y.reshape(M, k + S, d).astype(np.float64)
+    ref = (yy[:, :k] * w[:, :, None]).sum(1) + yy[:, k:].sum(1)
+    assert np.array_equal(oracle.combine(y, w, k, S, accum="f32"), ref.astype(np.float32))
+    Mq, K, N = 4, 128, 24
+    X = g.integers(-20, 21, size=(Mq, K)).astype(np.float32)
+    wq = g.integers(-127, 128, size=(N, K), dtype=np.int8)
+    e = g.integers(-6, 1, size=(N, K // 32))
+    ws = (2.0 ** e).astype(np.float16).view(np.uint16)
+    scale = np.repeat(2.0 ** e, 32, axis=1)
+    Wint = (wq.astype(np.int64) * (scale * 64).astype(np.int64))
+    refq = (X.astype(np.int64) @ Wint.T).astype(np.float64) / 64
+    assert np.array_equal(oracle.q8_0_matmul(X, wq, ws, accum="f32"), refq.astype(np.float32))
+    # block order: a scaled partial of 2^24 ahead of a block of small terms
+    X2 = np.zeros((1, 64), np.float32)
+    X2[0, 0] = 2.0 ** 17          # 127 * 2^17 = 16,646,144 in block 0
+    X2[0, 32:63] = 1.0            # 31 ones in block 1
+    wq2 = np.ones((1, 64), np.int8)
+    wq2[0, 0] = 127
+    ws2 = np.full((1, 2), np.float16(1.0).view(np.uint16), np.uint16)
+    assert oracle.q8_0_matmul(X2, wq2, ws2, accum="f32")[0, 0] == np.float32(127 * 2 ** 17 + 31)
+
+
+def test_f32_and_f64_readings_agree_at_kimi_shape():
+    """The two readings differ far below the layer's 1e-5 bar: the fp64 one
+    may serve as the reference for a tolerance stated against fp32."""
+    shp = synth.KIMI
+    x = synth.block_x(shp, 3, 2)
+    xf = oracle.as_f32_rows(x)
+    wr = synth.router_weight(shp, 0)
+    l64, l32 = oracle.router_logits(xf, wr), oracle.router_logits(xf, wr, accum="f32")
+    assert rel_l2(l32, l64) <= 1e-6
+    ids, w64 = oracle.topk(l64, shp.k)
+    assert rel_l2(oracle.topk(l64, shp.k, accum="f32")[1], w64) <= 1e-6
+    ys64, ys32 = [], []
+    for e in (int(ids[0, 0]), shp.n_routed):  # one routed and one shared expert
+        rec = synth.expert_record(shp, 0, e)
+        y64, y32 = oracle.expert_ffn(xf, rec, shp.d, shp.f), oracle.expert_ffn(xf, rec, shp.d, shp.f, accum="f32")
+        assert rel_l2(y32, y64) <= 1e-6, e
+        ys64.append(y64)
+        ys32.append(y32)
+    X, (wq, ws) = synth.q8_0_x(4, 1, 7168), synth.q8_0_weight(4, 7168, 2048)
+    assert rel_l2(oracle.q8_0_matmul(X, wq, ws, accum="f32"), oracle.q8_0_matmul(X, wq, ws)) <= 1e-6
