@@ -35,11 +35,15 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, published
 N_LAYERS = 4  # distinct resident layers the steps rotate through
+BLOCK_SIGMA = 0.3  # spread of a verification block's rows around row 0
 # rocprofv3 counter summary of the gate/up kernel on the 1-row workload; its
 # traffic figure is used only while the kernel sources are the ones it was
 # measured on
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "ffn_gateup_kimi_decode_1row_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "router_top_bucket_amd", "csrc", n) for n in ("ffn.hip", "common.h")]
+# every kernel source of a layer pass (the layer traffic figure's validity)
+LAYER_SOURCES = [os.path.join(ROOT, "router_top_bucket_amd", "csrc", n)
+                 for n in ("ffn.hip", "common.h", "route.hip", "bucket.hip", "topk.h")]
 
 
 def log(*a):
@@ -60,12 +64,32 @@ def parse():
     return p.parse_args()
 
 
-def kernel_sources_sha() -> str:
+def kernel_sources_sha(paths=None) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in (KERNEL_SOURCES if paths is None else paths):
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
+
+
+def traffic_layer():
+    """HBM bytes per 1-row layer pass from the committed counter summary of
+    every kernel of the pass, or None when absent or taken on other sources."""
+    path = os.path.join(ROOT, "profiles", "moe_kernels_kimi_decode_1row_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_sources_sha256") != kernel_sources_sha(LAYER_SOURCES):
+        return None
+    try:
+        return float(kv["layer_traffic_bytes"])
+    except (KeyError, ValueError):
+        return None
 
 
 def measured_traffic():
@@ -85,6 +109,13 @@ def measured_traffic():
         return float(kv["traffic_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def layer_bytes(shp, M, n_active, router):
+    """Algorithmic HBM bytes of one layer pass over M rows: every distinct
+    expert record read once, the fp32 router matrix once (when the logits are
+    computed), bf16 x in and fp32 output rows out."""
+    return n_active * shp.stride + (shp.n_routed * shp.d * 4 if router else 0) + M * shp.d * 2 + M * shp.d * 4
 
 
 class Timer:
@@ -288,6 +319,162 @@ def page_context(results):
     return out
 
 
+def cpu_info():
+    """The host's CPU model and the CPUs this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count()
+    return {"cpu_model": model, "cpus_available": avail, "logical_cpus": os.cpu_count()}
+
+
+def run_cpu_baseline(args, synth, shp, results):
+    """The oracle (the plain C reference, fp64 accumulation, OpenMP over
+    output elements) timed on this host's cores on bounded samples of each
+    workload, each figure placed beside the GPU figure it matches; the
+    headline object is the 1-row layer.  Expert records are generated before
+    any clock starts."""
+    import numpy as np
+
+    import oracle
+
+    threads = oracle.max_threads()
+    info = cpu_info()
+    seed = 0
+    wr_h = synth.router_weight(shp, seed)
+    cache = {}
+
+    def rec(e):
+        if e not in cache:
+            cache[e] = synth.expert_record(shp, seed, e)
+        return cache[e]
+
+    def prepare(x, logits=None):
+        lg = oracle.router_logits(x, wr_h) if logits is None else logits
+        ids, _ = oracle.topk(lg, shp.k)
+        for e in set(ids.ravel().tolist()) | {shp.n_routed + s for s in range(shp.n_shared)}:
+            rec(e)
+
+    def layer(x, logits=None):
+        if logits is None:
+            return oracle.layer(x, shp.k, shp.n_routed, shp.n_shared, shp.d, shp.f, rec, w_r=wr_h)
+        return oracle.layer(x, shp.k, shp.n_routed, shp.n_shared, shp.d, shp.f, rec, logits=logits)
+
+    def clock(fn, nthreads=threads):
+        oracle.set_threads(nthreads)
+        t = time.perf_counter()
+        fn()
+        dt = time.perf_counter() - t
+        oracle.set_threads(threads)
+        return dt
+
+    def attach(name, fig):
+        if name in results:
+            results[name]["cpu_oracle"] = fig
+
+    # headline: rows of the 1-row layer, one layer call per row
+    nrows = args.cpu_sample_rows
+    xh = synth.rows_x(shp, 1000, nrows)
+    prepare(xh)
+    dt = clock(lambda: [layer(xh[m:m + 1]) for m in range(nrows)])
+    dt1 = clock(lambda: layer(xh[:1]), 1)
+    attach("decode_1row", {"rows_per_s": nrows / dt, "threads": threads, "seconds": dt, "sample": f"{nrows} rows",
+                           "rows_per_s_1thread": 1 / dt1})
+    log(f"[bench] cpu oracle 1-row layer: {nrows / dt:.3f} rows/s on {threads} threads, {1 / dt1:.3f} on 1")
+    headline = {"value": nrows / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
+                "sample": f"{nrows} rows of the 1-row Kimi layer, one layer call per row (router + top-16 + 18 expert "
+                          f"FFNs + combine), C oracle with fp64 accumulation, {dt:.1f} s on {threads} OpenMP threads",
+                "cpu": info, "rows_per_s_1thread": 1 / dt1}
+
+    # the tiny layer (20 rows, one call per row), N threads and 1 thread
+    tshp = synth.TINY
+    trecs = {e: synth.expert_record(tshp, 0, e) for e in range(tshp.n_experts)}
+    twr = synth.router_weight(tshp, 0)
+    tx = synth.rows_x(tshp, 0, 20)
+
+    def tiny():
+        for m in range(20):
+            oracle.layer(tx[m:m + 1], tshp.k, tshp.n_routed, 0, tshp.d, tshp.f, trecs.__getitem__, w_r=twr)
+
+    tn, t1 = clock(tiny), clock(tiny, 1)
+    headline["tiny_layer_rows_per_s"] = 20 / tn
+    headline["tiny_layer_rows_per_s_1thread"] = 20 / t1
+
+    # verification blocks: one block per workload
+    for name, B, sigma in (("block_16rows", 16, BLOCK_SIGMA), ("block_2rows", 2, BLOCK_SIGMA),
+                           ("block_8rows", 8, BLOCK_SIGMA), ("block_16rows_sigma0.5", 16, 0.5),
+                           ("block_16rows_sigma1", 16, 1.0)):
+        if name not in results:
+            continue
+        xb = synth.block_x(shp, 0, B, sigma=sigma)
+        prepare(xb)
+        dtb = clock(lambda: layer(xb))
+        attach(name, {"rows_per_s": B / dtb, "threads": threads, "seconds": dtb, "sample": "1 block (seed 0)"})
+        log(f"[bench] cpu oracle {name}: {B / dtb:.2f} rows/s")
+
+    # prefill: routing, bucketing and combine in full; the expert FFNs timed
+    # on 8 experts spread over the popularity range, each with all its rows,
+    # and extrapolated to every active expert with t = a + b * rows
+    for Mp in (1533, 270):
+        name = f"prefill_{Mp}rows"
+        if name not in results:
+            continue
+        xp = oracle.as_f32_rows(synth.rows_x(shp, 2000, Mp))
+        lgp = synth.zipf_logits(shp, 2000, Mp)
+        kps = shp.k + shp.n_shared
+        t0 = time.perf_counter()
+        ids, wts = oracle.topk(lgp, shp.k)
+        off, perm, act, na = oracle.bucket(ids, shp.n_routed, shp.n_shared)
+        t_route = time.perf_counter() - t0
+        counts = np.diff(off)[act]
+        order = act[np.argsort(counts, kind="stable")]
+        pick = sorted(set(order[np.linspace(0, len(order) - 1, 8).astype(int)].tolist()))
+        xs_, ts_ = [], []
+        for e in pick:
+            seg = perm[off[e]:off[e + 1]]
+            rows = xp[seg // kps]
+            rec(int(e))
+            xs_.append(len(seg))
+            ts_.append(clock(lambda: oracle.expert_ffn(rows, rec(int(e)), shp.d, shp.f)))
+        b, a = np.polyfit(np.array(xs_, float), np.array(ts_, float), 1)
+        t_ffn = float(np.sum(a + b * counts))
+        y0 = np.zeros((Mp * kps, shp.d), np.float32)
+        t_comb = clock(lambda: oracle.combine(y0, wts, shp.k, shp.n_shared))
+        tot = t_route + t_ffn + t_comb
+        attach(name, {"rows_per_s": Mp / tot, "threads": threads, "seconds_estimated": tot,
+                      "sample": f"routing, bucketing and combine timed in full; the FFNs of 8 of the {na} active "
+                                f"experts timed with all their rows ({sum(xs_)} slots) and extrapolated linearly "
+                                f"in rows to all {int(counts.sum())} slots"})
+        log(f"[bench] cpu oracle {name}: {Mp / tot:.2f} rows/s (estimated {tot:.1f} s per layer)")
+
+    # Q8_0: up to 4096 output columns per shape, scaled to N (the work is
+    # linear in N); 1 thread at M = 1
+    if "q8_0" in results:
+        for (K, N) in synth.Q8_0_SHAPES:
+            ncol = min(N, 4096)
+            wq, ws = synth.q8_0_weight(3, K, ncol)
+            for Mq in (1, 2, 4, 8):
+                X = synth.q8_0_x(3, Mq, K)
+                dtq = clock(lambda: oracle.q8_0_matmul(X, wq, ws)) * N / ncol
+                fig = {"us": dtq * 1e6, "threads": threads, "sample": f"{ncol} of {N} columns, scaled"}
+                if Mq == 1:
+                    fig["us_1thread"] = clock(lambda: oracle.q8_0_matmul(X, wq, ws), 1) * N / ncol * 1e6
+                key = f"K{K}_N{N}_M{Mq}"
+                if key in results["q8_0"]:
+                    results["q8_0"][key]["cpu_oracle"] = fig
+        log("[bench] cpu oracle q8_0: done")
+    return headline
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -405,7 +592,8 @@ def main():
         # mean experts read per step over the steps timed
         na_mean = float(np.mean([na[i % P] for i in range(steps)]))
         del mls
-        return dict(eager_ms=eager_ms, graph_ms=graph_ms, gu_ms=gu_ms, ffn_ms=ffn_ms, n_active=na_mean)
+        return dict(eager_ms=eager_ms, graph_ms=graph_ms, gu_ms=gu_ms, ffn_ms=ffn_ms, n_active=na_mean,
+                    router=logits is None)
 
     def layer_result(M, r):
         ms = min(r["eager_ms"], r["graph_ms"]) if r["graph_ms"] is not None else r["eager_ms"]
@@ -414,9 +602,15 @@ def main():
         # weights once, x in (bf16), h out (fp32)
         gu_alg = r["n_active"] * gu_bytes_per_expert + M * shp.d * 2 + T * shp.f * 4
         eff = r["n_active"] * shp.stride / (ms / 1e3) / 1e9
+        # the layer's algorithmic bytes: each distinct expert's record once,
+        # the router matrix once when the logits are computed, x in and the
+        # output rows out
+        lay = layer_bytes(shp, M, r["n_active"], r["router"])
         return dict(rows=M, ms_per_layer=ms, ms_per_layer_eager=r["eager_ms"], ms_per_layer_graph=r["graph_ms"],
                     rows_per_s=M / (ms / 1e3), experts_read=r["n_active"], effective_weight_GBps=eff,
-                    hbm_frac_effective=eff / HBM_PEAK_GBS, gateup_us=r["gu_ms"] * 1e3,
+                    hbm_frac_effective=eff / HBM_PEAK_GBS, layer_alg_bytes=lay,
+                    layer_GBps=lay / (ms / 1e3) / 1e9, layer_hbm_frac=lay / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                    gateup_us=r["gu_ms"] * 1e3,
                     gateup_GBps=gu_alg / (r["gu_ms"] / 1e3) / 1e9, gateup_alg_bytes=gu_alg,
                     down_us_derived=(r["ffn_ms"] - r["gu_ms"]) * 1e3, ffn_us=r["ffn_ms"] * 1e3)
 
@@ -432,14 +626,20 @@ def main():
 
     # ------------------------------------------------------------ 16-row verification blocks
     if "block16" in only:
-        # blocks of 16 (the reported block) and of 2 and 8 rows
-        for B in (16, 2, 8):
-            xsb = [torch.from_numpy(synth.block_x(shp, s, B)).view(torch.bfloat16).to(dev) for s in range(20)]
-            res = layer_result(B, run_workload(B, xsb, None, max(40, args.steps // 4), 5, graphs=(B == 16)))
-            results[f"block_{B}rows"] = res
-            log(f"[bench] {B} rows: {res['ms_per_layer'] * 1e3:.1f} us/layer ({res['rows_per_s']:.0f} rows/s; eager "
-                f"{res['ms_per_layer_eager'] * 1e3:.1f} us), U+S={res['experts_read']:.1f}, gate/up "
-                f"{res['gateup_us']:.1f} us, ffn {res['ffn_us']:.1f} us")
+        # blocks of 16 (the reported block) and of 2 and 8 rows, rows spread
+        # around row 0 with sigma 0.3; then 16-row blocks with sigma 0.5 and
+        # 1.0, whose unions reach the upper end of the pages' 40-120 experts
+        for B, sigma in ((16, BLOCK_SIGMA), (2, BLOCK_SIGMA), (8, BLOCK_SIGMA), (16, 0.5), (16, 1.0)):
+            xsb = [torch.from_numpy(synth.block_x(shp, s, B, sigma=sigma)).view(torch.bfloat16).to(dev)
+                   for s in range(20)]
+            res = layer_result(B, run_workload(B, xsb, None, max(40, args.steps // 4), 5,
+                                               graphs=(B == 16 and sigma == BLOCK_SIGMA)))
+            res["sigma"] = sigma
+            name = f"block_{B}rows" + ("" if sigma == BLOCK_SIGMA else f"_sigma{sigma:g}")
+            results[name] = res
+            log(f"[bench] {B} rows, sigma {sigma:g}: {res['ms_per_layer'] * 1e3:.1f} us/layer "
+                f"({res['rows_per_s']:.0f} rows/s; eager {res['ms_per_layer_eager'] * 1e3:.1f} us), "
+                f"U+S={res['experts_read']:.1f}, gate/up {res['gateup_us']:.1f} us, ffn {res['ffn_us']:.1f} us")
 
     # ------------------------------------------------------------ prefill 1533 (and 270) rows
     if "prefill" in only:
@@ -502,42 +702,31 @@ def main():
     # ------------------------------------------------------------ CPU baseline: the oracle
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle
-
-        nrows = args.cpu_sample_rows
-        seed = 0  # layer 0's experts and router, the first decode batches
-        xh = synth.rows_x(shp, 1000, nrows)
-        wr_h = synth.router_weight(shp, seed)
-        cache = {}
-
-        def rec(e):
-            if e not in cache:
-                cache[e] = synth.expert_record(shp, seed, e)
-            return cache[e]
-
-        # records are generated before the clock starts: input preparation, not oracle work
-        lg = oracle.router_logits(xh, wr_h)
-        ids, _ = oracle.topk(lg, shp.k)
-        for e in set(ids.ravel().tolist()) | {shp.n_routed + s for s in range(shp.n_shared)}:
-            rec(e)
-        t1 = time.time()
-        for m in range(nrows):
-            oracle.layer(xh[m:m + 1], shp.k, shp.n_routed, shp.n_shared, shp.d, shp.f, rec, w_r=wr_h)
-        dt = time.time() - t1
-        threads = oracle.max_threads()
-        cpu = dict(value=nrows / dt, unit="rows/s", cores=threads, kind="oracle",
-                   sample=f"{nrows} rows of the 1-row Kimi layer, one layer call per row (router + top-16 + "
-                          f"18 expert FFNs + combine), C oracle with fp64 accumulation, {dt:.1f} s")
-        log(f"[bench] cpu oracle: {nrows / dt:.3f} rows/s on {threads} threads")
+        cpu = run_cpu_baseline(args, synth, shp, results)
 
     dec = results.get("decode_1row", {})
     roof = None
     traffic = measured_traffic()
     if dec:
-        ach = dec["gateup_GBps"]
-        roof = {"bound": "hbm", "kernel": "ffn_gateup_kernel (moe_ffn_gateup_mxfp4, 1 row)", "achieved": ach,
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
-                "algorithmic_bytes_per_launch": dec["gateup_alg_bytes"], "launch_us": dec["gateup_us"]}
+        # the layer pass is the unit of the metric: its algorithmic bytes over
+        # its measured time; the dominant kernel's own figure is a sub-field
+        per = {}
+        for name in ("decode_1row", "block_16rows", "prefill_1533rows"):
+            r = results.get(name)
+            if r:
+                per[name] = {"rows": r["rows"], "us": r["ms_per_layer"] * 1e3, "alg_bytes": r["layer_alg_bytes"],
+                             "GBps": r["layer_GBps"], "hbm_frac": r["layer_hbm_frac"]}
+                if "mfma_frac" in r:
+                    per[name]["mfma_frac"] = r["mfma_frac"]
+        roof = {"bound": "hbm", "achieved": dec["layer_GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": dec["layer_hbm_frac"], "traffic": traffic_layer(),
+                "scope": "whole 1-row layer pass (router, top-k + bucket, expert FFN, combine): 18 expert records, "
+                         "the fp32 router matrix, x in and the output row out, over the layer's measured time",
+                "algorithmic_bytes_per_step": dec["layer_alg_bytes"], "target_frac": 0.70,
+                "per_workload": per,
+                "kernel": {"name": "ffn_gateup_kernel (moe_ffn_gateup_mxfp4, 1 row)", "achieved": dec["gateup_GBps"],
+                           "frac": dec["gateup_GBps"] / HBM_PEAK_GBS, "traffic": traffic,
+                           "algorithmic_bytes_per_launch": dec["gateup_alg_bytes"], "launch_us": dec["gateup_us"]}}
     line = {
         "metric": "MoE-layer rows/s + effective MXFP4 weight GB/s at 1, 16, 1533 rows",
         "value": dec.get("rows_per_s"),
@@ -555,6 +744,9 @@ def main():
                    "shared_experts": shp.n_shared, "top_k": shp.k, "rows": 1,
                    "weights": "mxfp4, codes planes in tile order (moe_pack_experts)",
                    "x": "bf16", "router": "fp32",
+                   "arithmetic": "bf16 MFMA operands with fp32 accumulation: FP4 weights decoded exactly to bf16, "
+                                 "bf16 x exact, the fp32 hidden h as two bf16 parts (hi + lo, |h - hi - lo| <= "
+                                 "2^-18 |h|); router logits and combine in fp32",
                    "timing": f"{N_LAYERS} resident layers in rotation, back-to-back steps between two HIP events"},
         "roofline": roof,
         "effective_weight_GBps": dec.get("effective_weight_GBps"),

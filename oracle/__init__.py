@@ -40,6 +40,7 @@ def _load():
         i32, i64 = ctypes.c_int32, ctypes.c_int64
         sig = {
             "orc_max_threads": (ctypes.c_int, []),
+            "orc_set_threads": (None, [ctypes.c_int]),
             "orc_e2m1": (ctypes.c_double, [ctypes.c_int]),
             "orc_e8m0": (ctypes.c_double, [ctypes.c_int]),
             "orc_fp16": (ctypes.c_double, [ctypes.c_uint16]),
@@ -87,6 +88,11 @@ def _fn(name: str, accum: str):
 def max_threads() -> int:
     """Threads the oracle's parallel loops run on."""
     return int(_load().orc_max_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads the oracle's later parallel loops use (results do not change)."""
+    _load().orc_set_threads(int(n))
 
 
 def e2m1(code: int) -> float:

@@ -53,6 +53,16 @@ int orc_max_threads(void) {
 #endif
 }
 
+/* Sets the threads later parallel regions use (no effect without OpenMP).
+ * Results do not depend on it: every output element is one thread's. */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* Element formats                                                          */
 /* ------------------------------------------------------------------------ */

@@ -458,18 +458,57 @@ def test_kimi_block_rows_equal_single_rows(kimi_layer, B):
                 assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), (B, seed, m, key)
 
 
-@pytest.mark.parametrize("B,seed", [(16, 0), (8, 3), (2, 5)])
-def test_kimi_block16_parity(kimi_layer, B, seed):
+@pytest.mark.parametrize("B", [2, 8, 16])
+def test_kimi_block_parity_all_seeds(kimi_layer, B):
+    """The verification-block workload: 20 seeded blocks per block size (row 0
+    x0 ~ N(0,1), rows i > 0 x0 + N(0, 0.3^2)), every output of every block
+    against the oracle."""
     moe = _moe()
     L = kimi_layer
     shp = L["shape"]
-    x = synth.block_x(shp, seed, B)
     layer = moe.MoELayer(L["experts"], shp.k, B, w_router=L["wr_dev"])
-    res = layer.forward(_x_dev(shp, x))
-    ref = oracle.layer(x, shp.k, shp.n_routed, shp.n_shared, shp.d, shp.f, L["rec"], w_r=L["wr"])
-    print(f"block of {B}: {ref['n_active'] - shp.n_shared} unique routed experts", flush=True)
-    _compare_layer(res, ref, f"kimi block {B}", shp.k, shp.n_shared,
-                   rerun=lambda lg: oracle.layer(x, shp.k, shp.n_routed, shp.n_shared, shp.d, shp.f, L["rec"], logits=lg))
+    unions = []
+    for seed in range(20):
+        x = synth.block_x(shp, seed, B)
+        res = layer.forward(_x_dev(shp, x))
+        ref = oracle.layer(x, shp.k, shp.n_routed, shp.n_shared, shp.d, shp.f, L["rec"], w_r=L["wr"])
+        _compare_layer(res, ref, f"kimi block {B} seed {seed}", shp.k, shp.n_shared,
+                       rerun=lambda lg: oracle.layer(x, shp.k, shp.n_routed, shp.n_shared, shp.d, shp.f, L["rec"],
+                                                     logits=lg))
+        unions.append(int(ref["n_active"]))
+        print(f"block of {B} seed {seed}: U+S = {unions[-1]}", flush=True)
+    print(f"block of {B}: U+S mean {np.mean(unions):.1f}, range {min(unions)}-{max(unions)}", flush=True)
+
+
+@pytest.mark.parametrize("sigma", [0.5, 1.0])
+def test_kimi_block16_wider_unions(kimi_layer, sigma):
+    """16-row blocks whose rows spread further from row 0 (sigma 0.5 and 1.0)
+    reach the upper end of the pages' block unions (about 40 to 120 experts):
+    5 seeded blocks each, every output against the oracle, and every row
+    bit-identical to the same row called alone."""
+    moe = _moe()
+    L = kimi_layer
+    shp = L["shape"]
+    blk = moe.MoELayer(L["experts"], shp.k, 16, w_router=L["wr_dev"])
+    one = moe.MoELayer(L["experts"], shp.k, 1, w_router=L["wr_dev"])
+    unions = []
+    for seed in range(100, 105):
+        x = synth.block_x(shp, seed, 16, sigma=sigma)
+        xd = _x_dev(shp, x)
+        res = blk.forward(xd)
+        ref = oracle.layer(x, shp.k, shp.n_routed, shp.n_shared, shp.d, shp.f, L["rec"], w_r=L["wr"])
+        _compare_layer(res, ref, f"kimi block 16 sigma {sigma} seed {seed}", shp.k, shp.n_shared,
+                       rerun=lambda lg: oracle.layer(x, shp.k, shp.n_routed, shp.n_shared, shp.d, shp.f, L["rec"],
+                                                     logits=lg))
+        for m in range(16):
+            r1 = one.forward(xd[m:m + 1])
+            a = _row_outputs(res, m, shp.k, shp.n_shared)
+            b = _row_outputs(r1, 0, shp.k, shp.n_shared)
+            for key in a:
+                assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), (sigma, seed, m, key)
+        unions.append(int(ref["n_active"]))
+        print(f"block of 16, sigma {sigma}, seed {seed}: U+S = {unions[-1]}", flush=True)
+    assert max(unions) > 47, "wider spreads must reach larger unions than sigma 0.3"
 
 
 def test_kimi_expert_order_independence(kimi_layer):
@@ -577,15 +616,35 @@ def test_kimi_prefill_parity_sampled(kimi_layer, M):
         assert_close(y[m * kps:(m + 1) * kps], y_ref, f"prefill M={M} row {m} y_slots")
         o_ref = oracle.combine(y_ref, w_ref[m:m + 1], shp.k, shp.n_shared)
         assert_close(out[m:m + 1], o_ref, f"prefill M={M} row {m} out")
-    # the most popular expert's segment spans many groups of 16: check its
-    # first and last slots
-    counts = np.diff(off_ref)[:shp.n_routed]
-    e_hot = int(np.argmax(counts))
-    seg = perm_ref[off_ref[e_hot]:off_ref[e_hot + 1]]
-    for t in (seg[0], seg[len(seg) // 2], seg[-1]):
-        m = t // kps
-        y_ref = oracle.expert_ffn(xf[m:m + 1], L["rec"](e_hot), shp.d, shp.f)[0]
-        assert_close(y[t], y_ref, f"prefill hot expert slot {t}")
+    # slots from every kind of group the many-row path forms: an expert with
+    # at most 16 slots is one narrow group; a longer segment is cut into
+    # groups of 64 slots plus a remainder that is narrow (<= 16), 32-wide
+    # (17..32) or 64-wide (33..63); the first, middle and last slot of two
+    # groups of each kind (the hottest routed expert's first 64-group among them)
+    samples = {"narrow": [], "32-wide": [], "64-wide": []}
+    for e in np.argsort(-np.diff(off_ref), kind="stable"):
+        seg = perm_ref[off_ref[e]:off_ref[e + 1]]
+        n = len(seg)
+        if n == 0:
+            continue
+        if n <= 16:
+            groups = [("narrow", seg)]
+        else:
+            full, rem = n // 64, n % 64
+            groups = [("64-wide", seg[64 * j:64 * (j + 1)]) for j in range(full)]
+            if rem:
+                groups.append(("narrow" if rem <= 16 else "32-wide" if rem <= 32 else "64-wide", seg[64 * full:]))
+        for kind, gs in groups:
+            if len(samples[kind]) < 2:
+                samples[kind].append((int(e), gs))
+    for kind, got in samples.items():
+        assert got, f"prefill M={M}: no {kind} group to sample"
+        for e, gs in got:
+            for t in sorted({int(gs[0]), int(gs[len(gs) // 2]), int(gs[-1])}):
+                m = t // kps
+                y_ref = oracle.expert_ffn(xf[m:m + 1], L["rec"](e), shp.d, shp.f)[0]
+                assert_close(y[t], y_ref, f"prefill M={M} {kind} group of expert {e}, slot {t}")
+    print(f"prefill M={M}: sampled " + ", ".join(f"{len(v)} {k} groups" for k, v in samples.items()), flush=True)
 
 
 def test_kimi_prefill_rows_equal_decode_rows(kimi_layer):
