@@ -61,7 +61,8 @@ typedef enum {
   MOE_OK = 0,
   MOE_EINVAL = -1,       /* bad argument: NULL pointer, negative size, k > E, d % 32, ... */
   MOE_EUNSUPPORTED = -2, /* valid but outside what this build implements (see per function) */
-  MOE_EHIP = -3          /* a HIP launch or runtime call failed */
+  MOE_EHIP = -3,         /* a HIP launch or runtime call failed */
+  MOE_ESCRATCH = -4      /* moe_layer_mxfp4_noalloc: the call needs more than its static scratch */
 } moe_status;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
@@ -194,6 +195,31 @@ int moe_layer_mxfp4(const void *x, moe_dtype x_dtype, const float *w_router, flo
                     const moe_experts *W, int32_t *topk_ids, float *topk_w, int32_t *offsets, int32_t *perm,
                     int32_t *active, int32_t *n_active, int32_t *dev_error, float *y_slots, float *out,
                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* moe_layer_mxfp4 without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It enqueues the same kernels and every
+ * output is bit-identical to moe_layer_mxfp4's for the same arguments.
+ *
+ * Scratch: a static device array of moe_noalloc_scratch_bytes() (8 MiB) per
+ * GPU, part of the library's code object; each GPU the library runs on holds
+ * it until the process ends.  The first call on a device looks its address up
+ * (with that device current); no call allocates or frees memory.  A call
+ * whose scratch need (moe_workspace_bytes(M, k, W)) exceeds the array returns
+ * MOE_ESCRATCH before enqueueing anything: a Kimi-shaped layer (d = 7168,
+ * f = 1536, k = 16, S = 2) needs 1.77 MB at 16 rows and fits up to 75 rows.
+ * The array keeps the last call's contents; no call relies on them (every
+ * kernel writes what it reads first).  All calls on one GPU share the array,
+ * so calls that may overlap on one GPU race: issue them on one stream, or
+ * order them with events.  `stream` (or, for the null stream, the current
+ * device) selects the GPU.  Other arguments, requirements and errors are
+ * moe_layer_mxfp4's. */
+int moe_layer_mxfp4_noalloc(const void *x, moe_dtype x_dtype, const float *w_router, float *logits, int32_t M,
+                            int32_t k, const moe_experts *W, int32_t *topk_ids, float *topk_w, int32_t *offsets,
+                            int32_t *perm, int32_t *active, int32_t *n_active, int32_t *dev_error, float *y_slots,
+                            float *out, void *stream);
+/* Bytes of the static scratch array of moe_layer_mxfp4_noalloc (host-only). */
+size_t moe_noalloc_scratch_bytes(void);
 
 /* ------------------------------------------------------------------------
  * Expert streaming ("One GPU, three storage tiers" and "Read the experts the

@@ -17,13 +17,14 @@ import torch
 
 from .build import LIB_PATH
 
-MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP = 0, -1, -2, -3
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EHIP, MOE_ESCRATCH = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16 = 0, 1
 MOE_LAYOUT_ROWS, MOE_LAYOUT_TILES = 0, 1
 
 # names exported by include/moe.h
 ABI_FUNCTIONS = ("moe_route", "moe_bucket", "moe_expert_ffn_mxfp4", "moe_ffn_gateup_mxfp4", "moe_ffn_down_mxfp4",
-                 "moe_workspace_bytes", "moe_pack_experts", "moe_combine", "moe_layer_mxfp4", "moe_cache_create", "moe_cache_destroy",
+                 "moe_workspace_bytes", "moe_pack_experts", "moe_combine", "moe_layer_mxfp4", "moe_layer_mxfp4_noalloc",
+                 "moe_noalloc_scratch_bytes", "moe_cache_create", "moe_cache_destroy",
                  "moe_cache_get_stats", "moe_layer_streamed", "moe_cache_simulate", "q8_0_matmul", "q8_0_matmul_layout", "q8_0_pack", "q8_0_rows",
                  "moe_residual_bf16", "moe_rmsnorm", "moe_argmax_rows", "moe_fnv1a_rows", "moe_status_str")
 
@@ -71,6 +72,9 @@ def _load() -> ctypes.CDLL:
         "moe_pack_experts": (ctypes.c_int, [P, P, i64, i64, i32, i32, ctypes.c_int, P]),
         "moe_combine": (ctypes.c_int, [P, P, i32, i32, i32, i32, P, P]),
         "moe_layer_mxfp4": (ctypes.c_int, [P, ctypes.c_int, P, P, i32, i32, EP, P, P, P, P, P, P, P, P, P, P, sz, P]),
+        "moe_layer_mxfp4_noalloc": (ctypes.c_int, [P, ctypes.c_int, P, P, i32, i32, EP, P, P, P, P, P, P, P, P, P,
+                                                   P]),
+        "moe_noalloc_scratch_bytes": (sz, []),
         "moe_cache_create": (ctypes.c_int, [ctypes.POINTER(_CacheConfig), ctypes.POINTER(P)]),
         "moe_cache_destroy": (ctypes.c_int, [P]),
         "moe_cache_get_stats": (ctypes.c_int, [P, ctypes.POINTER(_CacheStats)]),
@@ -297,6 +301,38 @@ def moe_layer_mxfp4(x, w_router, logits, k, experts: Experts, topk_ids, topk_w, 
                               _ptr(dev_error), _ptr(y_slots), _ptr(out), _ptr(workspace), workspace.numel(),
                               _stream(stream))
     _check("moe_layer_mxfp4", rc)
+
+
+def moe_layer_mxfp4_noalloc(x, w_router, logits, k, experts: Experts, topk_ids, topk_w, offsets, perm, active,
+                            n_active, dev_error, y_slots, out, stream=None):
+    """moe_layer_mxfp4 with its scratch in the library's static device array
+    (no workspace argument; nothing is allocated).  Calls that may overlap on
+    one GPU share that array and must be ordered."""
+    M, d = x.shape
+    E, S = experts.n_routed, experts.n_shared
+    if d != experts.d or tuple(logits.shape) != (M, E) or tuple(out.shape) != (M, d):
+        raise ValueError("x [M x d], logits [M x E] and out [M x d] must match the experts")
+    if tuple(topk_ids.shape) != (M, k) or tuple(topk_w.shape) != (M, k):
+        raise ValueError("topk outputs must be [M x k]")
+    if tuple(y_slots.shape) != (M * (k + S), d) or y_slots.dtype != torch.float32 or out.dtype != torch.float32:
+        raise ValueError("y_slots must be float32 [M*(k+S) x d], out float32")
+    for t in (topk_ids, offsets, perm, active, n_active, dev_error):
+        if t.dtype != torch.int32:
+            raise ValueError("ids and bucket tensors are int32")
+    if offsets.numel() < E + S + 1 or perm.numel() < M * (k + S) or active.numel() < E + S:
+        raise ValueError("bucket outputs too small")
+    if w_router is not None and (w_router.dtype != torch.float32 or tuple(w_router.shape) != (E, d)):
+        raise ValueError("w_router must be float32 [E x d]")
+    s = experts.c_struct()
+    rc = _lib.moe_layer_mxfp4_noalloc(_ptr(x), _x_dtype(x), _ptr(w_router), _ptr(logits), M, k, ctypes.byref(s),
+                                      _ptr(topk_ids), _ptr(topk_w), _ptr(offsets), _ptr(perm), _ptr(active),
+                                      _ptr(n_active), _ptr(dev_error), _ptr(y_slots), _ptr(out), _stream(stream))
+    _check("moe_layer_mxfp4_noalloc", rc)
+
+
+def moe_noalloc_scratch_bytes() -> int:
+    """Bytes of moe_layer_mxfp4_noalloc's static scratch array."""
+    return int(_lib.moe_noalloc_scratch_bytes())
 
 
 def q8_0_pack(src, dst, to_layout, stream=None):

@@ -14,7 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["capi.cpp", "cache.cpp", "route.hip", "bucket.hip", "ffn.hip", "q8_0.hip", "verify.hip", "pack.hip"]
+SOURCES = ["capi.cpp", "cache.cpp", "route.hip", "bucket.hip", "ffn.hip", "q8_0.hip", "verify.hip", "pack.hip",
+           "noalloc.hip"]
 ARCH = "gfx950"
 
 

@@ -98,6 +98,8 @@ const char *moe_status_str(int status) {
     case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
     case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: valid but not supported by this build";
     case MOE_EHIP: return "MOE_EHIP: HIP launch or runtime error";
+    case MOE_ESCRATCH:
+      return "MOE_ESCRATCH: the call needs more scratch than the no-allocation entry point's static array holds";
     default: return "unknown moe_status";
   }
 }
@@ -187,6 +189,17 @@ int moe_layer_mxfp4(const void *x, moe_dtype x_dtype, const float *w_router, flo
   const int rc = moe_layer_check(x, x_dtype, w_router, logits, M, k, W, topk_ids, topk_w, offsets, perm, active,
                                  n_active, dev_error, y_slots, out, workspace, workspace_bytes);
   if (rc != MOE_OK || M == 0) return rc;
+  return moe_layer_enqueue(x, x_dtype, w_router, logits, M, k, W, topk_ids, topk_w, offsets, perm, active, n_active,
+                           dev_error, y_slots, out, workspace, stream);
+}
+
+}  // extern "C"
+
+// The kernels of one layer pass (arguments already checked).
+int moe_layer_enqueue(const void *x, moe_dtype x_dtype, const float *w_router, float *logits, int32_t M, int32_t k,
+                      const moe_experts *W, int32_t *topk_ids, float *topk_w, int32_t *offsets, int32_t *perm,
+                      int32_t *active, int32_t *n_active, int32_t *dev_error, float *y_slots, float *out,
+                      void *workspace, void *stream) {
   const int E = W->n_routed, S = W->n_shared, d = W->d;
   const hipStream_t st = as_stream(stream);
   const int bf = x_dtype == MOE_BF16;
@@ -198,6 +211,8 @@ int moe_layer_mxfp4(const void *x, moe_dtype x_dtype, const float *w_router, flo
     return MOE_EHIP;
   return status_of(moe::combine_launch(y_slots, topk_w, M, k, S, d, out, st));
 }
+
+extern "C" {
 
 int q8_0_matmul_layout(const float *X, int32_t M, int32_t K, const int8_t *Wq, const uint16_t *Ws, int32_t N,
                        float *Y, moe_layout layout, void *stream) {

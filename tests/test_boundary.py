@@ -51,6 +51,7 @@ def test_status_strings():
     assert lib.moe_status_str(-1).startswith(b"MOE_EINVAL")
     assert lib.moe_status_str(-2).startswith(b"MOE_EUNSUPPORTED")
     assert lib.moe_status_str(-3).startswith(b"MOE_EHIP")
+    assert lib.moe_status_str(-4).startswith(b"MOE_ESCRATCH")
 
 
 FAKE = 0x100000  # never dereferenced: every call below fails host validation
@@ -186,6 +187,37 @@ def test_layer_validation():
     assert call(wsp=FAKE + 16) == EINVAL
     assert call(ex=_experts(n_routed=5000, n_shared=0)) == EUNSUP
     assert call(M=0) == moe.MOE_OK
+
+
+def test_noalloc_layer_validation():
+    """The no-allocation layer call checks what moe_layer_mxfp4 checks (no
+    workspace argument), and refuses a call whose scratch need exceeds its
+    static array, all on the host before anything is enqueued."""
+    import router_top_bucket_amd as moe
+    lib = moe.raw_library()
+    EINVAL, EUNSUP = moe.MOE_EINVAL, moe.MOE_EUNSUPPORTED
+    cap = lib.moe_noalloc_scratch_bytes()
+    assert cap == 8 << 20
+    ok = _experts()
+
+    def call(x=FAKE, dt=0, wr=FAKE, lg=FAKE, M=2, k=2, ex=ok, out=FAKE, dev_error=FAKE, y=FAKE):
+        return lib.moe_layer_mxfp4_noalloc(x, dt, wr, lg, M, k, ctypes.byref(ex), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                           FAKE, dev_error, y, out, None)
+
+    assert call(ex=_experts(d=100)) == EINVAL
+    assert call(M=-1) == EINVAL
+    assert call(k=17) == EINVAL
+    assert call(lg=None) == EINVAL
+    assert call(out=FAKE + 4) == EINVAL
+    assert call(y=None) == EINVAL
+    assert call(ex=_experts(n_routed=5000, n_shared=0)) == EUNSUP
+    assert call(M=0) == moe.MOE_OK
+    # the Kimi shape: 75 rows fit the 8 MiB array, 76 do not
+    kimi = _experts(d=7168, f=1536, n_routed=896, n_shared=2, stride=17547264)
+    assert lib.moe_workspace_bytes(75, 16, ctypes.byref(kimi)) <= cap < lib.moe_workspace_bytes(76, 16,
+                                                                                                 ctypes.byref(kimi))
+    assert call(M=76, k=16, ex=kimi) == moe.MOE_ESCRATCH
+    assert call(M=76, k=16, ex=kimi, out=None) == EINVAL  # argument errors come first
 
 
 def test_cache_and_streamed_layer_validation():
