@@ -241,33 +241,10 @@ __global__ __launch_bounds__(TB_MAX_ROWS * 64) void topk_bucket_kernel(
     w[(int64_t)wv * k + lane] = wt;
   }
   const int kps = k + S, NE = E + S;
-  // One row (the workgroup is one wave): its k routed and S shared experts
-  // are distinct, so lane t's slot has rank = the number of experts below
-  // its own, and offsets[e] = the number of experts below e.  Lane l writes
-  // offsets[l*C .. l*C+C) from that count at l*C and a mask of the experts
-  // inside its range.  Same results as the general path below.
+  // One row (the workgroup is one wave): bucket_one_row, same results as
+  // the general path below.
   if (M == 1 && NE + 1 <= 64 * 64 && __ballot(lane < k && (id < 0 || id >= E)) == 0ull) {
-    const int e_t = lane < k ? id : (lane < kps ? E + (lane - k) : 0x7FFFFFFF);
-    const int C = (NE + 1 + 63) >> 6, e0 = lane * C;
-    int rank = 0, below = 0;
-    uint64_t inside = 0ull;
-    for (int u = 0; u < kps; ++u) {
-      const int eu = __builtin_amdgcn_readlane(e_t, u);
-      rank += eu < e_t;
-      below += eu < e0;
-      const int rel = eu - e0;
-      if (rel >= 0 && rel < C) inside |= 1ull << rel;
-    }
-    if (lane < kps) {
-      perm[rank] = lane;
-      active[rank] = e_t;
-    }
-    for (int i = 0; i < C; ++i)
-      if (e0 + i <= NE) offsets[e0 + i] = below + __popcll(inside & ((1ull << i) - 1ull));
-    if (lane == 0) {
-      *n_active = kps;
-      *dev_error = 0;
-    }
+    bucket_one_row(id, lane, E, k, S, offsets, perm, active, n_active, dev_error);
     return;
   }
   if (lane < k) sids[wv * k + lane] = id;

@@ -203,6 +203,29 @@ int moe_layer_enqueue(const void *x, moe_dtype x_dtype, const float *w_router, f
   const int E = W->n_routed, S = W->n_shared, d = W->d;
   const hipStream_t st = as_stream(stream);
   const int bf = x_dtype == MOE_BF16;
+  if (moe::ffn_route_fusable(M, bf, d, E, k, S)) {
+    // one row: the gate/up launch ranks the logits and writes the routing
+    // and bucketing outputs itself (the same code as the top-k and bucket
+    // kernels), one launch fewer
+    if (w_router && moe::logits_launch(x, bf, w_router, logits, M, d, E, st)) return MOE_EHIP;
+    moe::RouteArgs ra;
+    ra.logits = logits;
+    ra.E = E;
+    ra.k = k;
+    ra.S = S;
+    ra.ids = topk_ids;
+    ra.w = topk_w;
+    ra.offsets = offsets;
+    ra.perm = perm;
+    ra.active = active;
+    ra.n_active = n_active;
+    ra.dev_error = dev_error;
+    if (moe::ffn_launch(x, bf, M, k, W->base, W->stride, W->d, W->f, E, S, offsets, perm, active, n_active, y_slots,
+                        workspace, moe::kStageGateUp | moe::kStageDown, nullptr, 0, 0,
+                        W->layout == MOE_LAYOUT_TILES, st, &ra))
+      return MOE_EHIP;
+    return status_of(moe::combine_launch(y_slots, topk_w, M, k, S, d, out, st));
+  }
   if (moe::route_bucket_launch(x, bf, w_router, logits, M, d, E, k, S, topk_ids, topk_w, offsets, perm, active,
                                 n_active, dev_error, st))
     return MOE_EHIP;

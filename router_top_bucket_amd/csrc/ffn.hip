@@ -32,6 +32,7 @@
 // is the order the vector-memory counter retires them in.
 #include "common.h"
 #include "launch.h"
+#include "topk.h"
 
 #include <algorithm>
 
@@ -109,6 +110,42 @@ __device__ __forceinline__ bool load_group(const GroupSrc &src, int g, int &expe
   }
   count = count < maxc ? count : maxc;
   return count > 0;
+}
+
+// One-row layer calls in one launch (route mode): the router logits of the
+// row are the input, and group g of the launch is the row's g-th expert in
+// bucket order: its k routed experts by ascending id (ids are below E), then
+// the S shared ones.  A workgroup of a shared expert knows it at once; one
+// of a routed expert ranks the logits in its first wave (topk_row, the top-k
+// kernel's code, so the set and its rank order are the top-k kernel's) and
+// takes the id at ascending position g.  The workgroup of item 0 also writes
+// what the top-k and bucket kernels would (ids, weights, offsets, perm,
+// active, n_active, dev_error: the same code, the same bits); the down pass
+// and the combine read them after this launch.  Every thread of the
+// workgroup calls this.  `lists`: at least topk_wave_lds(16) bytes of LDS,
+// free until the function returns.
+__device__ int route_one_row(const RouteArgs &ra, int g, bool writer, uint8_t *lists, int *bcast) {
+  if (g >= ra.k) return ra.E + (g - ra.k);
+  const int lane = threadIdx.x & 63;
+  if (threadIdx.x < 64) {
+    int32_t id;
+    float wt;
+    topk_row<16>(ra.logits, ra.E, ra.k, (uint64_t(*)[64])lists, lane, id, wt);
+    int pos = 0;  // ascending position of this lane's id among the k (distinct) ids
+    for (int i = 0; i < ra.k; ++i) pos += __builtin_amdgcn_readlane(id, i) < id;
+    const uint64_t hit = __ballot(lane < ra.k && pos == g);
+    const int e = __builtin_amdgcn_readlane(id, (int)__ffsll((unsigned long long)hit) - 1);
+    if (lane == 0) *bcast = e;
+    if (writer) {
+      if (lane < ra.k) {
+        ra.ids[lane] = id;
+        ra.w[lane] = wt;
+      }
+      bucket_one_row(id, lane, ra.E, ra.k, ra.S, ra.offsets, ra.perm, ra.active, ra.n_active, ra.dev_error);
+    }
+  }
+  lds_barrier();  // the expert is in LDS, and the first wave is done with the lists
+  return *bcast;
 }
 
 // Many rows: one workgroup cuts every active expert's segment into groups
@@ -373,11 +410,16 @@ __device__ __forceinline__ float lds_scale(const uint8_t *row, int s, int q) {
 // x staging (ring mode): piece i of a step (i < MAXC*16) is column i/16,
 // elements 8*(i%16)..+8 of the step; thread t stages pieces t, t+GW*64, ...
 // fp32 x is split exactly into three bf16 parts as it is staged.
-template <int XBF16, int TPW, int GW, int PF, int MAXC, bool SX4, bool BRES, bool PAIR>
+//
+// ROUTE (one row, resident B): the groups come from the router logits
+// (route_one_row) instead of the bucketing arrays, which this launch writes.
+template <int XBF16, int TPW, int GW, int PF, int MAXC, bool SX4, bool BRES, bool PAIR, bool ROUTE = false>
 __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
     const void *__restrict__ x, int d, int f, int kps, int n_slots, const uint8_t *__restrict__ experts,
-    int64_t stride, GroupSrc src, const int32_t *__restrict__ perm, int n_ftiles, uint16_t *__restrict__ h_ws) {
+    int64_t stride, GroupSrc src, const int32_t *__restrict__ perm, int n_ftiles, uint16_t *__restrict__ h_ws,
+    RouteArgs ra) {
   static_assert(PAIR || GW % 2 == 0, "gate and up waves come in pairs");
+  static_assert(!ROUTE || BRES, "route mode stages x once (one row)");
   constexpr int HW = PAIR ? GW : GW / 2;  // waves per row group
   constexpr int ROWS = HW * TPW * 16;
   constexpr int NT = PAIR ? 2 * TPW : TPW;  // tiles per wave
@@ -388,12 +430,19 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
   constexpr int SPT = BRES ? 0 : (MAXC * 16 + NTH - 1) / NTH;
   constexpr int SPTA = SPT > 0 ? SPT : 1;  // array extent
   extern __shared__ __align__(16) uint8_t lds[];
-  const int item = xcd_item(group_count(src) * n_ftiles);
+  const int item = xcd_item((ROUTE ? ra.k + ra.S : group_count(src)) * n_ftiles);
   if (item < 0) return;
   const int g = item / n_ftiles;
   const int ft = item - g * n_ftiles;
   int expert, start, count;
-  if (!load_group(src, g, expert, start, count, MAXC)) return;
+  if constexpr (ROUTE) {
+    __shared__ int route_bcast;
+    expert = route_one_row(ra, g, item == 0, lds, &route_bcast);
+    start = g;  // one slot per expert: bucket position g
+    count = 1;
+  } else {
+    if (!load_group(src, g, expert, start, count, MAXC)) return;
+  }
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = lane & 15, q = lane >> 4;
@@ -479,7 +528,8 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
     uint32_t xb[MAXC];
 #pragma unroll
     for (int c = 0; c < MAXC; ++c) {
-      const int t = perm[start + (c < count ? c : count - 1)];
+      // route mode: the one row's slots (perm is being written by this launch)
+      const int t = ROUTE ? 0 : perm[start + (c < count ? c : count - 1)];
       xb[c] = (c < count && t >= 0 && t < n_slots) ? (uint32_t)(t / kps) * (uint32_t)(d * EL) : kOOB;
     }
     constexpr int CH = 8;  // pieces per thread per round
@@ -1074,9 +1124,13 @@ size_t ffn_workspace_bytes(int64_t M, int k, int S, int d, int f, int n_experts)
 
 // gfx950 gives a workgroup up to 160 KB of LDS; kernels opt in past 64 KB.
 constexpr int kMaxLds = 160 * 1024;
-static bool allow_lds(const void *kernel) {
-  return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds) == hipSuccess;
+static bool allow_lds(const void *kernel, int bytes = kMaxLds) {
+  if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess) return true;
+  (void)hipGetLastError();  // leave no error behind for the next launch check
+  return false;
 }
+// Route-mode kernels hold a few bytes of static LDS besides the dynamic area.
+constexpr int kRouteMaxLds = kMaxLds - 1024;
 
 // Every buffer resource must stay below 2^30 bytes (see kOOB / kDead).
 bool ffn_shape_ok(int64_t M, int k, int S, int d, int f, int64_t stride) {
@@ -1088,19 +1142,22 @@ bool ffn_shape_ok(int64_t M, int k, int S, int d, int f, int64_t stride) {
          M * (int64_t)d * 4 < lim && T * kHParts * f * 2 < lim;
 }
 
-template <int XBF16, int TPW, int GW, int PF, int MAXC, bool SX4, bool BRES, bool PAIR>
+template <int XBF16, int TPW, int GW, int PF, int MAXC, bool SX4, bool BRES, bool PAIR, bool ROUTE = false>
 static int launch_gateup(const void *x, int d, int f, int kps, int T, const uint8_t *experts, int64_t stride,
-                         const GroupSrc &src, const int32_t *perm, int64_t maxg, uint16_t *h_ws, hipStream_t stream) {
+                         const GroupSrc &src, const int32_t *perm, int64_t maxg, uint16_t *h_ws, hipStream_t stream,
+                         const RouteArgs &ra = RouteArgs{}) {
   constexpr int ROWS = (PAIR ? GW : GW / 2) * TPW * 16;
   const int n_ftiles = (f + ROWS - 1) / ROWS;
   if (maxg <= 0) return 0;
-  const size_t smem = gateup_lds_bytes(d, PF, XBF16 ? 1 : 3, MAXC, BRES, ROWS);
-  if (smem > (size_t)kMaxLds) return -3;
+  size_t smem = gateup_lds_bytes(d, PF, XBF16 ? 1 : 3, MAXC, BRES, ROWS);
+  if (ROUTE) smem = std::max(smem, topk_wave_lds(16));  // the ranking lists alias the start of LDS
+  if (smem > (size_t)(ROUTE ? kRouteMaxLds : kMaxLds)) return -3;
   static const bool lds_ok =
-      allow_lds(reinterpret_cast<const void *>(&ffn_gateup_kernel<XBF16, TPW, GW, PF, MAXC, SX4, BRES, PAIR>));
+      allow_lds(reinterpret_cast<const void *>(&ffn_gateup_kernel<XBF16, TPW, GW, PF, MAXC, SX4, BRES, PAIR, ROUTE>),
+                ROUTE ? kRouteMaxLds : kMaxLds);
   if (!lds_ok) return -3;
-  hipLaunchKernelGGL((ffn_gateup_kernel<XBF16, TPW, GW, PF, MAXC, SX4, BRES, PAIR>), dim3((unsigned)align_up((size_t)(maxg * n_ftiles), kXcds)), dim3(GW * 64),
-                     smem, stream, x, d, f, kps, T, experts, stride, src, perm, n_ftiles, h_ws);
+  hipLaunchKernelGGL((ffn_gateup_kernel<XBF16, TPW, GW, PF, MAXC, SX4, BRES, PAIR, ROUTE>), dim3((unsigned)align_up((size_t)(maxg * n_ftiles), kXcds)), dim3(GW * 64),
+                     smem, stream, x, d, f, kps, T, experts, stride, src, perm, n_ftiles, h_ws, ra);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
@@ -1136,10 +1193,22 @@ static int launch_down(int d, int f, int T, const uint8_t *experts, int64_t stri
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
+// The one-row gate/up shapes that route mode runs in (see ffn_launch).
+static bool gateup_one_row_bres(int x_bf16, int d) {
+  const size_t half = (size_t)kMaxLds / 2;
+  return x_bf16 ? gateup_lds_bytes(d, 4, 1, 1, true, 64) <= half : gateup_lds_bytes(d, 4, 3, 4, true, 32) <= half;
+}
+
+bool ffn_route_fusable(int64_t M, int x_bf16, int d, int E, int k, int S) {
+  return M == 1 && E <= 16 * 64 && k + S <= 64 && E + S + 1 <= 64 * 64 && gateup_one_row_bres(x_bf16, d);
+}
+
 int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *experts, int64_t stride, int d, int f,
                int n_routed, int n_shared, const int32_t *offsets, const int32_t *perm, const int32_t *active,
                const int32_t *n_active, float *y, void *workspace, int stages, const int32_t *slot_map,
-               int n_records, int64_t max_active, int tiled, hipStream_t stream) {
+               int n_records, int64_t max_active, int tiled, hipStream_t stream, const RouteArgs *route) {
+  if (route && (!ffn_route_fusable(M, x_bf16, d, n_routed, k, n_shared) || !(stages & kStageGateUp) || slot_map))
+    return -3;
   const int S = n_shared;
   const int kps = k + S;
   const int64_t T = M * kps;
@@ -1194,6 +1263,11 @@ int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *exper
 #define MOE_GU(XB, T, G, P, C, R, PR)                                                                          \
   (gsx4 ? launch_gateup<XB, T, G, P, C, true, R, PR>(x, d, f, kps, T_, experts, stride, src[0], perm, cap[0], h_ws, stream) \
         : launch_gateup<XB, T, G, P, C, false, R, PR>(x, d, f, kps, T_, experts, stride, src[0], perm, cap[0], h_ws, stream))
+#define MOE_GUR(XB, T, G, P, C)                                                                                  \
+  (gsx4 ? launch_gateup<XB, T, G, P, C, true, true, true, true>(x, d, f, kps, T_, experts, stride, src[0], perm,   \
+                                                                 cap[0], h_ws, stream, *route)                    \
+        : launch_gateup<XB, T, G, P, C, false, true, true, true>(x, d, f, kps, T_, experts, stride, src[0], perm,  \
+                                                                  cap[0], h_ws, stream, *route))
 #define MOE_GUW(XB, G, P, NCB, CL) \
   launch_gateup_wide<XB, G, P, NCB>(x, d, f, kps, T_, experts, stride, src[CL], perm, cap[CL], h_ws, stream)
 #define MOE_DN(T, D, P, C, R, CL, CS)                                                                                   \
@@ -1214,7 +1288,11 @@ int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *exper
   if (stages & kStageGateUp) {
     const int np = x_bf16 ? 1 : 3;
     const size_t half = (size_t)kMaxLds / 2;
-    if (x_bf16) {
+    if (route) {
+      // one row, groups from the logits (ffn_route_fusable checked the shape)
+      cap[0] = k + S;
+      rc = x_bf16 ? MOE_GUR(1, 1, 4, 4, 1) : MOE_GUR(0, 1, 2, 4, 4);
+    } else if (x_bf16) {
       if (M == 1 && gateup_lds_bytes(d, 4, np, 1, true, 64) <= half) rc = MOE_GU(1, 1, 4, 4, 1, true, true);
       else if (M == 2 && gateup_lds_bytes(d, 4, np, 2, true, 64) <= half) rc = MOE_GU(1, 1, 4, 4, 2, true, true);
       else if (M >= 5 && M <= 8) rc = MOE_GU(1, 1, 4, 4, 16, false, false);
@@ -1239,6 +1317,7 @@ int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *exper
     if (!rc && wide) rc = MOE_DN(4, 8, 2, 64, false, 2, 2);
   }
 #undef MOE_GU
+#undef MOE_GUR
 #undef MOE_GUW
 #undef MOE_DN
   return rc;

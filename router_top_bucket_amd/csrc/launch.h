@@ -22,6 +22,18 @@ int route_bucket_launch(const void *x, int x_bf16, const float *w_router, float 
                         int S, int32_t *ids, float *w, int32_t *offsets, int32_t *perm, int32_t *active,
                         int32_t *n_active, int32_t *dev_error, hipStream_t stream);
 
+// Route mode of the one-row expert FFN: the gate/up launch ranks the logits
+// itself and writes the routing and bucketing outputs (ffn_gateup_kernel).
+struct RouteArgs {
+  const float *logits = nullptr;  // [1 x E]
+  int E = 0, k = 0, S = 0;
+  int32_t *ids = nullptr;  // [k]
+  float *w = nullptr;      // [k]
+  int32_t *offsets = nullptr, *perm = nullptr, *active = nullptr, *n_active = nullptr, *dev_error = nullptr;
+};
+// Whether a layer call of M rows can take route mode.
+bool ffn_route_fusable(int64_t M, int x_bf16, int d, int E, int k, int S);
+
 int64_t ffn_max_groups(int64_t M, int k, int S, int n_experts);
 size_t ffn_workspace_bytes(int64_t M, int k, int S, int d, int f, int n_experts);
 bool ffn_shape_ok(int64_t M, int k, int S, int d, int f, int64_t stride);
@@ -35,7 +47,7 @@ constexpr int kStageGateUp = 1, kStageDown = 2;
 int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *experts, int64_t stride, int d, int f,
                int n_routed, int n_shared, const int32_t *offsets, const int32_t *perm, const int32_t *active,
                const int32_t *n_active, float *y, void *workspace, int stages, const int32_t *slot_map,
-               int n_records, int64_t max_active, int tiled, hipStream_t stream);
+               int n_records, int64_t max_active, int tiled, hipStream_t stream, const RouteArgs *route = nullptr);
 
 // Copies n_records expert records from src to dst (distinct buffers), the
 // codes planes permuted from row to tile order (to_tiles) or back; every

@@ -135,4 +135,39 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ row, int E, i
   w_out = ej / z;
 }
 
+// Bucketing of one row in one wave, from its top-k ids (lane j < k holds
+// the expert of rank j, every id in [0, E)).  The row's k routed and S shared
+// experts are distinct, so slot t's position in bucket order is the number
+// of the row's experts below its own, and offsets[e] is the number of them
+// below e.  Lane l writes offsets[l*C .. l*C+C) (C = ceil((E+S+1)/64)) from
+// that count at l*C and a mask of the experts inside its range.  Needs
+// k + S <= 64 and E + S + 1 <= 4096; the results equal the general
+// counting sort's.
+__device__ __forceinline__ void bucket_one_row(int32_t id, int lane, int E, int k, int S, int32_t *offsets,
+                                               int32_t *perm, int32_t *active, int32_t *n_active,
+                                               int32_t *dev_error) {
+  const int kps = k + S, NE = E + S;
+  const int e_t = lane < k ? id : (lane < kps ? E + (lane - k) : 0x7FFFFFFF);
+  const int C = (NE + 1 + 63) >> 6, e0 = lane * C;
+  int rank = 0, below = 0;
+  uint64_t inside = 0ull;
+  for (int u = 0; u < kps; ++u) {
+    const int eu = __builtin_amdgcn_readlane(e_t, u);
+    rank += eu < e_t;
+    below += eu < e0;
+    const int rel = eu - e0;
+    if (rel >= 0 && rel < C) inside |= 1ull << rel;
+  }
+  if (lane < kps) {
+    perm[rank] = lane;
+    active[rank] = e_t;
+  }
+  for (int i = 0; i < C; ++i)
+    if (e0 + i <= NE) offsets[e0 + i] = below + __popcll(inside & ((1ull << i) - 1ull));
+  if (lane == 0) {
+    *n_active = kps;
+    *dev_error = 0;
+  }
+}
+
 }  // namespace moe
