@@ -276,16 +276,19 @@ __host__ __device__ __forceinline__ size_t gateup_dummy_off(int d, int pf, int n
 __host__ __device__ __forceinline__ size_t gateup_lds_bytes(int d, int pf, int np, int maxc, bool bres, int rows) {
   return gateup_dummy_off(d, pf, np, maxc, bres, rows) + 16 * 3;
 }
-// Down LDS: the scale rows (ROWS), then B (resident: 3*MAXC rows; ring: PF
-// slots of 3*MAXC rows), whose space the per-(row, column) part sums of YC
-// columns at a time (ROWS x (YC + 1) floats, see down_yc) reuse once the
-// main loop is done, then the dummy area.
-__host__ __device__ __forceinline__ size_t down_b_off(int f, int rows) { return lds_align16((size_t)rows * sc_pitch(f)); }
+// Down LDS: the scale rows (ROWS; none when the scales travel with the ring
+// loads, scr), then B (resident: 3*MAXC rows; ring: PF slots of 3*MAXC
+// rows), whose space the per-(row, column) part sums of YC columns at a time
+// (ROWS x (YC + 1) floats, see down_yc) reuse once the main loop is done,
+// then the dummy area.
+__host__ __device__ __forceinline__ size_t down_b_off(int f, int rows, bool scr = false) {
+  return scr ? 0 : lds_align16((size_t)rows * sc_pitch(f));
+}
 __host__ __device__ __forceinline__ size_t down_b_bytes(int f, int pf, int maxc, bool bres) {
   return bres ? (size_t)kHParts * maxc * bres_row_bytes(f) : (size_t)pf * kHParts * maxc * kBRow;
 }
-__host__ __device__ __forceinline__ size_t down_y_off(int f, int pf, int maxc, bool bres, int rows) {
-  return down_b_off(f, rows);
+__host__ __device__ __forceinline__ size_t down_y_off(int f, int pf, int maxc, bool bres, int rows, bool scr = false) {
+  return down_b_off(f, rows, scr);
 }
 // Columns of the epilogue's per-(row, column) sums held at a time: all of
 // them for up to 16 slots (or a resident B), else as many whole 16-slot
@@ -297,13 +300,15 @@ __host__ __device__ constexpr int down_yc(int pf, int maxc, bool bres, int rows)
   const int yc = avail / blk * blk;
   return (bres || nc <= blk) ? nc : (yc < blk ? blk : (yc > nc ? nc : yc));
 }
-__host__ __device__ __forceinline__ size_t down_dummy_off(int f, int pf, int maxc, bool bres, int rows) {
+__host__ __device__ __forceinline__ size_t down_dummy_off(int f, int pf, int maxc, bool bres, int rows,
+                                                          bool scr = false) {
   const int yc = down_yc(pf, maxc, bres, rows);
   const size_t b = down_b_bytes(f, pf, maxc, bres), y = (size_t)rows * (yc + 1) * sizeof(float);
-  return lds_align16(down_b_off(f, rows) + (b > y ? b : y));
+  return lds_align16(down_b_off(f, rows, scr) + (b > y ? b : y));
 }
-__host__ __device__ __forceinline__ size_t down_lds_bytes(int f, int pf, int maxc, bool bres, int rows) {
-  return down_dummy_off(f, pf, maxc, bres, rows) + 16;
+__host__ __device__ __forceinline__ size_t down_lds_bytes(int f, int pf, int maxc, bool bres, int rows,
+                                                          bool scr = false) {
+  return down_dummy_off(f, pf, maxc, bres, rows, scr) + 16;
 }
 
 // ------------------------------------------------------------------ scales
@@ -890,7 +895,14 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_wide_kernel(
 // fixed order, independent of the column's position; the epilogue adds a
 // slot's two part sums, hi + lo.  Lanes of columns past the group's read B
 // row 0 (those columns are never used).
-template <int TPW, int DW, int PF, int MAXC, bool SX4, bool BRES, int CS>
+//
+// SCR (ring mode, f % 128 == 0): the scales travel with the ring loads
+// instead of being staged in LDS, as in the wide gate/up kernel: every 4
+// steps lane (r, q) of a tile loads the dword of its row holding the 4
+// block scales of step 4j + q, and at step 4j + u a bpermute from lane
+// (r, u) hands lane (r, q) byte q (the same byte, the same 2^(b-127), as a
+// staged scale).  The LDS it frees lets two wide workgroups share a CU.
+template <int TPW, int DW, int PF, int MAXC, bool SX4, bool BRES, int CS, bool SCR = false>
 __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
     int d, int f, int n_slots, const uint8_t *__restrict__ experts, int64_t stride, GroupSrc src,
     const int32_t *__restrict__ perm, int n_dtiles, const uint16_t *__restrict__ h_ws, float *__restrict__ y) {
@@ -907,6 +919,7 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
   constexpr int SPP = YC / kHParts;                   // slots per phase
   constexpr int NPH = (MAXC + SPP - 1) / SPP;         // epilogue phases
   constexpr int YP = YC + 1;                          // epilogue row pitch (floats)
+  static_assert(!SCR || (!BRES && 4 % PF == 0), "ring scales: ring mode, ring depth divides 4");
   extern __shared__ __align__(16) uint8_t lds[];
   const int item = xcd_item(group_count(src) * n_dtiles);
   if (item < 0) return;
@@ -926,8 +939,8 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
   const uint32_t hbase = (uint32_t)start * (uint32_t)(kHParts * f * 2);  // the group's first h row
   const int r0 = dt * ROWS;
   const uint32_t brow = bres_row_bytes(f);
-  const uint32_t dummy = (uint32_t)down_dummy_off(f, PF, MAXC, BRES, ROWS);
-  uint8_t *const bmem = lds + down_b_off(f, ROWS);  // B area (after the scale rows)
+  const uint32_t dummy = (uint32_t)down_dummy_off(f, PF, MAXC, BRES, ROWS, SCR);
+  uint8_t *const bmem = lds + down_b_off(f, ROWS, SCR);  // B area (after the scale rows)
   int bsel[NCBW];  // B row read by this lane in each of its column blocks
 #pragma unroll
   for (int cbl = 0; cbl < NCBW; ++cbl) {
@@ -947,12 +960,15 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
   }
   uint32_t aoff[TPW];
   const uint8_t *srow[TPW];  // this lane's LDS scale row per tile
+  uint32_t soff[TPW];        // SCR: this lane's scale dword of step q per tile
+  const int nb = f >> 5;
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     const int lrow = (rgw * TPW + t) * 16 + r;
     const int row = r0 + lrow;
     aoff[t] = sel_off(row < d, dn_c + code_off(src, row, r, q, f));
     srow[t] = lds + lrow * sc_pitch(f);
+    soff[t] = sel_off(row < d, dn_s + (uint32_t)row * (uint32_t)nb + 4u * q);
   }
   f32x4 acc[TPW][NCBW];
 #pragma unroll
@@ -975,16 +991,27 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
       hst[p][i] = buf_load16(hr, pbase[i] + (k < f ? (uint32_t)(k * 2) : kDead));
     }
   };
+  // SCR: the scale dwords of step group j (4 steps); a padding step's dword
+  // would lie past the row's f/32 scale bytes, so such lanes read past the
+  // resource (zero bytes) instead (see the wide gate/up kernel)
+  const int ngroups4 = (nsteps + 3) >> 2;
+  uint32_t sc_cur[TPW], sc_nxt[TPW];
+  auto load_sc = [&](int j, uint32_t (&scv)[TPW]) {
+    const uint32_t js = (j < ngroups4 && 4 * j + q < nsteps) ? 16u * (uint32_t)j : kDead;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) scv[t] = buf_load4(wr, soff[t] + js);
+  };
   // scale staging loads, then the ring prefill, one wait (see the gate/up kernel)
   const int rv = d - r0 < ROWS ? d - r0 : ROWS;
   ScaleStage<SX4, !BRES> ss;
-  ss.begin(wr, dn_s, r0, rv, ROWS, f, tid, NTH);
+  if constexpr (SCR) load_sc(0, sc_cur);
+  else ss.begin(wr, dn_s, r0, rv, ROWS, f, tid, NTH);
 #pragma unroll
   for (int p = 0; p < PF; ++p) issue(p, p);
   asm volatile("" ::: "memory");
   if constexpr (!BRES) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   asm volatile("" ::: "memory");
-  ss.end(wr, dn_s, r0, rv, ROWS, f, lds, dummy, lds, tid, NTH);
+  if constexpr (!SCR) ss.end(wr, dn_s, r0, rv, ROWS, f, lds, dummy, lds, tid, NTH);
   if constexpr (BRES) {
     // the group's nc h rows for the whole f, all loads of a round issued first
     constexpr int CH = 8;
@@ -1011,18 +1038,18 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
     lds_barrier();
   }
 
-  const int nsteps_pad = (nsteps + PF - 1) / PF * PF;  // see the gate/up kernel
-  for (int s0 = 0; s0 < nsteps_pad; s0 += PF) {
-#pragma unroll
-    for (int p = 0; p < PF; ++p) {
-      const int s = s0 + p;
+  // one step: stage B of step s into ring slot p, then its MFMAs, then the
+  // refill of slot p.  The scales are the ring's (SCR: sc_ring) or read from
+  // LDS after the step's barrier, which on the first step also publishes the
+  // staged scale rows of every wave.
+  auto step = [&](int s, int p, const float (&sc_ring)[TPW]) {
 #pragma unroll
       for (int i = 0; i < SPT; ++i)
         *(u32x4 *)(tid + i * NTH < NPIECE ? bmem + (p * NC + prow[i]) * kBRow + pel[i] * 2 : lds + dummy) = hst[p][i];
       if constexpr (!BRES) lds_barrier();
       float sc[TPW];
 #pragma unroll
-      for (int t = 0; t < TPW; ++t) sc[t] = lds_scale(srow[t], s, q);
+      for (int t = 0; t < TPW; ++t) sc[t] = SCR ? sc_ring[t] : lds_scale(srow[t], s, q);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         bf16x8 a[TPW];
@@ -1048,6 +1075,31 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
       // keep the refill here: the scheduler would otherwise sink it past the
       // next steps' waits and drain the ring once per unrolled window
       __builtin_amdgcn_sched_barrier(0);
+  };
+  if constexpr (SCR) {
+    // whole groups of 4 steps: steps past f load zeros and add exact zeros
+    int j = 0;
+    do {
+      load_sc(j + 1, sc_nxt);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        float sc[TPW];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+          const uint32_t w = (uint32_t)__builtin_amdgcn_ds_bpermute((r + 16 * u) * 4, (int)sc_cur[t]);
+          sc[t] = e8m0_to_f32((w >> (8 * q)) & 0xFFu);
+        }
+        step(4 * j + u, u % PF, sc);
+      }
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) sc_cur[t] = sc_nxt[t];
+    } while (++j < ngroups4);
+  } else {
+    const int nsteps_pad = (nsteps + PF - 1) / PF * PF;  // see the gate/up kernel
+    const float none[TPW] = {};
+    for (int s0 = 0; s0 < nsteps_pad; s0 += PF) {
+#pragma unroll
+      for (int p = 0; p < PF; ++p) step(s0 + p, p, none);
     }
   }
 
@@ -1055,7 +1107,7 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
   // past their last B read at the first barrier), SPP slots (YC columns) per
   // phase; each slot's part sums are added in a fixed order and its
   // rows written as float4
-  float *ys = (float *)(lds + down_y_off(f, PF, MAXC, BRES, ROWS));
+  float *ys = (float *)(lds + down_y_off(f, PF, MAXC, BRES, ROWS, SCR));
 #pragma unroll
   for (int ph = 0; ph < NPH; ++ph) {
     lds_barrier();
@@ -1177,18 +1229,19 @@ static int launch_gateup_wide(const void *x, int d, int f, int kps, int T, const
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
-template <int TPW, int DW, int PF, int MAXC, bool SX4, bool BRES, int CS>
+template <int TPW, int DW, int PF, int MAXC, bool SX4, bool BRES, int CS, bool SCR = false>
 static int launch_down(int d, int f, int T, const uint8_t *experts, int64_t stride, const GroupSrc &src,
                        const int32_t *perm, int64_t maxg, const uint16_t *h_ws, float *y, hipStream_t stream) {
   constexpr int ROWS = DW / CS * TPW * 16;
   const int n_dtiles = (d + ROWS - 1) / ROWS;
   if (maxg <= 0) return 0;
-  const size_t smem = down_lds_bytes(f, PF, MAXC, BRES, ROWS);
+  if (SCR && f % 128) return -3;
+  const size_t smem = down_lds_bytes(f, PF, MAXC, BRES, ROWS, SCR);
   if (smem > (size_t)kMaxLds) return -3;
   static const bool lds_ok =
-      allow_lds(reinterpret_cast<const void *>(&ffn_down_kernel<TPW, DW, PF, MAXC, SX4, BRES, CS>));
+      allow_lds(reinterpret_cast<const void *>(&ffn_down_kernel<TPW, DW, PF, MAXC, SX4, BRES, CS, SCR>));
   if (!lds_ok) return -3;
-  hipLaunchKernelGGL((ffn_down_kernel<TPW, DW, PF, MAXC, SX4, BRES, CS>), dim3((unsigned)align_up((size_t)(maxg * n_dtiles), kXcds)), dim3(DW * 64), smem,
+  hipLaunchKernelGGL((ffn_down_kernel<TPW, DW, PF, MAXC, SX4, BRES, CS, SCR>), dim3((unsigned)align_up((size_t)(maxg * n_dtiles), kXcds)), dim3(DW * 64), smem,
                      stream, d, f, T, experts, stride, src, perm, n_dtiles, h_ws, y);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
@@ -1270,6 +1323,11 @@ int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *exper
                                                                   cap[0], h_ws, stream, *route))
 #define MOE_GUW(XB, G, P, NCB, CL) \
   launch_gateup_wide<XB, G, P, NCB>(x, d, f, kps, T_, experts, stride, src[CL], perm, cap[CL], h_ws, stream)
+#define MOE_DNR(T, D, P, C, CL, CS)                                                                                    \
+  (dsx4 ? launch_down<T, D, P, C, true, false, CS, true>(d, f, T_, experts, stride, src[CL], perm, cap[CL], h_ws, y,     \
+                                                          stream)                                                       \
+        : launch_down<T, D, P, C, false, false, CS, true>(d, f, T_, experts, stride, src[CL], perm, cap[CL], h_ws, y,    \
+                                                           stream))
 #define MOE_DN(T, D, P, C, R, CL, CS)                                                                                   \
   (dsx4 ? launch_down<T, D, P, C, true, R, CS>(d, f, T_, experts, stride, src[CL], perm, cap[CL], h_ws, y, stream) \
         : launch_down<T, D, P, C, false, R, CS>(d, f, T_, experts, stride, src[CL], perm, cap[CL], h_ws, y, stream))
@@ -1312,14 +1370,21 @@ int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *exper
     if (M == 1 && down_lds_bytes(f, 4, 1, true, 256) <= half) rc = MOE_DN(2, 8, 4, 1, true, 0, 1);
     else if (M <= 4 && down_lds_bytes(f, 4, 4, true, 128) <= half) rc = MOE_DN(1, 8, 4, 4, true, 0, 1);
     else if (M <= kGroupCols) rc = MOE_DN(2, 8, 4, 16, false, 0, 1);
-    else rc = MOE_DN(4, 8, 2, 16, false, 0, 1);
-    if (!rc && wide) rc = MOE_DN(4, 8, 4, 32, false, 1, 2);
-    if (!rc && wide) rc = MOE_DN(4, 8, 2, 64, false, 2, 2);
+    // more rows (the prefill's narrow groups): scales through the ring where
+    // f % 128 == 0 (measured 4.90 -> 4.84 ms at 1,533 rows; at 16 rows the
+    // staged scales are faster, 191.5 against 197.6 us)
+    else rc = f % 128 == 0 ? MOE_DNR(4, 8, 2, 16, 0, 1) : MOE_DN(4, 8, 2, 16, false, 0, 1);
+    // the wide groups (MFMA-bound): scales through the ring where f % 128 == 0
+    // (two workgroups a CU), else staged
+    const bool scr = f % 128 == 0;
+    if (!rc && wide) rc = scr ? MOE_DNR(4, 8, 4, 32, 1, 2) : MOE_DN(4, 8, 4, 32, false, 1, 2);
+    if (!rc && wide) rc = scr ? MOE_DNR(4, 8, 2, 64, 2, 2) : MOE_DN(4, 8, 2, 64, false, 2, 2);
   }
 #undef MOE_GU
 #undef MOE_GUR
 #undef MOE_GUW
 #undef MOE_DN
+#undef MOE_DNR
   return rc;
 }
 

@@ -271,6 +271,10 @@ def test_ffn_ragged_parity(shape, M):
 WIDE = [
     synth.LayerShape("w1", 256, 96, 5, 1, 2, -6, -2, 0.05, "f32"),
     synth.LayerShape("w2", 384, 160, 6, 1, 2, -6, -2, 0.05, "bf16"),
+    # f % 128 == 0: the wide down kernels take their scales through the ring
+    # (one 128-element step plus three padding steps; three steps)
+    synth.LayerShape("w3", 256, 128, 5, 1, 2, -6, -2, 0.05, "bf16"),
+    synth.LayerShape("w4", 384, 384, 6, 1, 2, -6, -2, 0.05, "f32"),
 ]
 
 
