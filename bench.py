@@ -648,6 +648,18 @@ def main():
             lg_p = [torch.from_numpy(synth.zipf_logits(shp, 2000 + s, Mp)).to(dev) for s in range(3)]
             r = run_workload(Mp, xs_p, lg_p, 12, 2, graphs=False)
             res = layer_result(Mp, r)
+            # the router on the same rows (the workload gives logits; a prompt
+            # pass computes them): logits, top-k and weights
+            lgo = torch.empty((Mp, shp.n_routed), dtype=torch.float32, device=dev)
+            ids_o = torch.empty((Mp, shp.k), dtype=torch.int32, device=dev)
+            w_o = torch.empty((Mp, shp.k), dtype=torch.float32, device=dev)
+
+            def route(i):
+                moe.moe_route(xs_p[i % len(xs_p)], layers[i % L][1], lgo, shp.k, ids_o, w_o, stream=stream)
+
+            for i in range(2):
+                route(i)
+            res["router_us"] = timer.region(route, 12) * 1e3
             flops = 2.0 * Mp * (shp.k + shp.n_shared) * 3 * shp.d * shp.f
             res.update(useful_TFLOPs=flops / (res["ms_per_layer"] / 1e3) / 1e12,
                        mfma_frac=flops / (res["ms_per_layer"] / 1e3) / 1e12 / MFMA_BF16_PEAK_TFS,
@@ -655,7 +667,7 @@ def main():
             results[f"prefill_{Mp}rows"] = res
             log(f"[bench] prefill {Mp}: {res['ms_per_layer']:.3f} ms/layer, experts {res['experts_read']:.0f}, "
                 f"{res['useful_TFLOPs']:.1f} TFLOP/s, gate/up {res['gateup_us'] / 1e3:.3f} ms, "
-                f"ffn {res['ffn_us'] / 1e3:.3f} ms")
+                f"ffn {res['ffn_us'] / 1e3:.3f} ms; router on these rows {res['router_us']:.1f} us")
 
     # ------------------------------------------------------------ Q8_0 spine matmul
     if "q8_0" in only:

@@ -139,6 +139,167 @@ __global__ __launch_bounds__(LG_THREADS) void router_logits_kernel(const void *_
   }
 }
 
+// ------------------------------------------------------------------ logits on MFMA (more than 16 rows)
+// logits[m, e] = sum_c W_r[e, c] x[m, c] on bf16 MFMA with fp32 accumulation
+// and exact products: every fp32 weight is split exactly into three bf16
+// parts (split3_x8), bf16 x is used as is and fp32 x is split into three
+// parts as well.  The reduction over d is cut into slices of 32 elements;
+// slice c belongs to range q = c mod 16.  Range q's partial sum P_q is one
+// MFMA accumulator chain over its slices in ascending order, each slice
+// adding W_hi, W_mid, W_lo times each x part in the order (x part, W part).
+// The logit is ((P_0 + P_1) + P_2) + ... + P_15 in fp32.  That arithmetic
+// depends on d alone: the rows of one call do not influence each other (an
+// MFMA output element depends only on its own A row, B column and
+// accumulator).  Calls of up to 16 rows use the VALU form above, whose
+// summation order differs: a row's logits agree across the two forms within
+// rounding, not bit for bit (prefill rows are compared within tolerance).
+// Workgroup = one wave: 16 TR router rows x 16 TX x rows.  The ranges run
+// one after another (each chain is the same sequence of MFMAs as with all
+// ranges interleaved), so a tile needs only the running chain and the sum
+// of the finished ranges; per slice TR A fragments (W, three parts) and TX B
+// fragments, a ring of NR slices in flight.
+constexpr int kRqRanges = 16;
+constexpr int kRqMaxRows = 16;  // calls of up to this many rows take the VALU form
+
+// Three bf16 parts of 8 fp32 values, v == hi + mid + lo exactly: hi is v
+// truncated to its top 16 bits, r = v - hi is exact, mid is r truncated and
+// lo = r - mid is exact and has at most 8 significant bits (v has 24), so it
+// is a bf16 value.  A part's bf16 is the top half of its fp32 bits.
+__device__ __forceinline__ void split3_x8(const float (&v)[8], bf16x8 &hi, bf16x8 &mid, bf16x8 &lo) {
+  u32x4 h, m, l;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint32_t hb[2], mb[2], lb[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint32_t u = __float_as_uint(v[2 * e + t]);
+      hb[t] = u & 0xFFFF0000u;
+      const float r = v[2 * e + t] - __uint_as_float(hb[t]);
+      mb[t] = __float_as_uint(r) & 0xFFFF0000u;
+      lb[t] = __float_as_uint(r - __uint_as_float(mb[t]));
+    }
+    // high halves of two fp32 words -> one dword of two bf16 (element 2e low)
+    h[e] = __builtin_amdgcn_perm(hb[1], hb[0], 0x07060302u);
+    m[e] = __builtin_amdgcn_perm(mb[1], mb[0], 0x07060302u);
+    l[e] = __builtin_amdgcn_perm(lb[1], lb[0], 0x07060302u);
+  }
+  hi = bits_to_bf16x8(h);
+  mid = bits_to_bf16x8(m);
+  lo = bits_to_bf16x8(l);
+}
+
+// The x parts' order in a chain, then the W parts' (both forms).
+template <int NP>
+__device__ __forceinline__ f32x4 rq_chain(const bf16x8 (&a)[3], const bf16x8 (&b)[NP], f32x4 acc) {
+#pragma unroll
+  for (int p = 0; p < NP; ++p)
+#pragma unroll
+    for (int w = 0; w < 3; ++w) acc = mfma16x16x32(a[w], b[p], acc);
+  return acc;
+}
+
+template <int XBF16, int NR, int TR, int TX>
+__global__ __launch_bounds__(64) void router_mfma_tile_kernel(const void *__restrict__ x, const float *__restrict__ w,
+                                                              int M, int d, int E, float *__restrict__ logits) {
+  constexpr int NP = XBF16 ? 1 : 3;
+  constexpr int EL = XBF16 ? 2 : 4;
+  static_assert(kRqRanges % NR == 0, "the ring depth divides a range round");
+  const int lane = threadIdx.x & 63;
+  const int i = lane & 15, kg = lane >> 4;
+  const int e0 = blockIdx.x * 16 * TR, m0 = blockIdx.y * 16 * TX;
+  const int nsl = d / 32;
+  const int nper = (nsl + kRqRanges - 1) / kRqRanges;  // slices per range, the last ones past d are zeros
+  const int total = kRqRanges * nper;
+  const rsrc_t wres = make_rsrc(w, (uint32_t)((int64_t)E * d * 4));
+  const rsrc_t xres = make_rsrc(x, (uint32_t)((int64_t)M * d * EL));
+  uint32_t wbase[TR], xbase[TX];
+#pragma unroll
+  for (int tr = 0; tr < TR; ++tr) {
+    const int e = e0 + 16 * tr + i;
+    wbase[tr] = e < E ? (uint32_t)e * (uint32_t)(d * 4) + (uint32_t)(8 * kg) * 4u : kOOB;
+  }
+#pragma unroll
+  for (int tx = 0; tx < TX; ++tx) {
+    const int m = m0 + 16 * tx + i;
+    xbase[tx] = m < M ? (uint32_t)m * (uint32_t)(d * EL) + (uint32_t)(8 * kg * EL) : kOOB;
+  }
+  u32x4 wr[NR][TR][2], xr[NR][TX][EL / 2];
+  // iteration it = range q, its r-th slice c = q + 16 r (ranges outermost)
+  auto issue = [&](int it, int p) {
+    const int q = it / nper, r = it - q * nper, c = q + kRqRanges * r;
+    const bool ok = it < total && c < nsl;
+#pragma unroll
+    for (int tr = 0; tr < TR; ++tr) {
+      const uint32_t o = ok ? wbase[tr] + (uint32_t)c * 128u : kOOB;
+      wr[p][tr][0] = buf_load16(wres, o);
+      wr[p][tr][1] = buf_load16(wres, o + 16);
+    }
+#pragma unroll
+    for (int tx = 0; tx < TX; ++tx) {
+      const uint32_t o = ok ? xbase[tx] + (uint32_t)c * (uint32_t)(32 * EL) : kOOB;
+#pragma unroll
+      for (int h = 0; h < EL / 2; ++h) xr[p][tx][h] = buf_load16(xres, o + 16 * h);
+    }
+  };
+  f32x4 acc[TR][TX], sum[TR][TX];
+#pragma unroll
+  for (int tr = 0; tr < TR; ++tr)
+#pragma unroll
+    for (int tx = 0; tx < TX; ++tx) acc[tr][tx] = sum[tr][tx] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < NR; ++p) issue(p, p);
+  for (int it0 = 0; it0 < total; it0 += NR) {
+#pragma unroll
+    for (int p = 0; p < NR; ++p) {
+      const int it = it0 + p;
+      bf16x8 a[TR][3];
+#pragma unroll
+      for (int tr = 0; tr < TR; ++tr) {
+        float wv8[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) wv8[t] = __uint_as_float(wr[p][tr][t >> 2][t & 3]);
+        split3_x8(wv8, a[tr][0], a[tr][1], a[tr][2]);
+      }
+#pragma unroll
+      for (int tx = 0; tx < TX; ++tx) {
+        bf16x8 b[NP];
+        if constexpr (XBF16) {
+          b[0] = bits_to_bf16x8(xr[p][tx][0]);
+        } else {
+          float xv8[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) xv8[t] = __uint_as_float(xr[p][tx][t >> 2][t & 3]);
+          split3_x8(xv8, b[0], b[1], b[2]);
+        }
+#pragma unroll
+        for (int tr = 0; tr < TR; ++tr) acc[tr][tx] = rq_chain<NP>(a[tr], b, acc[tr][tx]);
+      }
+      issue(it + NR, p);
+      if ((it + 1) % nper == 0) {  // range q = it / nper is complete: add it in range order
+        const bool first = it < nper;
+#pragma unroll
+        for (int tr = 0; tr < TR; ++tr)
+#pragma unroll
+          for (int tx = 0; tx < TX; ++tx) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) sum[tr][tx][t] = first ? acc[tr][tx][t] : sum[tr][tx][t] + acc[tr][tx][t];
+            acc[tr][tx] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+      }
+    }
+  }
+  // lane (j, g) holds D[4 g + t][j]: router row e0 + 16 tr + 4 g + t, x row m0 + 16 tx + j
+#pragma unroll
+  for (int tr = 0; tr < TR; ++tr)
+#pragma unroll
+    for (int tx = 0; tx < TX; ++tx)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int e = e0 + 16 * tr + 4 * kg + t, m = m0 + 16 * tx + i;
+        if (e < E && m < M) logits[(int64_t)m * E + e] = sum[tr][tx][t];
+      }
+}
+
 // ------------------------------------------------------------------ top-k
 // One wave per row (topk_row), TK_WAVES rows per workgroup.
 constexpr int TK_WAVES = 4;
@@ -168,6 +329,20 @@ static void launch_topk(const float *logits, int M, int E, int k, int32_t *ids, 
 }
 
 template <int XBF16>
+static void launch_logits_mfma(const void *x, const float *w_router, float *logits, int M, int d, int E,
+                               hipStream_t stream) {
+  // tiles per wave by row count (measured at E = 896, d = 7168: 2 x 4 at
+  // 1,533 rows 166 us, 1 x 2 at 270 rows 67 us); the arithmetic of a logit
+  // does not depend on it
+  if (M > 768)
+    hipLaunchKernelGGL((router_mfma_tile_kernel<XBF16, 4, 2, 4>), dim3((E + 31) / 32, (M + 63) / 64), dim3(64), 0,
+                       stream, x, w_router, M, d, E, logits);
+  else
+    hipLaunchKernelGGL((router_mfma_tile_kernel<XBF16, 4, 1, 2>), dim3((E + 15) / 16, (M + 31) / 32), dim3(64), 0,
+                       stream, x, w_router, M, d, E, logits);
+}
+
+template <int XBF16>
 static void launch_logits(const void *x, const float *w_router, float *logits, int M, int d, int E,
                           hipStream_t stream) {
   // pass shapes by row count (measured on MI355X at E = 896, d = 7168: two
@@ -187,8 +362,13 @@ static void launch_logits(const void *x, const float *w_router, float *logits, i
 
 int logits_launch(const void *x, int x_bf16, const float *w_router, float *logits, int M, int d, int E,
                   hipStream_t stream) {
-  if (x_bf16) launch_logits<1>(x, w_router, logits, M, d, E, stream);
-  else launch_logits<0>(x, w_router, logits, M, d, E, stream);
+  if (M > kRqMaxRows) {
+    if (x_bf16) launch_logits_mfma<1>(x, w_router, logits, M, d, E, stream);
+    else launch_logits_mfma<0>(x, w_router, logits, M, d, E, stream);
+  } else {
+    if (x_bf16) launch_logits<1>(x, w_router, logits, M, d, E, stream);
+    else launch_logits<0>(x, w_router, logits, M, d, E, stream);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

@@ -126,6 +126,50 @@ def test_route_given_logits_exact(M, E, k):
     assert_close(_host(w), w_ref, "topk weights")
 
 
+ROUTER_SHAPES = [
+    synth.KIMI,
+    synth.LayerShape("r3", 416, 224, 9, 2, 4, -7, -3, 0.05, "bf16"),
+    synth.LayerShape("f32", 256, 128, 16, 0, 2, -6, -2, 0.05, "f32"),
+    synth.LayerShape("odd", 1056, 64, 37, 0, 3, -6, -2, 0.05, "bf16"),
+]
+
+
+@pytest.mark.parametrize("shape", ROUTER_SHAPES, ids=lambda s: s.name)
+def test_router_logits_rows_equal_single_rows(shape):
+    """Router logits: every row of a call of up to 16 rows equals the same
+    row computed alone, bit for bit; above 16 rows (the MFMA form) the rows
+    of one call equal the same rows in another call of more than 16 rows
+    bit for bit, and the single-row logits within the bar; all agree with
+    the oracle within the bar."""
+    moe = _moe()
+    wr = synth.router_weight(shape, 61)
+    dwr = _dev(wr)
+    x = synth.rows_x(shape, 62, 150)
+    xd = _x_dev(shape, x)
+    E, k = shape.n_routed, shape.k
+
+    def logits(rows):
+        M = rows.shape[0]
+        lg = torch.empty((M, E), dtype=torch.float32, device="cuda")
+        ids = torch.empty((M, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((M, k), dtype=torch.float32, device="cuda")
+        moe.moe_route(rows, dwr, lg, k, ids, w)
+        return _host(lg)
+
+    single = np.stack([logits(xd[m:m + 1])[0] for m in range(150)])
+    ref = oracle.router_logits(x, wr)
+    assert_close(single, ref, f"{shape.name} router logits")
+    for M in (2, 3, 5, 9, 16):
+        got = logits(xd[:M])
+        assert np.array_equal(got.view(np.uint32), single[:M].view(np.uint32)), (shape.name, M)
+    big = logits(xd)
+    assert_close(big, ref, f"{shape.name} router logits, 150 rows")
+    assert_close(big, single, f"{shape.name} 150-row logits against single rows")
+    for M in (17, 40, 64, 65):
+        got = logits(xd[:M])
+        assert np.array_equal(got.view(np.uint32), big[:M].view(np.uint32)), (shape.name, M)
+
+
 def test_route_zipf_prefill_logits_exact():
     moe = _moe()
     for M in (270, 1533):
