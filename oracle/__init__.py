@@ -44,6 +44,8 @@ def _load():
             "orc_e2m1": (ctypes.c_double, [ctypes.c_int]),
             "orc_e8m0": (ctypes.c_double, [ctypes.c_int]),
             "orc_fp16": (ctypes.c_double, [ctypes.c_uint16]),
+            "orc_e4m3": (ctypes.c_double, [ctypes.c_int]),
+            "orc_mx_tile": (ctypes.c_int, [P, P, P, P, P]),
             "orc_widen_bf16": (None, [P, i64, P]),
             "orc_expert_layout": (ctypes.c_int, [i64, i64, P]),
             "orc_mxfp4_dequant": (ctypes.c_int, [P, P, i64, i64, P]),
@@ -103,6 +105,24 @@ def e2m1(code: int) -> float:
 def e8m0(b: int) -> float:
     """E8M0 shared scale 2^(b-127); 255 is NaN."""
     return _load().orc_e8m0(int(b))
+
+
+def e4m3(code: int) -> float:
+    """OCP FP8 E4M3 code -> value (NaN for 0x7F / 0xFF)."""
+    return float(_load().orc_e4m3(int(code)))
+
+
+def mx_tile(a_codes: np.ndarray, a_scales: np.ndarray, b_codes: np.ndarray, b_scales: np.ndarray) -> np.ndarray:
+    """One MX-scaled 16 x 16 x 128 tile in fp64: A [16 x 64] E2M1 code bytes
+    with [16 x 4] E8M0 scales, B given as 16 columns of 128 E4M3 codes with
+    [16 x 4] E8M0 scales; returns D [16 x 16] float64."""
+    ops = [np.ascontiguousarray(a, dtype=np.uint8) for a in (a_codes, a_scales, b_codes, b_scales)]
+    for a, shp in zip(ops, ((16, 64), (16, 4), (16, 128), (16, 4))):
+        if a.shape != shp:
+            raise ValueError(f"mx_tile: operand of shape {a.shape}, expected {shp}")
+    d = np.empty((16, 16), dtype=np.float64)
+    _check(_load().orc_mx_tile(*[_ptr(a) for a in ops], _ptr(d)), "mx_tile")
+    return d
 
 
 def fp16(bits: int) -> float:

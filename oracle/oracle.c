@@ -84,6 +84,47 @@ double orc_e8m0(int b) {
   return ldexp(1.0, b - 127);
 }
 
+/* OCP FP8 E4M3 (an OCP MX v1.0 element type): sign, 4-bit exponent with bias
+ * 7, 3-bit mantissa; exponent 0 is subnormal (m * 2^-9); 0x7F and 0xFF are
+ * NaN; there are no infinities (the largest value is 448). */
+double orc_e4m3(int code) {
+  int sign = (code >> 7) & 1;
+  int e = (code >> 3) & 15;
+  int m = code & 7;
+  double mag;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    mag = ldexp((double)m, -9);
+  else
+    mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sign ? -mag : mag;
+}
+
+/* One MX-scaled matrix tile, 16 x 16 over K = 128, the arithmetic of an
+ * expert GEMM on MXFP4 weights with FP8 activations ("What is
+ * established—and what remains open": expert GEMM choices are an arithmetic
+ * path of their own):
+ *   D[i][j] = sum_k A[i][k] sA[i][k/32] * B[k][j] sB[j][k/32]
+ * A row i: 64 bytes of E2M1 codes (element 2c in the low nibble of byte c);
+ * B column j: 128 bytes of E4M3 codes; scales: 4 E8M0 bytes per row/column.
+ * The sum runs over ascending k in double precision. */
+int orc_mx_tile(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *b_codes, const uint8_t *b_scales,
+                double *d) {
+  if (!a_codes || !a_scales || !b_codes || !b_scales || !d) return ORC_EINVAL;
+  for (int i = 0; i < 16; ++i)
+    for (int j = 0; j < 16; ++j) {
+      double s = 0.0;
+      for (int k = 0; k < 128; ++k) {
+        const int byte = a_codes[i * 64 + k / 2];
+        const double a = orc_e2m1((k & 1) ? (byte >> 4) : (byte & 15)) * orc_e8m0(a_scales[i * 4 + k / 32]);
+        const double b = orc_e4m3(b_codes[j * 128 + k]) * orc_e8m0(b_scales[j * 4 + k / 32]);
+        s += a * b;
+      }
+      d[i * 16 + j] = s;
+    }
+  return ORC_OK;
+}
+
 /* IEEE binary16 bits to double, written out from the format definition. */
 double orc_fp16(uint16_t h) {
   int sign = (h >> 15) & 1;

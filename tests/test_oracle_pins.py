@@ -556,3 +556,67 @@ def test_f32_and_f64_readings_agree_at_kimi_shape():
         ys32.append(y32)
     X, (wq, ws) = synth.q8_0_x(4, 1, 7168), synth.q8_0_weight(4, 7168, 2048)
     assert rel_l2(oracle.q8_0_matmul(X, wq, ws, accum="f32"), oracle.q8_0_matmul(X, wq, ws)) <= 1e-6
+
+
+# ----------------------------------------------------------------------------- MX-scaled tile
+def test_e4m3_values_from_the_format():
+    """OCP FP8 E4M3: bias 7, 3 mantissa bits, subnormals m * 2^-9, no
+    infinities, 0x7F/0xFF NaN, largest 448."""
+    assert oracle.e4m3(0x38) == 1.0 and oracle.e4m3(0xB8) == -1.0
+    assert oracle.e4m3(0x7E) == 448.0 and oracle.e4m3(0xFE) == -448.0
+    assert oracle.e4m3(0x08) == 2.0 ** -6 and oracle.e4m3(0x07) == 7 * 2.0 ** -9 and oracle.e4m3(0x01) == 2.0 ** -9
+    assert oracle.e4m3(0x00) == 0.0 and math.copysign(1.0, oracle.e4m3(0x80)) == -1.0
+    assert math.isnan(oracle.e4m3(0x7F)) and math.isnan(oracle.e4m3(0xFF))
+    pos = [oracle.e4m3(c) for c in range(0x7F)]
+    assert all(a < b for a, b in zip(pos, pos[1:]))  # positive codes are ordered by value
+    assert all(oracle.e4m3(c | 0x80) == -oracle.e4m3(c) for c in range(0x7F))
+    # 4 significant bits: every value is an integer multiple of its binade's step
+    for c in range(1, 0x7F):
+        v = pos[c]
+        step = 2.0 ** (max(math.floor(math.log2(v)), -6) - 3)
+        assert v / step == int(v / step)
+
+
+def _mx_ops(seed):
+    g = np.random.default_rng(seed)
+    return (np.zeros((16, 64), np.uint8), np.full((16, 4), 127, np.uint8),
+            g.integers(0, 0x7F, (16, 128)).astype(np.uint8), np.full((16, 4), 127, np.uint8))
+
+
+def test_mx_tile_one_hot_rows_and_column_scales():
+    """A row i = 1.0 at k = i (E2M1 code 2 in the low nibble for even k, the
+    high one for odd k): D[i][j] = B[i][j] * sB[j][0]."""
+    a, sa, b, sb = _mx_ops(1)
+    for i in range(16):
+        a[i, i // 2] = 2 << (4 * (i & 1))
+    sb[:, 0] = 127 + (np.arange(16) % 3)
+    d = oracle.mx_tile(a, sa, b, sb)
+    for i in range(16):
+        for j in range(16):
+            assert d[i, j] == oracle.e4m3(b[j, i]) * 2.0 ** (j % 3), (i, j)
+
+
+def test_mx_tile_block_scales_cover_their_32_elements():
+    """A row i = 1.0 at k = 32 (i % 4) + i // 4 with sA[i][blk] = 2^blk and
+    sB[j][blk] = 2^-blk: D[i][j] = B[k][j] (the two scales of that block)."""
+    a, sa, b, sb = _mx_ops(2)
+    for i in range(16):
+        k = 32 * (i % 4) + i // 4
+        a[i, k // 2] = 2 << (4 * (k & 1))
+    sa[:] = 127 + np.arange(4)[None, :]
+    sb[:] = 127 - np.arange(4)[None, :]
+    d = oracle.mx_tile(a, sa, b, sb)
+    for i in range(16):
+        k = 32 * (i % 4) + i // 4
+        for j in range(16):
+            assert d[i, j] == oracle.e4m3(b[j, k]), (i, j)
+
+
+def test_mx_tile_nibble_order_and_sum():
+    """Byte c of an A row holds element 2c (low nibble) and 2c+1 (high):
+    codes 2 (1.0) low and 4 (2.0) high in byte 0 give B[0] + 2 B[1]."""
+    a, sa, b, sb = _mx_ops(3)
+    a[:, 0] = 2 | (4 << 4)
+    d = oracle.mx_tile(a, sa, b, sb)
+    for j in range(16):
+        assert d[0, j] == oracle.e4m3(b[j, 0]) + 2 * oracle.e4m3(b[j, 1])
