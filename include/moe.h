@@ -20,8 +20,13 @@
  *  - M = 0 rows is valid and enqueues nothing.
  *  - Rows of one call never influence each other's results: the result of a
  *    row is bit-identical whether it is alone (M = 1) or inside a block of
- *    any M, for every function here (the verification blocks of "A drafter
- *    that leaves the answer unchanged" must reproduce one-row steps exactly).
+ *    up to 16 rows, for every function here (the verification blocks of "A
+ *    drafter that leaves the answer unchanged" must reproduce one-row steps
+ *    exactly), and bit-identical across calls of any M for every function
+ *    but the router logits: moe_route's logits in calls of more than 16 rows
+ *    (a matrix-core form with another summation order) equal each other
+ *    across such calls bit for bit and the one-row logits within rounding.
+ *    Everything after the logits is bit-identical for the same logits.
  *
  * MXFP4 storage (OCP MX v1.0 elements; the byte layout is this library's
  * data contract, the pages give only the format name and the 17,547,264-byte
@@ -353,6 +358,24 @@ int moe_argmax_rows(const float *X, int32_t M, int32_t N, int32_t *idx, void *st
  * 0x100000001b3) of the 4*N bytes of row m of X [M x N] fp32, in memory order.
  * A sequential recurrence: one thread per row, milliseconds for long rows. */
 int moe_fnv1a_rows(const float *X, int32_t M, int32_t N, uint64_t *hash, void *stream);
+
+/* One MX-scaled matrix-core instruction (gfx950 v_mfma_scale_f32_16x16x128_f8f6f4),
+ * the building block of an expert GEMM on MXFP4 weights without a bf16
+ * decode ("What is established—and what remains open": expert GEMM choices
+ * are an arithmetic path of their own).  The FFN kernels above do not use
+ * it; this entry point exists so that its arithmetic can be measured:
+ *   D[i][j] = sum_{k<128} A[i][k] sA[i][k/32] B[k][j] sB[j][k/32]
+ * with the instruction's own summation and rounding, fp32 out.
+ *   a_codes   [16 x 64] bytes: A row i, K 0..127 as E2M1 codes, element 2c
+ *             in the low nibble of byte c (the MXFP4 codes layout above).
+ *   a_scales  [16 x 4] E8M0 bytes: scale of row i, K block b (32 elements).
+ *   b_codes   [16 x 128] bytes: B column j, K 0..127, one OCP FP8 E4M3 code
+ *             per byte (bias 7, no infinities, 0x7F/0xFF NaN).
+ *   b_scales  [16 x 4] E8M0 bytes: scale of column j, K block b.
+ *   d         [16 x 16] fp32 out, row-major.
+ * One wave on `stream`; a_codes and b_codes 16-byte aligned. */
+int moe_mx_mfma_probe(const uint8_t *a_codes, const uint8_t *a_scales, const uint8_t *b_codes,
+                      const uint8_t *b_scales, float *d, void *stream);
 
 /* Human-readable name of a status code (static string). */
 const char *moe_status_str(int status);

@@ -26,7 +26,8 @@ ABI_FUNCTIONS = ("moe_route", "moe_bucket", "moe_expert_ffn_mxfp4", "moe_ffn_gat
                  "moe_workspace_bytes", "moe_pack_experts", "moe_combine", "moe_layer_mxfp4", "moe_layer_mxfp4_noalloc",
                  "moe_noalloc_scratch_bytes", "moe_cache_create", "moe_cache_destroy",
                  "moe_cache_get_stats", "moe_layer_streamed", "moe_cache_simulate", "q8_0_matmul", "q8_0_matmul_layout", "q8_0_pack", "q8_0_rows",
-                 "moe_residual_bf16", "moe_rmsnorm", "moe_argmax_rows", "moe_fnv1a_rows", "moe_status_str")
+                 "moe_residual_bf16", "moe_rmsnorm", "moe_argmax_rows", "moe_fnv1a_rows", "moe_mx_mfma_probe",
+                 "moe_status_str")
 
 
 class MoeError(RuntimeError):
@@ -89,6 +90,7 @@ def _load() -> ctypes.CDLL:
         "moe_rmsnorm": (ctypes.c_int, [P, i32, i32, ctypes.c_float, P, P, P]),
         "moe_argmax_rows": (ctypes.c_int, [P, i32, i32, P, P]),
         "moe_fnv1a_rows": (ctypes.c_int, [P, i32, i32, P, P]),
+        "moe_mx_mfma_probe": (ctypes.c_int, [P, P, P, P, P, P]),
         "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sigs.items():
@@ -333,6 +335,19 @@ def moe_layer_mxfp4_noalloc(x, w_router, logits, k, experts: Experts, topk_ids, 
 def moe_noalloc_scratch_bytes() -> int:
     """Bytes of moe_layer_mxfp4_noalloc's static scratch array."""
     return int(_lib.moe_noalloc_scratch_bytes())
+
+
+def moe_mx_mfma_probe(a_codes, a_scales, b_codes, b_scales, d, stream=None):
+    """One MX-scaled matrix-core instruction: d [16 x 16] fp32 = A x B with
+    a_codes [16 x 64] E2M1 bytes, a_scales [16 x 4] E8M0, b_codes [16 x 128]
+    E4M3 bytes (column-major B), b_scales [16 x 4] E8M0 (uint8 tensors)."""
+    for t, shp in ((a_codes, (16, 64)), (a_scales, (16, 4)), (b_codes, (16, 128)), (b_scales, (16, 4))):
+        if t.dtype != torch.uint8 or tuple(t.shape) != shp or not t.is_contiguous():
+            raise ValueError(f"moe_mx_mfma_probe: contiguous uint8 {shp} operands")
+    if d.dtype != torch.float32 or tuple(d.shape) != (16, 16) or not d.is_contiguous():
+        raise ValueError("moe_mx_mfma_probe: d is a contiguous float32 [16 x 16]")
+    _check("moe_mx_mfma_probe", _lib.moe_mx_mfma_probe(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes), _ptr(b_scales),
+                                                       _ptr(d), _stream(stream)))
 
 
 def q8_0_pack(src, dst, to_layout, stream=None):

@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["capi.cpp", "cache.cpp", "route.hip", "bucket.hip", "ffn.hip", "q8_0.hip", "verify.hip", "pack.hip",
-           "noalloc.hip"]
+           "noalloc.hip", "mxprobe.hip"]
 ARCH = "gfx950"
 
 

@@ -345,13 +345,17 @@ static void launch_logits_mfma(const void *x, const float *w_router, float *logi
 template <int XBF16>
 static void launch_logits(const void *x, const float *w_router, float *logits, int M, int d, int E,
                           hipStream_t stream) {
-  // pass shapes by row count (measured on MI355X at E = 896, d = 7168: two
-  // router rows per workgroup halve the x re-reads against one and still give
-  // 448 workgroups, 2.3x faster than four at 1533 rows); the arithmetic of a
-  // logit does not change
+  // pass shapes by row count (measured on MI355X at E = 896, d = 7168, moe_route
+  // with top-k: 2-4 rows 4 router rows x 4 x rows x 4 chunks, 11.9 / 12.7 us
+  // against 12.8 / 13.4 for the 5-8-row shape; above 8 rows two router rows
+  // per workgroup halve the x re-reads against one and still give 448
+  // workgroups); the arithmetic of a logit does not change
   if (M == 1)
     hipLaunchKernelGGL((router_logits_kernel<XBF16, 1, 1, 8>), dim3(E), dim3(LG_THREADS), 0, stream, x, w_router, M,
                        d, E, logits);
+  else if (M <= 4)
+    hipLaunchKernelGGL((router_logits_kernel<XBF16, 4, 4, 4>), dim3((E + 3) / 4), dim3(LG_THREADS), 0, stream, x,
+                       w_router, M, d, E, logits);
   else if (M <= 8)
     hipLaunchKernelGGL((router_logits_kernel<XBF16, 2, 4, 8>), dim3((E + 1) / 2), dim3(LG_THREADS), 0, stream, x,
                        w_router, M, d, E, logits);
