@@ -234,7 +234,7 @@ __global__ __launch_bounds__(TB_MAX_ROWS * 64) void topk_bucket_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int32_t id;
   float wt;
-  topk_row<NPL>(logits + (int64_t)wv * E, E, k, (uint64_t(*)[64])(smem + (size_t)wv * topk_wave_lds(NPL)), lane, id,
+  topk_row_any<NPL>(logits + (int64_t)wv * E, E, k, (uint64_t(*)[64])(smem + (size_t)wv * topk_wave_lds(NPL)), lane, id,
                 wt);
   if (lane < k) {
     ids[(int64_t)wv * k + lane] = id;

@@ -130,7 +130,7 @@ __device__ int route_one_row(const RouteArgs &ra, int g, bool writer, uint8_t *l
   if (threadIdx.x < 64) {
     int32_t id;
     float wt;
-    topk_row<16>(ra.logits, ra.E, ra.k, (uint64_t(*)[64])lists, lane, id, wt);
+    topk_row_any<16>(ra.logits, ra.E, ra.k, (uint64_t(*)[64])lists, lane, id, wt);
     int pos = 0;  // ascending position of this lane's id among the k (distinct) ids
     for (int i = 0; i < ra.k; ++i) pos += __builtin_amdgcn_readlane(id, i) < id;
     const uint64_t hit = __ballot(lane < ra.k && pos == g);

@@ -314,7 +314,7 @@ __global__ __launch_bounds__(TK_WAVES * 64) void topk_kernel(const float *__rest
   if (m >= M) return;  // whole wave; the LDS lists are per wave, no barrier
   int32_t id;
   float wt;
-  topk_row<NPL>(logits + (int64_t)m * E, E, k, lists[wv], lane, id, wt);
+  topk_row_any<NPL>(logits + (int64_t)m * E, E, k, lists[wv], lane, id, wt);
   if (lane < k) {
     ids[(int64_t)m * k + lane] = id;
     w[(int64_t)m * k + lane] = wt;

@@ -65,6 +65,18 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return max(max(r0, r1), max(r2, r3));
 }
 
+// Lane j < k holds the logit and id of rank j: the weights
+// exp(l_j - l_0) / sum_{i<k} exp(l_i - l_0), the normaliser summed in rank order.
+__device__ __forceinline__ void topk_weights(float my_l, int32_t my_id, int lane, int k, int32_t &id_out,
+                                             float &w_out) {
+  const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_l), 0));
+  const float ej = (lane < k) ? expf(my_l - l0) : 0.f;
+  float z = 0.f;
+  for (int i = 0; i < k; ++i) z += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ej), i));
+  id_out = my_id;
+  w_out = ej / z;
+}
+
 // Keys per lane list: NPL rounded up to a power of two.
 __host__ __device__ constexpr int topk_list_len(int npl) {
   return npl <= 1 ? 1 : npl <= 2 ? 2 : npl <= 4 ? 4 : npl <= 8 ? 8 : npl <= 16 ? 16 : npl <= 32 ? 32 : 64;
@@ -127,12 +139,81 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ row, int E, i
       my_id = (int32_t)~lmax;
     }
   }
-  const float l0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_l), 0));
-  const float ej = (lane < k) ? expf(my_l - l0) : 0.f;
-  float z = 0.f;
-  for (int i = 0; i < k; ++i) z += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ej), i));
-  id_out = my_id;
-  w_out = ej / z;
+  topk_weights(my_l, my_id, lane, k, id_out, w_out);
+}
+
+// The same top-k by a threshold: every key is at most its lane's maximum, so
+// the k-th largest key is at least the k-th largest of the 64 lane maxima,
+// and in particular its top 16 bits are at least t, the k-th largest top 16
+// bits among the lane maxima (found by an MSB-first bitwise search with wave
+// ballots).  The keys whose top 16 bits are at least t are gathered in LDS;
+// when there are at most 64 of them (the usual case: logits that share the
+// threshold's sign, exponent and 7 mantissa bits are few) each is ranked by
+// counting the larger ones, else the list-based rounds above run.  Keys are
+// distinct, so the k largest and their order are the same either way, and the
+// weights are computed by the same code from the same values.  `lists`: at
+// least topk_wave_lds(NPL) bytes of this wave's LDS.
+template <int NPL>
+__device__ __forceinline__ void topk_row_fast(const float *__restrict__ row, int E, int k, uint64_t (*lists)[64],
+                                              int lane, int32_t &id_out, float &w_out) {
+  static_assert(NPL >= 2, "the candidate and ranked keys need 136 keys of LDS");
+  float v[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) v[i] = row[min(lane + 64 * i, E - 1)];
+  uint64_t key[NPL];
+  uint64_t m = 0ull;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = lane + 64 * i;
+    key[i] = e < E ? (((uint64_t)order_bits(v[i]) << 32) | (uint32_t)~(uint32_t)e) : 0ull;
+    m = max_u64(m, key[i]);
+  }
+  // t: the largest 16-bit value with at least k lane maxima at or above it
+  const uint32_t mh = (uint32_t)(m >> 48);
+  uint32_t t = 0;
+  for (int b = 15; b >= 0; --b) {
+    const uint32_t c = t | (1u << b);
+    if (__popcll(__ballot(mh >= c)) >= k) t = c;
+  }
+  // gather the keys at or above t (key 0 marks an entry past E); slots past
+  // the count read as key 0, which is below every real key
+  uint64_t *cand = &lists[0][0];  // [64 + 8] keys, then the k ranked keys
+  uint64_t *ranked = cand + 72;
+  cand[lane] = 0ull;
+  if (lane < 8) cand[64 + lane] = 0ull;
+  int n = 0;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const bool c = key[i] != 0ull && (uint32_t)(key[i] >> 48) >= t;
+    const uint64_t msk = __ballot(c);
+    const int slot = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(msk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)msk, 0u));
+    if (c && slot < 64) cand[slot] = key[i];
+    n += (int)__popcll(msk);
+  }
+  if (n > 64) {  // uniform: too many near the threshold
+    topk_row<NPL>(row, E, k, lists, lane, id_out, w_out);
+    return;
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+  // rank of candidate `lane`: the number of larger candidates
+  const uint64_t mine = lane < n ? cand[lane] : 0ull;
+  int rank = 0;
+  for (int j0 = 0; j0 < n; j0 += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) rank += cand[j0 + u] > mine;
+  }
+  if (lane < n && rank < k) ranked[rank] = mine;
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_wave_barrier();
+  float my_l = 0.f;
+  int32_t my_id = 0;
+  if (lane < k) {
+    const uint64_t kj = ranked[lane];
+    my_l = from_order_bits((uint32_t)(kj >> 32));
+    my_id = (int32_t)~(uint32_t)kj;
+  }
+  topk_weights(my_l, my_id, lane, k, id_out, w_out);
 }
 
 // Bucketing of one row in one wave, from its top-k ids (lane j < k holds
@@ -168,6 +249,18 @@ __device__ __forceinline__ void bucket_one_row(int32_t id, int lane, int E, int 
     *n_active = kps;
     *dev_error = 0;
   }
+}
+
+// The ranking every kernel uses: the threshold form where a lane holds two or
+// more logits, the list rounds otherwise (their LDS is too small for the
+// threshold form's 136 keys).  Both give the same ids and weights.
+template <int NPL>
+__device__ __forceinline__ void topk_row_any(const float *__restrict__ row, int E, int k, uint64_t (*lists)[64],
+                                             int lane, int32_t &id_out, float &w_out) {
+  if constexpr (NPL >= 2)
+    topk_row_fast<NPL>(row, E, k, lists, lane, id_out, w_out);
+  else
+    topk_row<NPL>(row, E, k, lists, lane, id_out, w_out);
 }
 
 }  // namespace moe

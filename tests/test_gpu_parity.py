@@ -126,6 +126,53 @@ def test_route_given_logits_exact(M, E, k):
     assert_close(_host(w), w_ref, "topk weights")
 
 
+def _near_threshold_logits(g, M, E, n_near):
+    """Rows of logits in [-1, 0.9) with n_near of them set to 1 + i 2^-20
+    (distinct values that share their top 16 order bits), in n_near distinct
+    lanes (index mod 64) while n_near <= 64."""
+    lg = (g.random((M, E), dtype=np.float32) * np.float32(1.9) - np.float32(1.0)).astype(np.float32)
+    near = np.float32(1.0) + np.arange(n_near, dtype=np.float32) * np.float32(2.0 ** -20)
+    for m in range(M):
+        if n_near <= 64:
+            lanes = g.choice(64, n_near, replace=False)
+            pos = lanes + 64 * g.integers(0, E // 64, n_near)
+        else:
+            pos = g.choice(E, n_near, replace=False)
+        lg[m, pos] = g.permutation(near)
+    return lg
+
+
+@pytest.mark.parametrize("n_near", [16, 17, 40, 64, 65, 130])
+def test_route_threshold_candidates(n_near):
+    """The ranking gathers the logits whose top 16 order bits reach those of
+    the k-th largest lane maximum and ranks up to 64 of them by counting;
+    past 64 it runs the list rounds.  With n_near near-equal top logits in
+    distinct lanes exactly n_near are gathered: ids exact and weights within
+    the bar against the oracle on both sides of the boundary, for moe_route
+    (1, 4 and 16 rows) and for the one-row layer call, whose gate/up launch
+    ranks the logits itself (route mode)."""
+    moe = _moe()
+    E, k = 896, 16
+    g = np.random.default_rng(1000 + n_near)
+    for M in (1, 4, 16):
+        lg = _near_threshold_logits(g, M, E, n_near)
+        ids_ref, w_ref = oracle.topk(lg, k)
+        ids = torch.empty((M, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((M, k), dtype=torch.float32, device="cuda")
+        moe.moe_route(None, None, _dev(lg), k, ids, w)
+        assert np.array_equal(_host(ids), ids_ref), (n_near, M)
+        assert_close(_host(w), w_ref, f"topk weights, {n_near} near the threshold, M={M}")
+    shape = synth.LayerShape("e896", 64, 32, E, 1, k, -6, -2, 0.05, "bf16")
+    ex, recs = _small_layer(shape, 51)
+    layer = moe.MoELayer(ex, k, 1)
+    for trial in range(3):
+        lg = _near_threshold_logits(g, 1, E, n_near)
+        x = synth.rows_x(shape, 52 + trial, 1)
+        res = layer.forward(_x_dev(shape, x), logits=_dev(lg))
+        ref = oracle.layer(x, k, shape.n_routed, shape.n_shared, shape.d, shape.f, recs.__getitem__, logits=lg)
+        _compare_layer(res, ref, f"route mode, {n_near} near the threshold", k, shape.n_shared)
+
+
 ROUTER_SHAPES = [
     synth.KIMI,
     synth.LayerShape("r3", 416, 224, 9, 2, 4, -7, -3, 0.05, "bf16"),
