@@ -293,8 +293,8 @@ def run_stream(torch, moe, synth, shp, layers, stream, dev):
 
 
 # The pages' own end-to-end figures: the whole Kimi K3.1 model (92 MoE
-# layers plus attention, spine and head) on one 96 GB RTX PRO 6000 Blackwell
-# with experts streamed from NVMe ("A drafter that leaves the answer
+# layers plus attention, spine and head) on a single RTX PRO 6000 Blackwell
+# (96 GB), experts streamed from NVMe ("A drafter that leaves the answer
 # unchanged" and the published run record).  Context only: another machine,
 # another scope.
 PAGE_BLOCK_16ROWS_S = 3.8

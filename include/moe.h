@@ -20,7 +20,7 @@
  *  - M = 0 rows is valid and enqueues nothing.
  *  - Rows of one call never influence each other's results: the result of a
  *    row is bit-identical whether it is alone (M = 1) or inside a block of
- *    up to 16 rows, for every function here (the verification blocks of "A
+ *    at most 16 rows, for every function here (the verification blocks of "A
  *    drafter that leaves the answer unchanged" must reproduce one-row steps
  *    exactly), and bit-identical across calls of any M for every function
  *    but the router logits: moe_route's logits in calls of more than 16 rows

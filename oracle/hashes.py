@@ -1,6 +1,6 @@
 """64-bit FNV-1a, the logits hash of the pages' run record ("Run Kimi 3.1
-locally on one GPU": token ids and FNV-1a hashes of every position's logits
-compared with the plain run).  TEST INFRASTRUCTURE ONLY, like the rest of
+locally on one GPU": the block path and plain decoding are compared by their
+tokens and by one FNV-1a hash per decoded position's logits).  TEST INFRASTRUCTURE ONLY, like the rest of
 ``oracle/``.  The definition is Fowler, Noll and Vo's: start from the offset
 basis 0xcbf29ce484222325 and for each byte b: h = (h xor b) * 0x100000001b3
 modulo 2^64.  Plain Python, one byte at a time."""

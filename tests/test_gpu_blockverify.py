@@ -1,8 +1,8 @@
 """Block verification ("A drafter that leaves the answer unchanged"): the
 harness kernels against exact references, a layer stack whose 16-row block
 equals 16 plain steps in every logits bit (FNV-1a per position, as the pages'
-run record compares), greedy acceptance with forced rejections of the first,
-a middle and the last draft and short proposals, and the stack's composition
+run record compares), greedy acceptance with a wrong draft planted at the
+start, in the middle and at the end, short proposals, and the stack's composition
 checked layer by layer against the oracle.  Needs an MI355X."""
 import numpy as np
 import pytest
@@ -150,7 +150,7 @@ def test_block_equals_plain_steps_and_greedy_acceptance():
     emitted, kept, bh = verify_block(stack, t0, seq[1:16])
     assert kept == 15 and emitted == plain[:16]
     assert bh == ph[:16]
-    # forced rejections: the first, a middle and the last draft
+    # a wrong draft planted at position 1, in the middle and at the end
     for j in (1, 8, 15):
         drafts = list(seq[1:16])
         drafts[j - 1] = (drafts[j - 1] + 1) % VOCAB
