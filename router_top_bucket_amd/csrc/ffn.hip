@@ -130,7 +130,8 @@ __device__ int route_one_row(const RouteArgs &ra, int g, bool writer, uint8_t *l
   if (threadIdx.x < 64) {
     int32_t id;
     float wt;
-    topk_row_any<16>(ra.logits, ra.E, ra.k, (uint64_t(*)[64])lists, lane, id, wt);
+    // only the writer stores the weights; the others need the ids alone
+    topk_row_any<16>(ra.logits, ra.E, ra.k, (uint64_t(*)[64])lists, lane, id, wt, writer);
     int pos = 0;  // ascending position of this lane's id among the k (distinct) ids
     for (int i = 0; i < ra.k; ++i) pos += __builtin_amdgcn_readlane(id, i) < id;
     const uint64_t hit = __ballot(lane < ra.k && pos == g);
@@ -439,28 +440,90 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
   if (item < 0) return;
   const int g = item / n_ftiles;
   const int ft = item - g * n_ftiles;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int M = n_slots / kps;
+  const rsrc_t xr = make_rsrc(x, (uint32_t)((int64_t)M * d * EL));
+  const uint32_t brow = bres_row_bytes(d);
+  const uint32_t dummy = (uint32_t)gateup_dummy_off(d, PF, NP, MAXC, BRES, ROWS);
+  uint8_t *const bmem = lds + gateup_b_off(d, ROWS);  // B area (after the scale rows)
+
+  // Resident B: x of the group's `cnt` columns (x row offsets xb, kOOB past
+  // the group) for the whole d, 8 elements per piece, all loads of a round
+  // issued before its LDS writes; threads t0 .. t0 + nthr - 1 take part.
+  auto stage_x = [&](int cnt, const uint32_t (&xb)[MAXC], int t0, int nthr) {
+    constexpr int CH = 8;  // pieces per thread per round
+    const int per_col = d / 8;
+    const int npieces = cnt * per_col;
+    for (int base = 0; base < npieces; base += CH * nthr) {
+      u32x4 v[CH][EL / 2];
+      int pc[CH], pe[CH];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int piece = base + c * nthr + t0;
+        pc[c] = piece / per_col;
+        pe[c] = (piece - pc[c] * per_col) * 8;
+        uint32_t xrow = xb[0];
+#pragma unroll
+        for (int cc = 1; cc < MAXC; ++cc) xrow = pc[c] == cc ? xb[cc] : xrow;
+        const uint32_t off = piece < npieces ? xrow + (uint32_t)(pe[c] * EL) : kOOB;
+#pragma unroll
+        for (int h = 0; h < EL / 2; ++h) v[c][h] = buf_load16(xr, off + 16 * h);
+      }
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const bool live = base + c * nthr + t0 < npieces;
+        if (XBF16) {
+          *(u32x4 *)(live ? bmem + pc[c] * brow + pe[c] * 2 : lds + dummy) = v[c][0];
+        } else {
+          uint32_t hi[8], mi[8], lo[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) split3_bf16(__uint_as_float(v[c][e >> 2][e & 3]), hi[e], mi[e], lo[e]);
+          u32x4 ph, pm, pl;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            ph[e] = hi[2 * e] | (hi[2 * e + 1] << 16);
+            pm[e] = mi[2 * e] | (mi[2 * e + 1] << 16);
+            pl[e] = lo[2 * e] | (lo[2 * e + 1] << 16);
+          }
+          *(u32x4 *)(live ? bmem + (0 * MAXC + pc[c]) * brow + pe[c] * 2 : lds + dummy) = ph;
+          *(u32x4 *)(live ? bmem + (1 * MAXC + pc[c]) * brow + pe[c] * 2 : lds + dummy + 16) = pm;
+          *(u32x4 *)(live ? bmem + (2 * MAXC + pc[c]) * brow + pe[c] * 2 : lds + dummy + 32) = pl;
+        }
+      }
+    }
+    for (int idx = t0; idx < NP * MAXC * (kBresTail / 16); idx += nthr) {
+      const int row = idx / (kBresTail / 16), c = idx - row * (kBresTail / 16);
+      *(u32x4 *)(bmem + row * brow + d * 2 + 16 * c) = u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+
   int expert, start, count;
+  // route mode, a routed group: x (the one row, row 0) does not depend on
+  // the ranking, so the other waves stage it while the first wave ranks,
+  // where the B area lies past the ranking's LDS
+  bool x_staged = false;
   if constexpr (ROUTE) {
     __shared__ int route_bcast;
-    expert = route_one_row(ra, g, item == 0, lds, &route_bcast);
+    x_staged = g < ra.k && gateup_b_off(d, ROWS) >= topk_wave_lds(16);
+    if (x_staged && tid >= 64) {
+      uint32_t xb[MAXC];
+#pragma unroll
+      for (int c = 0; c < MAXC; ++c) xb[c] = c == 0 ? 0u : kOOB;
+      stage_x(1, xb, tid - 64, NTH - 64);
+    }
+    expert = route_one_row(ra, g, item == 0, lds, &route_bcast);  // its barrier publishes x too
     start = g;  // one slot per expert: bucket position g
     count = 1;
   } else {
     if (!load_group(src, g, expert, start, count, MAXC)) return;
   }
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = lane & 15, q = lane >> 4;
   const int mat = PAIR ? 0 : (wv >= HW ? 1 : 0);  // 0: W_gate, 1: W_up (split layout)
   const int rw = wv - mat * HW;                    // row-tile group of this wave
   const int i0 = ft * ROWS;
   const uint32_t plane_c = (uint32_t)((int64_t)f * d / 2), plane_s = (uint32_t)((int64_t)f * d / 32);
   const rsrc_t wr = expert_rsrc(src, experts, stride, expert);
-  const int M = n_slots / kps;
-  const rsrc_t xr = make_rsrc(x, (uint32_t)((int64_t)M * d * EL));
-  const uint32_t brow = bres_row_bytes(d);
-  const uint32_t dummy = (uint32_t)gateup_dummy_off(d, PF, NP, MAXC, BRES, ROWS);
-  uint8_t *const bmem = lds + gateup_b_off(d, ROWS);  // B area (after the scale rows)
   const int bcol = r < count ? r : 0;  // resident-B column read by this lane
 
   // staging pieces of this thread: x row base offset (kOOB when empty) and
@@ -527,61 +590,18 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_kernel(
   sg.end(wr, plane_c, i0, rv, ROWS, d, lds, dummy, lds, tid, NTH);
   su.end(wr, 2 * plane_c + plane_s, i0, rv, ROWS, d, lds + ROWS * sc_pitch(d), dummy, lds, tid, NTH);
   if constexpr (BRES) {
-    // x of the group's columns for the whole d, 8 elements per piece, all
-    // loads of a round issued before its LDS writes.  The x row of each
-    // column is read from perm once, up front.
-    uint32_t xb[MAXC];
+    if (!x_staged) {
+      // the x row of each column, read from perm once, up front
+      uint32_t xb[MAXC];
 #pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
-      // route mode: the one row's slots (perm is being written by this launch)
-      const int t = ROUTE ? 0 : perm[start + (c < count ? c : count - 1)];
-      xb[c] = (c < count && t >= 0 && t < n_slots) ? (uint32_t)(t / kps) * (uint32_t)(d * EL) : kOOB;
-    }
-    constexpr int CH = 8;  // pieces per thread per round
-    const int per_col = d / 8;
-    const int npieces = count * per_col;
-    for (int base = 0; base < npieces; base += CH * NTH) {
-      u32x4 v[CH][EL / 2];
-      int pc[CH], pe[CH];
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const int piece = base + c * NTH + tid;
-        pc[c] = piece / per_col;
-        pe[c] = (piece - pc[c] * per_col) * 8;
-        uint32_t xrow = xb[0];
-#pragma unroll
-        for (int cc = 1; cc < MAXC; ++cc) xrow = pc[c] == cc ? xb[cc] : xrow;
-        const uint32_t off = piece < npieces ? xrow + (uint32_t)(pe[c] * EL) : kOOB;
-#pragma unroll
-        for (int h = 0; h < EL / 2; ++h) v[c][h] = buf_load16(xr, off + 16 * h);
+      for (int c = 0; c < MAXC; ++c) {
+        // route mode: the one row's slots (perm is being written by this launch)
+        const int t = ROUTE ? 0 : perm[start + (c < count ? c : count - 1)];
+        xb[c] = (c < count && t >= 0 && t < n_slots) ? (uint32_t)(t / kps) * (uint32_t)(d * EL) : kOOB;
       }
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-        const bool live = base + c * NTH + tid < npieces;
-        if (XBF16) {
-          *(u32x4 *)(live ? bmem + pc[c] * brow + pe[c] * 2 : lds + dummy) = v[c][0];
-        } else {
-          uint32_t hi[8], mi[8], lo[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) split3_bf16(__uint_as_float(v[c][e >> 2][e & 3]), hi[e], mi[e], lo[e]);
-          u32x4 ph, pm, pl;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            ph[e] = hi[2 * e] | (hi[2 * e + 1] << 16);
-            pm[e] = mi[2 * e] | (mi[2 * e + 1] << 16);
-            pl[e] = lo[2 * e] | (lo[2 * e + 1] << 16);
-          }
-          *(u32x4 *)(live ? bmem + (0 * MAXC + pc[c]) * brow + pe[c] * 2 : lds + dummy) = ph;
-          *(u32x4 *)(live ? bmem + (1 * MAXC + pc[c]) * brow + pe[c] * 2 : lds + dummy + 16) = pm;
-          *(u32x4 *)(live ? bmem + (2 * MAXC + pc[c]) * brow + pe[c] * 2 : lds + dummy + 32) = pl;
-        }
-      }
+      stage_x(count, xb, tid, NTH);
     }
-    for (int idx = tid; idx < NP * MAXC * (kBresTail / 16); idx += NTH) {
-      const int row = idx / (kBresTail / 16), c = idx - row * (kBresTail / 16);
-      *(u32x4 *)(bmem + row * brow + d * 2 + 16 * c) = u32x4{0u, 0u, 0u, 0u};
-    }
-    lds_barrier();
+    lds_barrier();  // the scale rows (and x) are in LDS
   } else if constexpr (MAXC < 16) {
     // rows of columns >= MAXC are never staged: zero them once
     const int zrows = PF * NP * (16 - MAXC);

@@ -145,18 +145,19 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ row, int E, i
 // The same top-k by a threshold: every key is at most its lane's maximum, so
 // the k-th largest key is at least the k-th largest of the 64 lane maxima,
 // and in particular its top 16 bits are at least t, the k-th largest top 16
-// bits among the lane maxima (found by an MSB-first bitwise search with wave
-// ballots).  The keys whose top 16 bits are at least t are gathered in LDS;
-// when there are at most 64 of them (the usual case: logits that share the
-// threshold's sign, exponent and 7 mantissa bits are few) each is ranked by
-// counting the larger ones, else the list-based rounds above run.  Keys are
-// distinct, so the k largest and their order are the same either way, and the
-// weights are computed by the same code from the same values.  `lists`: at
+// bits among the lane maxima (found 4 bits at a time: 15 wave ballots per
+// step, one count each).  The keys whose top 16 bits are at least t are
+// gathered in LDS; when there are at most 64 of them (the usual case: logits
+// that share the threshold's sign, exponent and 7 mantissa bits are few)
+// each is ranked by counting the larger ones, else the list-based rounds
+// above run.  Keys are distinct, so the k largest and their order are the
+// same either way, and the weights are computed by the same code from the
+// same values (skipped when `need_w` is false: w_out is then 0).  `lists`: at
 // least topk_wave_lds(NPL) bytes of this wave's LDS.
 template <int NPL>
 __device__ __forceinline__ void topk_row_fast(const float *__restrict__ row, int E, int k, uint64_t (*lists)[64],
-                                              int lane, int32_t &id_out, float &w_out) {
-  static_assert(NPL >= 2, "the candidate and ranked keys need 136 keys of LDS");
+                                              int lane, int32_t &id_out, float &w_out, bool need_w = true) {
+  static_assert(NPL >= 2, "the candidate, ranked and spill keys need 144 keys of LDS");
   float v[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) v[i] = row[min(lane + 64 * i, E - 1)];
@@ -171,14 +172,20 @@ __device__ __forceinline__ void topk_row_fast(const float *__restrict__ row, int
   // t: the largest 16-bit value with at least k lane maxima at or above it
   const uint32_t mh = (uint32_t)(m >> 48);
   uint32_t t = 0;
-  for (int b = 15; b >= 0; --b) {
-    const uint32_t c = t | (1u << b);
-    if (__popcll(__ballot(mh >= c)) >= k) t = c;
+#pragma unroll
+  for (int sh = 12; sh >= 0; sh -= 4) {
+    uint32_t best = 0;
+#pragma unroll
+    for (uint32_t d = 1; d < 16; ++d)
+      best = __popcll(__ballot(mh >= (t | (d << sh)))) >= (uint32_t)k ? d : best;
+    t |= best << sh;
   }
   // gather the keys at or above t (key 0 marks an entry past E); slots past
-  // the count read as key 0, which is below every real key
-  uint64_t *cand = &lists[0][0];  // [64 + 8] keys, then the k ranked keys
+  // the count read as key 0, which is below every real key; entries that do
+  // not qualify, or past 64, go to a spill slot that nothing reads
+  uint64_t *cand = &lists[0][0];  // [64 + 8] keys, then the k ranked keys, then 8 spill slots
   uint64_t *ranked = cand + 72;
+  uint64_t *spill = cand + 136;
   cand[lane] = 0ull;
   if (lane < 8) cand[64 + lane] = 0ull;
   int n = 0;
@@ -187,7 +194,7 @@ __device__ __forceinline__ void topk_row_fast(const float *__restrict__ row, int
     const bool c = key[i] != 0ull && (uint32_t)(key[i] >> 48) >= t;
     const uint64_t msk = __ballot(c);
     const int slot = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(msk >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)msk, 0u));
-    if (c && slot < 64) cand[slot] = key[i];
+    *(c && slot < 64 ? cand + slot : spill + (lane & 7)) = key[i];
     n += (int)__popcll(msk);
   }
   if (n > 64) {  // uniform: too many near the threshold
@@ -203,7 +210,7 @@ __device__ __forceinline__ void topk_row_fast(const float *__restrict__ row, int
 #pragma unroll
     for (int u = 0; u < 8; ++u) rank += cand[j0 + u] > mine;
   }
-  if (lane < n && rank < k) ranked[rank] = mine;
+  *(lane < n && rank < k ? ranked + rank : spill + (lane & 7)) = mine;
   __builtin_amdgcn_s_waitcnt(0xC07F);
   __builtin_amdgcn_wave_barrier();
   float my_l = 0.f;
@@ -213,7 +220,12 @@ __device__ __forceinline__ void topk_row_fast(const float *__restrict__ row, int
     my_l = from_order_bits((uint32_t)(kj >> 32));
     my_id = (int32_t)~(uint32_t)kj;
   }
-  topk_weights(my_l, my_id, lane, k, id_out, w_out);
+  if (need_w) {
+    topk_weights(my_l, my_id, lane, k, id_out, w_out);
+  } else {
+    id_out = my_id;
+    w_out = 0.f;
+  }
 }
 
 // Bucketing of one row in one wave, from its top-k ids (lane j < k holds
@@ -256,9 +268,9 @@ __device__ __forceinline__ void bucket_one_row(int32_t id, int lane, int E, int 
 // threshold form's 136 keys).  Both give the same ids and weights.
 template <int NPL>
 __device__ __forceinline__ void topk_row_any(const float *__restrict__ row, int E, int k, uint64_t (*lists)[64],
-                                             int lane, int32_t &id_out, float &w_out) {
+                                             int lane, int32_t &id_out, float &w_out, bool need_w = true) {
   if constexpr (NPL >= 2)
-    topk_row_fast<NPL>(row, E, k, lists, lane, id_out, w_out);
+    topk_row_fast<NPL>(row, E, k, lists, lane, id_out, w_out, need_w);
   else
     topk_row<NPL>(row, E, k, lists, lane, id_out, w_out);
 }
