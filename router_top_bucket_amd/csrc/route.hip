@@ -20,16 +20,21 @@ namespace moe {
 // each pass issues all its loads (W and x, buffer loads: out-of-range chunks
 // read zero, and a zero term at the end of a chain leaves it unchanged)
 // before any arithmetic; with single-chunk passes (KC = 1) the next pass's
-// loads are issued before this pass's arithmetic.
+// loads are issued before this pass's arithmetic.  With XS > 1 the
+// workgroup holds XS such 256-thread sets over the same router rows, set s
+// taking x rows s*MCH.. of each XS*MCH (more independent waves per router
+// row, each with a shorter list of rows; every logit's chain is unchanged).
 constexpr int LG_THREADS = 256;
 
-template <int XBF16, int RW, int MCH, int KC>
-__global__ __launch_bounds__(LG_THREADS) void router_logits_kernel(const void *__restrict__ x,
-                                                                   const float *__restrict__ w, int M, int d, int E,
-                                                                   float *__restrict__ logits) {
-  __shared__ float red[4][RW * MCH];
+template <int XBF16, int RW, int MCH, int KC, int XS = 1>
+__global__ __launch_bounds__(LG_THREADS * XS) void router_logits_kernel(const void *__restrict__ x,
+                                                                        const float *__restrict__ w, int M, int d,
+                                                                        int E, float *__restrict__ logits) {
+  __shared__ float reds[XS][4][RW * MCH];
   const int e0 = blockIdx.x * RW;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int xs = threadIdx.x / LG_THREADS;
+  const int tid = threadIdx.x % LG_THREADS, lane = tid & 63, wv = tid >> 6;
+  float (&red)[4][RW * MCH] = reds[xs];
   const int nchunk = d >> 2;
   constexpr int EL = XBF16 ? 2 : 4;
   constexpr int STEP = LG_THREADS * KC;  // chunks per pass
@@ -40,8 +45,11 @@ __global__ __launch_bounds__(LG_THREADS) void router_logits_kernel(const void *_
   };
   const rsrc_t wres = make_rsrc(w, (uint32_t)((int64_t)E * d * 4));
   const rsrc_t xres = make_rsrc(x, (uint32_t)((int64_t)M * d * EL));
-  for (int mc = 0; mc < M; mc += MCH) {
-    const int mn = (M - mc) < MCH ? (M - mc) : MCH;
+  // every set takes the same trip count (the barriers below are the
+  // workgroup's); a set past the last row loads zeros and stores nothing
+  for (int mc0 = 0; mc0 < M; mc0 += MCH * XS) {
+    const int mc = mc0 + xs * MCH;
+    const int mn = (M - mc) < MCH ? ((M - mc) > 0 ? (M - mc) : 0) : MCH;
     float acc[MCH][RW];
 #pragma unroll
     for (int m = 0; m < MCH; ++m)
@@ -56,8 +64,9 @@ __global__ __launch_bounds__(LG_THREADS) void router_logits_kernel(const void *_
         for (int rr = 0; rr < RW; ++rr)
         {
           const uint32_t wo = (c < nchunk && e0 + rr < E) ? (uint32_t)(((e0 + rr) * d + 4 * c) * 4) : kOOB;
-          // W is read once when one pass takes every row: stream it
-          ps.w[i][rr] = __builtin_bit_cast(f32x4, M <= MCH ? buf_load16_stream(wres, wo) : buf_load16(wres, wo));
+          // W is read once when one pass of one set takes every row: stream it
+          ps.w[i][rr] =
+              __builtin_bit_cast(f32x4, XS == 1 && M <= MCH ? buf_load16_stream(wres, wo) : buf_load16(wres, wo));
         }
 #pragma unroll
         for (int m = 0; m < MCH; ++m) {
@@ -342,26 +351,26 @@ static void launch_logits_mfma(const void *x, const float *w_router, float *logi
                        stream, x, w_router, M, d, E, logits);
 }
 
+template <int XBF16, int RW, int MCH, int KC, int XS>
+static void launch_logits_shape(const void *x, const float *w_router, float *logits, int M, int d, int E,
+                                hipStream_t stream) {
+  hipLaunchKernelGGL((router_logits_kernel<XBF16, RW, MCH, KC, XS>), dim3((E + RW - 1) / RW), dim3(LG_THREADS * XS),
+                     0, stream, x, w_router, M, d, E, logits);
+}
+
 template <int XBF16>
 static void launch_logits(const void *x, const float *w_router, float *logits, int M, int d, int E,
                           hipStream_t stream) {
-  // pass shapes by row count (measured on MI355X at E = 896, d = 7168, moe_route
-  // with top-k: 2-4 rows 4 router rows x 4 x rows x 4 chunks, 11.9 / 12.7 us
-  // against 12.8 / 13.4 for the 5-8-row shape; above 8 rows two router rows
-  // per workgroup halve the x re-reads against one and still give 448
-  // workgroups); the arithmetic of a logit does not change
-  if (M == 1)
-    hipLaunchKernelGGL((router_logits_kernel<XBF16, 1, 1, 8>), dim3(E), dim3(LG_THREADS), 0, stream, x, w_router, M,
-                       d, E, logits);
-  else if (M <= 4)
-    hipLaunchKernelGGL((router_logits_kernel<XBF16, 4, 4, 4>), dim3((E + 3) / 4), dim3(LG_THREADS), 0, stream, x,
-                       w_router, M, d, E, logits);
-  else if (M <= 8)
-    hipLaunchKernelGGL((router_logits_kernel<XBF16, 2, 4, 8>), dim3((E + 1) / 2), dim3(LG_THREADS), 0, stream, x,
-                       w_router, M, d, E, logits);
-  else
-    hipLaunchKernelGGL((router_logits_kernel<XBF16, 2, 16, 1>), dim3((E + 1) / 2), dim3(LG_THREADS), 0, stream, x,
-                       w_router, M, d, E, logits);
+  // (router rows, x rows per set, chunks per pass, sets) by row count; a
+  // sweep of 20 shapes at E = 896, d = 7168, bf16 x (moe_route, logits +
+  // top-k, bit-identical logits throughout) kept: 2 and 4 rows 11.7 / 12.2 us
+  // (one set: 12.4 / 13.5), 8 rows 13.9 (15.5), 16 rows 17.6 (21.0); two or
+  // four sets give each router row more independent waves with shorter row
+  // lists.  The arithmetic of a logit never changes.
+  if (M == 1) launch_logits_shape<XBF16, 1, 1, 8, 1>(x, w_router, logits, M, d, E, stream);
+  else if (M <= 4) launch_logits_shape<XBF16, 2, 2, 4, 2>(x, w_router, logits, M, d, E, stream);
+  else if (M <= 8) launch_logits_shape<XBF16, 2, 4, 1, 2>(x, w_router, logits, M, d, E, stream);
+  else launch_logits_shape<XBF16, 4, 8, 1, 2>(x, w_router, logits, M, d, E, stream);
 }
 
 int logits_launch(const void *x, int x_bf16, const float *w_router, float *logits, int M, int d, int E,
