@@ -118,6 +118,28 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// ---- direct loads into LDS (gfx950 LDS DMA).  Lane l of one instruction
+// writes its 16 bytes to lds_base + 16 l (lds_base is wave-uniform), so one
+// instruction fills 1 KB of LDS in lane order; which global bytes land where
+// is chosen by each lane's offset.  The load is counted by vmcnt like any
+// other and its data is in LDS once this wave's vmcnt has passed it.
+__device__ __forceinline__ void buf_load16_lds(rsrc_t r, uint32_t off, uint8_t *lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds_base, 16, off, 0, 0, 0);
+}
+// Wait until at most N vector-memory loads of this wave are in flight
+// (s_waitcnt vmcnt(N), gfx9 encoding: vmcnt bits [3:0] and [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+// Barrier for LDS filled by LDS DMA: this wave's LDS reads and writes are
+// done, then s_barrier.  No fence: a workgroup fence makes the compiler wait
+// for every load in flight (LDS DMA included), which would drain the ring;
+// the caller waits for the DMA loads it needs with wait_vmcnt.  The memory
+// clobber keeps every memory access on its side of the barrier.
+__device__ __forceinline__ void lds_dma_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // ---- wave reductions without LDS: DPP inside each 16-lane row, then the four
 // row results read as scalars and combined in row order.  Every lane of a
 // row ends with bit-identical values (each step combines a lane with a fixed

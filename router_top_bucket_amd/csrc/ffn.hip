@@ -922,7 +922,18 @@ __global__ __launch_bounds__(GW * 64) void ffn_gateup_wide_kernel(
 // block scales of step 4j + q, and at step 4j + u a bpermute from lane
 // (r, u) hands lane (r, q) byte q (the same byte, the same 2^(b-127), as a
 // staged scale).  The LDS it frees lets two wide workgroups share a CU.
-template <int TPW, int DW, int PF, int MAXC, bool SX4, bool BRES, int CS, bool SCR = false>
+//
+// DMA (ring mode): B goes from the workspace straight into its ring slot
+// with LDS DMA instead of through registers.  A slot holds the step's B rows
+// at a 256-byte pitch, the 16-byte chunk c of row j at position c ^ (j % 16)
+// (16 consecutive rows then spread a chunk column over all banks); lane l of
+// a DMA instruction fills one chunk, choosing its source accordingly.  Slot
+// (s-1) % PF is refilled with step s+PF-1 right after step s's barrier (the
+// barrier that also tells every wave is done reading it), so B runs PF-1
+// steps ahead and the codes PF steps.  Step s waits for its own DMA loads by
+// count (wait_vmcnt; loads retire in issue order) before that barrier.
+// Same bytes, same products, same order: bit-identical to register staging.
+template <int TPW, int DW, int PF, int MAXC, bool SX4, bool BRES, int CS, bool SCR = false, bool DMA = false>
 __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
     int d, int f, int n_slots, const uint8_t *__restrict__ experts, int64_t stride, GroupSrc src,
     const int32_t *__restrict__ perm, int n_dtiles, const uint16_t *__restrict__ h_ws, float *__restrict__ y) {
@@ -940,6 +951,9 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
   constexpr int NPH = (MAXC + SPP - 1) / SPP;         // epilogue phases
   constexpr int YP = YC + 1;                          // epilogue row pitch (floats)
   static_assert(!SCR || (!BRES && 4 % PF == 0), "ring scales: ring mode, ring depth divides 4");
+  static_assert(!DMA || (!BRES && PF >= 2 && NPIECE % NTH == 0), "LDS DMA: ring mode, whole 1 KB pieces per wave");
+  constexpr uint32_t RP = DMA ? 256u : (uint32_t)kBRow;  // B row pitch in a ring slot
+  constexpr uint32_t SLOTB = (uint32_t)NC * RP;          // bytes of one ring slot
   extern __shared__ __align__(16) uint8_t lds[];
   const int item = xcd_item(group_count(src) * n_dtiles);
   if (item < 0) return;
@@ -975,7 +989,8 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
   for (int i = 0; i < SPT; ++i) {
     const int piece = tid + i * NTH;
     prow[i] = piece >> 4;
-    pel[i] = (piece & 15) * 8;
+    // DMA: the chunk stored at position piece % 16 of row prow
+    pel[i] = DMA ? ((piece & 15) ^ (prow[i] & 15)) * 8 : (piece & 15) * 8;
     pbase[i] = (piece < NPIECE && prow[i] < nc) ? hbase + (uint32_t)prow[i] * (uint32_t)(f * 2) : kOOB;
   }
   uint32_t aoff[TPW];
@@ -999,16 +1014,27 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
   const int nsteps = (f + 127) >> 7;
   const int smax = (f - (q << 5) + 127) >> 7;
   u32x4 ring[PF][TPW];
-  u32x4 hst[PF][SPTA];
+  u32x4 hst[PF][DMA ? 1 : SPTA];
   const uint32_t cstep = code_step(src);
   auto issue = [&](int s, int p) {
     const uint32_t ka = s < smax ? (uint32_t)s * cstep : kDead;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) ring[p][t] = MAXC <= kGroupCols ? buf_load16_stream(wr, aoff[t] + ka) : buf_load16(wr, aoff[t] + ka);
+    if constexpr (!DMA) {
+#pragma unroll
+      for (int i = 0; i < SPT; ++i) {
+        const int k = (s << 7) + pel[i];
+        hst[p][i] = buf_load16(hr, pbase[i] + (k < f ? (uint32_t)(k * 2) : kDead));
+      }
+    }
+  };
+  // DMA: B of step s into ring slot p, one 1 KB piece per wave instruction
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  auto dma_b = [&](int s, int p) {
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
       const int k = (s << 7) + pel[i];
-      hst[p][i] = buf_load16(hr, pbase[i] + (k < f ? (uint32_t)(k * 2) : kDead));
+      buf_load16_lds(hr, pbase[i] + (k < f ? (uint32_t)(k * 2) : kDead), bmem + p * SLOTB + (uint32_t)(i * NTH + wvu * 64) * 16u);
     }
   };
   // SCR: the scale dwords of step group j (4 steps); a padding step's dword
@@ -1028,6 +1054,10 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
   else ss.begin(wr, dn_s, r0, rv, ROWS, f, tid, NTH);
 #pragma unroll
   for (int p = 0; p < PF; ++p) issue(p, p);
+  if constexpr (DMA) {
+#pragma unroll
+    for (int p = 0; p < PF - 1; ++p) dma_b(p, p);
+  }
   asm volatile("" ::: "memory");
   if constexpr (!BRES) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   asm volatile("" ::: "memory");
@@ -1062,11 +1092,26 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
   // refill of slot p.  The scales are the ring's (SCR: sc_ring) or read from
   // LDS after the step's barrier, which on the first step also publishes the
   // staged scale rows of every wave.
-  auto step = [&](int s, int p, const float (&sc_ring)[TPW]) {
+  // DMA: loads issued after step s's B, by position u of s in its group of 4
+  // steps (ring scales): the codes of step s+1, then PF-2 steps of B and
+  // codes, plus the scale dwords of the next group where those were issued
+  // after step s's B (u < PF-1)
+  auto wait_b = [&](int u) {
+    constexpr int base = TPW + (PF - 2) * (SPT + TPW);
+    if (SCR && u < PF - 1) wait_vmcnt<base + TPW>();
+    else wait_vmcnt<base>();
+  };
+  auto step = [&](int s, int p, const float (&sc_ring)[TPW], int u) {
+      if constexpr (DMA) {
+        wait_b(u);
+        lds_dma_barrier();
+        dma_b(s + PF - 1, (p + PF - 1) % PF);
+      } else {
 #pragma unroll
-      for (int i = 0; i < SPT; ++i)
-        *(u32x4 *)(tid + i * NTH < NPIECE ? bmem + (p * NC + prow[i]) * kBRow + pel[i] * 2 : lds + dummy) = hst[p][i];
-      if constexpr (!BRES) lds_barrier();
+        for (int i = 0; i < SPT; ++i)
+          *(u32x4 *)(tid + i * NTH < NPIECE ? bmem + (p * NC + prow[i]) * kBRow + pel[i] * 2 : lds + dummy) = hst[p][i];
+        if constexpr (!BRES) lds_barrier();
+      }
       float sc[TPW];
 #pragma unroll
       for (int t = 0; t < TPW; ++t) sc[t] = SCR ? sc_ring[t] : lds_scale(srow[t], s, q);
@@ -1084,6 +1129,8 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
             bf16x8 b;
             if constexpr (BRES)
               b = lds_b_fragment(bmem, bsel[cbl] * brow + (s < smax ? ((s << 7) + (q << 5) + 8 * j) * 2 : f * 2 + 16 * j));
+            else if constexpr (DMA)
+              b = lds_b_fragment(bmem, p * SLOTB + bsel[cbl] * RP + (((4 * q + j) ^ (bsel[cbl] & 15)) << 4));
             else
               b = lds_b_fragment(bmem, (p * NC + bsel[cbl]) * kBRow + ((q << 5) + 8 * j) * 2);
 #pragma unroll
@@ -1109,7 +1156,7 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
           const uint32_t w = (uint32_t)__builtin_amdgcn_ds_bpermute((r + 16 * u) * 4, (int)sc_cur[t]);
           sc[t] = e8m0_to_f32((w >> (8 * q)) & 0xFFu);
         }
-        step(4 * j + u, u % PF, sc);
+        step(4 * j + u, u % PF, sc, u);
       }
 #pragma unroll
       for (int t = 0; t < TPW; ++t) sc_cur[t] = sc_nxt[t];
@@ -1119,7 +1166,7 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
     const float none[TPW] = {};
     for (int s0 = 0; s0 < nsteps_pad; s0 += PF) {
 #pragma unroll
-      for (int p = 0; p < PF; ++p) step(s0 + p, p, none);
+      for (int p = 0; p < PF; ++p) step(s0 + p, p, none, PF);
     }
   }
 
@@ -1127,6 +1174,9 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
   // past their last B read at the first barrier), SPP slots (YC columns) per
   // phase; each slot's part sums are added in a fixed order and its
   // rows written as float4
+  // DMA: every ring load (the padded steps' too) has landed before the B
+  // area is reused
+  if constexpr (DMA) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   float *ys = (float *)(lds + down_y_off(f, PF, MAXC, BRES, ROWS, SCR));
 #pragma unroll
   for (int ph = 0; ph < NPH; ++ph) {
@@ -1249,19 +1299,22 @@ static int launch_gateup_wide(const void *x, int d, int f, int kps, int T, const
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
-template <int TPW, int DW, int PF, int MAXC, bool SX4, bool BRES, int CS, bool SCR = false>
+template <int TPW, int DW, int PF, int MAXC, bool SX4, bool BRES, int CS, bool SCR = false, bool DMA = false>
 static int launch_down(int d, int f, int T, const uint8_t *experts, int64_t stride, const GroupSrc &src,
                        const int32_t *perm, int64_t maxg, const uint16_t *h_ws, float *y, hipStream_t stream) {
   constexpr int ROWS = DW / CS * TPW * 16;
   const int n_dtiles = (d + ROWS - 1) / ROWS;
   if (maxg <= 0) return 0;
   if (SCR && f % 128) return -3;
+  // LDS DMA: whole steps only, and every ring slot filled by a real step
+  // before a padded step reads it
+  if (DMA && (f % 128 || f < 128 * PF)) return -3;
   const size_t smem = down_lds_bytes(f, PF, MAXC, BRES, ROWS, SCR);
   if (smem > (size_t)kMaxLds) return -3;
   static const bool lds_ok =
-      allow_lds(reinterpret_cast<const void *>(&ffn_down_kernel<TPW, DW, PF, MAXC, SX4, BRES, CS, SCR>));
+      allow_lds(reinterpret_cast<const void *>(&ffn_down_kernel<TPW, DW, PF, MAXC, SX4, BRES, CS, SCR, DMA>));
   if (!lds_ok) return -3;
-  hipLaunchKernelGGL((ffn_down_kernel<TPW, DW, PF, MAXC, SX4, BRES, CS, SCR>), dim3((unsigned)align_up((size_t)(maxg * n_dtiles), kXcds)), dim3(DW * 64), smem,
+  hipLaunchKernelGGL((ffn_down_kernel<TPW, DW, PF, MAXC, SX4, BRES, CS, SCR, DMA>), dim3((unsigned)align_up((size_t)(maxg * n_dtiles), kXcds)), dim3(DW * 64), smem,
                      stream, d, f, T, experts, stride, src, perm, n_dtiles, h_ws, y);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
@@ -1351,6 +1404,12 @@ int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *exper
 #define MOE_DN(T, D, P, C, R, CL, CS)                                                                                   \
   (dsx4 ? launch_down<T, D, P, C, true, R, CS>(d, f, T_, experts, stride, src[CL], perm, cap[CL], h_ws, y, stream) \
         : launch_down<T, D, P, C, false, R, CS>(d, f, T_, experts, stride, src[CL], perm, cap[CL], h_ws, y, stream))
+  // ring mode with B through LDS DMA: scales through the ring (SCR) or staged
+#define MOE_DND(T, D, P, C, CL, CS, SCRV)                                                                               \
+  (dsx4 ? launch_down<T, D, P, C, true, false, CS, SCRV, true>(d, f, T_, experts, stride, src[CL], perm, cap[CL], h_ws, \
+                                                                y, stream)                                              \
+        : launch_down<T, D, P, C, false, false, CS, SCRV, true>(d, f, T_, experts, stride, src[CL], perm, cap[CL], h_ws, \
+                                                                 y, stream))
   // few rows: each group's B operand (x or h) stays resident in LDS for the
   // whole reduction; more rows: B is staged step by step through a ring.
   // Launch shapes (measured at the Kimi shape on tile-ordered records):
@@ -1387,23 +1446,29 @@ int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *exper
   }
   if (stages & kStageDown) {
     const size_t half = (size_t)kMaxLds / 2;
+    // ring mode: B by LDS DMA where f is whole steps of 128 and fills the
+    // ring (f >= 512 covers every ring below); measured on MI355X at the
+    // Kimi shape: 1,533-row prefill 4.86-4.88 -> 4.78-4.83 ms, blocks of 8
+    // and 16 rows 0-4 us faster, bit-identical everywhere
+    const bool dma = f % 128 == 0 && f >= 512;
     if (M == 1 && down_lds_bytes(f, 4, 1, true, 256) <= half) rc = MOE_DN(2, 8, 4, 1, true, 0, 1);
     else if (M <= 4 && down_lds_bytes(f, 4, 4, true, 128) <= half) rc = MOE_DN(1, 8, 4, 4, true, 0, 1);
-    else if (M <= kGroupCols) rc = MOE_DN(2, 8, 4, 16, false, 0, 1);
+    else if (M <= kGroupCols) rc = dma ? MOE_DND(2, 8, 2, 16, 0, 1, false) : MOE_DN(2, 8, 4, 16, false, 0, 1);
     // more rows (the prefill's narrow groups): scales through the ring where
     // f % 128 == 0 (measured 4.90 -> 4.84 ms at 1,533 rows; at 16 rows the
     // staged scales are faster, 191.5 against 197.6 us)
-    else rc = f % 128 == 0 ? MOE_DNR(4, 8, 2, 16, 0, 1) : MOE_DN(4, 8, 2, 16, false, 0, 1);
+    else rc = dma ? MOE_DND(4, 8, 2, 16, 0, 1, true) : f % 128 == 0 ? MOE_DNR(4, 8, 2, 16, 0, 1) : MOE_DN(4, 8, 2, 16, false, 0, 1);
     // the wide groups (MFMA-bound): scales through the ring where f % 128 == 0
     // (two workgroups a CU), else staged
     const bool scr = f % 128 == 0;
-    if (!rc && wide) rc = scr ? MOE_DNR(4, 8, 4, 32, 1, 2) : MOE_DN(4, 8, 4, 32, false, 1, 2);
-    if (!rc && wide) rc = scr ? MOE_DNR(4, 8, 2, 64, 2, 2) : MOE_DN(4, 8, 2, 64, false, 2, 2);
+    if (!rc && wide) rc = dma ? MOE_DND(4, 8, 4, 32, 1, 2, true) : scr ? MOE_DNR(4, 8, 4, 32, 1, 2) : MOE_DN(4, 8, 4, 32, false, 1, 2);
+    if (!rc && wide) rc = dma ? MOE_DND(4, 8, 2, 64, 2, 2, true) : scr ? MOE_DNR(4, 8, 2, 64, 2, 2) : MOE_DN(4, 8, 2, 64, false, 2, 2);
   }
 #undef MOE_GU
 #undef MOE_GUR
 #undef MOE_GUW
 #undef MOE_DN
+#undef MOE_DND
 #undef MOE_DNR
   return rc;
 }

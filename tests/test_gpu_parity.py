@@ -339,6 +339,10 @@ RAGGED = [
     synth.LayerShape("r2", 160, 96, 5, 1, 3, -6, -2, 0.05, "bf16"),
     synth.LayerShape("r3", 416, 224, 9, 2, 4, -7, -3, 0.05, "bf16"),
     synth.LayerShape("r4", 96, 32, 3, 0, 1, -5, -1, 0.05, "f32"),
+    # f = 640: five whole 128-element steps, so the ring-mode down kernels
+    # stage B by LDS DMA (staged scales up to 16 rows, d/32 not a multiple
+    # of 16; ring scales beyond)
+    synth.LayerShape("r5", 160, 640, 7, 1, 3, -6, -2, 0.05, "bf16"),
 ]
 
 
@@ -366,6 +370,9 @@ WIDE = [
     # (one 128-element step plus three padding steps; three steps)
     synth.LayerShape("w3", 256, 128, 5, 1, 2, -6, -2, 0.05, "bf16"),
     synth.LayerShape("w4", 384, 384, 6, 1, 2, -6, -2, 0.05, "f32"),
+    # f >= 512 in whole steps: every ring-mode down kernel stages B by LDS DMA
+    synth.LayerShape("w5", 256, 512, 5, 1, 2, -6, -2, 0.05, "bf16"),
+    synth.LayerShape("w6", 384, 640, 6, 1, 2, -6, -2, 0.05, "f32"),
 ]
 
 
