@@ -280,8 +280,8 @@ __host__ __device__ __forceinline__ size_t gateup_lds_bytes(int d, int pf, int n
 // Down LDS: the scale rows (ROWS; none when the scales travel with the ring
 // loads, scr), then B (resident: 3*MAXC rows; ring: PF slots of 3*MAXC
 // rows), whose space the per-(row, column) part sums of YC columns at a time
-// (ROWS x (YC + 1) floats, see down_yc) reuse once the main loop is done,
-// then the dummy area.
+// (YC columns of ROWS + 4 floats, see down_yc) reuse once the main loop is
+// done, then the dummy area.
 __host__ __device__ __forceinline__ size_t down_b_off(int f, int rows, bool scr = false) {
   return scr ? 0 : lds_align16((size_t)rows * sc_pitch(f));
 }
@@ -297,14 +297,14 @@ __host__ __device__ __forceinline__ size_t down_y_off(int f, int pf, int maxc, b
 __host__ __device__ constexpr int down_yc(int pf, int maxc, bool bres, int rows) {
   constexpr int blk = 16 * kHParts;  // the columns of 16 slots
   const int nc = kHParts * maxc;
-  const int avail = (int)((size_t)pf * nc * kBRow / ((size_t)rows * 4)) - 1;
+  const int avail = (int)((size_t)pf * nc * kBRow / ((size_t)(rows + 4) * 4));
   const int yc = avail / blk * blk;
   return (bres || nc <= blk) ? nc : (yc < blk ? blk : (yc > nc ? nc : yc));
 }
 __host__ __device__ __forceinline__ size_t down_dummy_off(int f, int pf, int maxc, bool bres, int rows,
                                                           bool scr = false) {
   const int yc = down_yc(pf, maxc, bres, rows);
-  const size_t b = down_b_bytes(f, pf, maxc, bres), y = (size_t)rows * (yc + 1) * sizeof(float);
+  const size_t b = down_b_bytes(f, pf, maxc, bres), y = (size_t)yc * (rows + 4) * sizeof(float);
   return lds_align16(down_b_off(f, rows, scr) + (b > y ? b : y));
 }
 __host__ __device__ __forceinline__ size_t down_lds_bytes(int f, int pf, int maxc, bool bres, int rows,
@@ -949,7 +949,7 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
   constexpr int YC = down_yc(PF, MAXC, BRES, ROWS);  // epilogue columns per phase
   constexpr int SPP = YC / kHParts;                   // slots per phase
   constexpr int NPH = (MAXC + SPP - 1) / SPP;         // epilogue phases
-  constexpr int YP = YC + 1;                          // epilogue row pitch (floats)
+  constexpr int YP = ROWS + 4;                        // epilogue column pitch (floats)
   static_assert(!SCR || (!BRES && 4 % PF == 0), "ring scales: ring mode, ring depth divides 4");
   static_assert(!DMA || (!BRES && PF >= 2 && NPIECE % NTH == 0), "LDS DMA: ring mode, whole 1 KB pieces per wave");
   constexpr uint32_t RP = DMA ? 256u : (uint32_t)kBRow;  // B row pitch in a ring slot
@@ -1172,8 +1172,11 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
 
   // every (row, column) sum goes through LDS (in the B area: all waves are
   // past their last B read at the first barrier), SPP slots (YC columns) per
-  // phase; each slot's part sums are added in a fixed order and its
-  // rows written as float4
+  // phase, column-major: a lane stores the 4 rows it holds of its column as
+  // one float4, and a thread reads 4 consecutive rows of a slot's two part
+  // columns as two float4 (a pitch of ROWS + 4 floats puts both on distinct
+  // banks across 16 lanes); each slot's part sums are added in a fixed
+  // order (hi + lo) and its rows written as float4
   // DMA: every ring load (the padded steps' too) has landed before the B
   // area is reused
   if constexpr (DMA) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -1187,9 +1190,7 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
       for (int cbl = 0; cbl < NCBW; ++cbl) {
         const int col = (cs * NCBW + cbl) * 16 + r;
         if (col >= YC * ph && col < YC * (ph + 1) && col < nc)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            ys[((rgw * TPW + t) * 16 + 4 * q + i) * YP + col - YC * ph] = acc[t][cbl][i];
+          *(f32x4 *)(ys + (col - YC * ph) * YP + (rgw * TPW + t) * 16 + 4 * q) = acc[t][cbl];
       }
     lds_barrier();
     const int j0 = SPP * ph, nj = count - j0 < SPP ? count - j0 : SPP;
@@ -1198,12 +1199,11 @@ __global__ __launch_bounds__(DW * 64) void ffn_down_kernel(
       const int row = r0 + lrow;
       const int t_slot = perm[start + j0 + jl];
       if (row < d && t_slot >= 0 && t_slot < n_slots) {
+        const f32x4 hi = *(const f32x4 *)(ys + (kHParts * jl) * YP + lrow);
+        const f32x4 lo = *(const f32x4 *)(ys + (kHParts * jl + 1) * YP + lrow);
         f32x4 v;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float *yr = ys + (lrow + i) * YP + kHParts * jl;
-          v[i] = yr[0] + yr[1];
-        }
+        for (int i = 0; i < 4; ++i) v[i] = hi[i] + lo[i];
         *(f32x4 *)(y + (int64_t)t_slot * d + row) = v;
       }
     }
