@@ -1449,20 +1449,23 @@ int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *exper
     // ring mode: B by LDS DMA where f is whole steps of 128 and fills the
     // ring (f >= 512 covers every ring below); measured on MI355X at the
     // Kimi shape: 1,533-row prefill 4.86-4.88 -> 4.78-4.83 ms, blocks of 8
-    // and 16 rows 0-4 us faster, bit-identical everywhere
+    // and 16 rows 0-4 us faster, bit-identical everywhere; up to 16 rows 4
+    // waves x 2 tiles (16-row block 183-185 -> 182 us in a 5-shape sweep)
     const bool dma = f % 128 == 0 && f >= 512;
     if (M == 1 && down_lds_bytes(f, 4, 1, true, 256) <= half) rc = MOE_DN(2, 8, 4, 1, true, 0, 1);
     else if (M <= 4 && down_lds_bytes(f, 4, 4, true, 128) <= half) rc = MOE_DN(1, 8, 4, 4, true, 0, 1);
-    else if (M <= kGroupCols) rc = dma ? MOE_DND(2, 8, 2, 16, 0, 1, false) : MOE_DN(2, 8, 4, 16, false, 0, 1);
+    else if (M <= kGroupCols) rc = dma ? MOE_DND(2, 4, 2, 16, 0, 1, false) : MOE_DN(2, 8, 4, 16, false, 0, 1);
     // more rows (the prefill's narrow groups): scales through the ring where
     // f % 128 == 0 (measured 4.90 -> 4.84 ms at 1,533 rows; at 16 rows the
     // staged scales are faster, 191.5 against 197.6 us)
     else rc = dma ? MOE_DND(4, 8, 2, 16, 0, 1, true) : f % 128 == 0 ? MOE_DNR(4, 8, 2, 16, 0, 1) : MOE_DN(4, 8, 2, 16, false, 0, 1);
     // the wide groups (MFMA-bound): scales through the ring where f % 128 == 0
-    // (two workgroups a CU), else staged
+    // (two workgroups a CU), else staged; with LDS DMA 2 tiles per wave
+    // (128 rows of d for 64 slots, 256 for 32): a sweep at 1,533 rows gave
+    // 4.64-4.66 -> 4.51-4.53 ms against the 4-tile shapes
     const bool scr = f % 128 == 0;
-    if (!rc && wide) rc = dma ? MOE_DND(4, 8, 4, 32, 1, 2, true) : scr ? MOE_DNR(4, 8, 4, 32, 1, 2) : MOE_DN(4, 8, 4, 32, false, 1, 2);
-    if (!rc && wide) rc = dma ? MOE_DND(4, 8, 2, 64, 2, 2, true) : scr ? MOE_DNR(4, 8, 2, 64, 2, 2) : MOE_DN(4, 8, 2, 64, false, 2, 2);
+    if (!rc && wide) rc = dma ? MOE_DND(2, 8, 2, 32, 1, 1, true) : scr ? MOE_DNR(4, 8, 4, 32, 1, 2) : MOE_DN(4, 8, 4, 32, false, 1, 2);
+    if (!rc && wide) rc = dma ? MOE_DND(2, 8, 2, 64, 2, 2, true) : scr ? MOE_DNR(4, 8, 2, 64, 2, 2) : MOE_DN(4, 8, 2, 64, false, 2, 2);
   }
 #undef MOE_GU
 #undef MOE_GUR
