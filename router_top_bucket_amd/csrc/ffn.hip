@@ -1457,10 +1457,10 @@ int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *exper
   // gate/up 4 waves each with the W_gate and W_up tiles of 16 rows (64 rows
   // of f) and a 4-step ring at 1-2 rows, 4 (5-8 rows) or 8 waves (half
   // W_gate, half W_up) with a 4-step ring beyond, and the wide kernel (8
-  // waves x 32 rows) for the 32- and 64-slot groups; down 8 waves x 2 tiles
-  // (256 rows of d) at 1 row, 8 waves x 1 tile at 2-4 rows, 8 waves x 2 tiles
-  // and a 4-step ring up to 16 rows, and for the narrow groups of more rows
-  // 8 waves x 4 tiles (512 rows) with a 2-step ring.  A resident B is used only where the LDS it takes still lets two
+  // waves x 32 rows) for the 32- and 64-slot groups; down 4 waves x 2 tiles
+  // (128 rows of d) at 1-4 rows, 4 waves x 2 tiles and a 2-step ring up to
+  // 16 rows (LDS DMA), and for the narrow groups of more rows 8 waves x 4
+  // tiles (512 rows) with a 2-step ring.  A resident B is used only where the LDS it takes still lets two
   // or more workgroups share a CU.
   int rc = 0;
   if (stages & kStageGateUp) {
@@ -1496,8 +1496,11 @@ int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *exper
     // and 16 rows 0-4 us faster, bit-identical everywhere; up to 16 rows 4
     // waves x 2 tiles (16-row block 183-185 -> 182 us in a 5-shape sweep)
     const bool dma = f % 128 == 0 && f >= 512;
-    if (M == 1 && down_lds_bytes(f, 4, 1, true, 256) <= half) rc = MOE_DN(2, 8, 4, 1, true, 0, 1);
-    else if (M <= 4 && down_lds_bytes(f, 4, 4, true, 128) <= half) rc = MOE_DN(1, 8, 4, 4, true, 0, 1);
+    // resident B, 4 waves x 2 tiles (128 rows of d): 1 row with a 2-step
+    // ring, 2-4 rows with a 4-step ring (measured against 8 waves: 1 row
+    // 69.7 -> 69.05 us, 2 rows 94 -> 90 us; a sweep of 11 shapes)
+    if (M == 1 && down_lds_bytes(f, 2, 1, true, 128) <= half) rc = MOE_DN(2, 4, 2, 1, true, 0, 1);
+    else if (M <= 4 && down_lds_bytes(f, 4, 4, true, 128) <= half) rc = MOE_DN(2, 4, 4, 4, true, 0, 1);
     else if (M <= kGroupCols) rc = dma ? MOE_DND(2, 4, 2, 16, 0, 1, false) : MOE_DN(2, 8, 4, 16, false, 0, 1);
     // more rows (the prefill's narrow groups): scales through the ring where
     // f % 128 == 0 (measured 4.90 -> 4.84 ms at 1,533 rows; at 16 rows the
