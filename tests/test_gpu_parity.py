@@ -373,6 +373,9 @@ WIDE = [
     # f >= 512 in whole steps: every ring-mode down kernel stages B by LDS DMA
     synth.LayerShape("w5", 256, 512, 5, 1, 2, -6, -2, 0.05, "bf16"),
     synth.LayerShape("w6", 384, 640, 6, 1, 2, -6, -2, 0.05, "f32"),
+    # bf16 x with d >= 512: the wide gate/up kernel stages x by LDS DMA
+    # (d = 640: five steps, padded to eight in whole groups of four)
+    synth.LayerShape("w7", 640, 512, 5, 1, 2, -6, -2, 0.05, "bf16"),
 ]
 
 
