@@ -1457,11 +1457,12 @@ int ffn_launch(const void *x, int x_bf16, int64_t M, int k, const uint8_t *exper
   // gate/up 4 waves each with the W_gate and W_up tiles of 16 rows (64 rows
   // of f) and a 4-step ring at 1-2 rows, 4 waves (half W_gate, half W_up) at
   // 5-8 rows, 4 waves each with both tiles again beyond (4-step rings), and
-  // the wide kernel (8 waves x 32 rows) for the 32- and 64-slot groups; down 4 waves x 2 tiles
-  // (128 rows of d) at 1-4 rows, 4 waves x 2 tiles and a 2-step ring up to
-  // 16 rows (LDS DMA), and for the narrow groups of more rows 8 waves x 4
-  // tiles (512 rows) with a 2-step ring.  A resident B is used only where the LDS it takes still lets two
-  // or more workgroups share a CU.
+  // the wide kernel (8 waves x 32 rows) for the 32- and 64-slot groups;
+  // down 4 waves x 2 tiles (128 rows of d) at 1-4 rows, 4 waves x 2 tiles
+  // and a 2-step ring up to 16 rows (LDS DMA), 8 waves x 4 tiles (512 rows)
+  // with a 2-step ring for the narrow groups of more rows, and 8 waves x 2
+  // tiles for the wide groups.  A resident B is used only where the LDS it
+  // takes still lets two or more workgroups share a CU.
   int rc = 0;
   if (stages & kStageGateUp) {
     const int np = x_bf16 ? 1 : 3;
