@@ -237,15 +237,21 @@ __global__ __launch_bounds__(64) void router_mfma_tile_kernel(const void *__rest
   auto issue = [&](int it, int p) {
     const int q = it / nper, r = it - q * nper, c = q + kRqRanges * r;
     const bool ok = it < total && c < nsl;
+    // a dead slice adds kDead to every lane's offset (one uniform value, no
+    // per-lane select, which the compiler turns into branches): both
+    // operands are under 2^30 bytes (checked by the host), so those loads
+    // read zeros
+    const uint32_t wstep = ok ? (uint32_t)c * 128u : kDead;
+    const uint32_t xstep = ok ? (uint32_t)c * (uint32_t)(32 * EL) : kDead;
 #pragma unroll
     for (int tr = 0; tr < TR; ++tr) {
-      const uint32_t o = ok ? wbase[tr] + (uint32_t)c * 128u : kOOB;
+      const uint32_t o = wbase[tr] + wstep;
       wr[p][tr][0] = buf_load16(wres, o);
       wr[p][tr][1] = buf_load16(wres, o + 16);
     }
 #pragma unroll
     for (int tx = 0; tx < TX; ++tx) {
-      const uint32_t o = ok ? xbase[tx] + (uint32_t)c * (uint32_t)(32 * EL) : kOOB;
+      const uint32_t o = xbase[tx] + xstep;
 #pragma unroll
       for (int h = 0; h < EL / 2; ++h) xr[p][tx][h] = buf_load16(xres, o + 16 * h);
     }
@@ -256,7 +262,11 @@ __global__ __launch_bounds__(64) void router_mfma_tile_kernel(const void *__rest
 #pragma unroll
     for (int tx = 0; tx < TX; ++tx) acc[tr][tx] = sum[tr][tx] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int p = 0; p < NR; ++p) issue(p, p);
+  // the slots are issued in order (the loop's load waits count on it)
+  for (int p = 0; p < NR; ++p) {
+    issue(p, p);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   for (int it0 = 0; it0 < total; it0 += NR) {
 #pragma unroll
     for (int p = 0; p < NR; ++p) {
@@ -284,6 +294,7 @@ __global__ __launch_bounds__(64) void router_mfma_tile_kernel(const void *__rest
         for (int tr = 0; tr < TR; ++tr) acc[tr][tx] = rq_chain<NP>(a[tr], b, acc[tr][tx]);
       }
       issue(it + NR, p);
+      __builtin_amdgcn_sched_barrier(0);
       if ((it + 1) % nper == 0) {  // range q = it / nper is complete: add it in range order
         const bool first = it < nper;
 #pragma unroll
@@ -337,18 +348,31 @@ static void launch_topk(const float *logits, int M, int E, int k, int32_t *ids, 
                      M, E, k, ids, w);
 }
 
+template <int XBF16, int TR, int TX>
+static void launch_logits_tiles(const void *x, const float *w_router, float *logits, int M, int d, int E,
+                                hipStream_t stream) {
+  hipLaunchKernelGGL((router_mfma_tile_kernel<XBF16, 4, TR, TX>),
+                     dim3((E + 16 * TR - 1) / (16 * TR), (M + 16 * TX - 1) / (16 * TX)), dim3(64), 0, stream, x,
+                     w_router, M, d, E, logits);
+}
+
 template <int XBF16>
 static void launch_logits_mfma(const void *x, const float *w_router, float *logits, int M, int d, int E,
                                hipStream_t stream) {
-  // tiles per wave by row count (measured at E = 896, d = 7168: 2 x 4 at
-  // 1,533 rows 166 us, 1 x 2 at 270 rows 67 us); the arithmetic of a logit
-  // does not depend on it
-  if (M > 768)
-    hipLaunchKernelGGL((router_mfma_tile_kernel<XBF16, 4, 2, 4>), dim3((E + 31) / 32, (M + 63) / 64), dim3(64), 0,
-                       stream, x, w_router, M, d, E, logits);
-  else
-    hipLaunchKernelGGL((router_mfma_tile_kernel<XBF16, 4, 1, 2>), dim3((E + 15) / 16, (M + 31) / 32), dim3(64), 0,
-                       stream, x, w_router, M, d, E, logits);
+  // router x row tiles per wave by row count, measured at E = 896, d = 7168
+  // (1 x 2, 1 x 4, 2 x 2 and 2 x 4 tiles from 200 to 1,533 rows): bf16 x
+  // 270 rows 60 us, 512 rows 85 us, 768 rows 112 us, 1,533 rows 166 us;
+  // fp32 x 270 rows 107 us, 768 rows 166 us, 1,533 rows 260 us.  The
+  // arithmetic of a logit does not depend on the tiles.
+  if constexpr (XBF16) {
+    if (M <= 288) launch_logits_tiles<XBF16, 1, 2>(x, w_router, logits, M, d, E, stream);
+    else if (M <= 512) launch_logits_tiles<XBF16, 1, 4>(x, w_router, logits, M, d, E, stream);
+    else launch_logits_tiles<XBF16, 2, 4>(x, w_router, logits, M, d, E, stream);
+  } else {
+    if (M <= 384) launch_logits_tiles<XBF16, 1, 2>(x, w_router, logits, M, d, E, stream);
+    else if (M <= 768) launch_logits_tiles<XBF16, 2, 2>(x, w_router, logits, M, d, E, stream);
+    else launch_logits_tiles<XBF16, 2, 4>(x, w_router, logits, M, d, E, stream);
+  }
 }
 
 template <int XBF16, int RW, int MCH, int KC, int XS>
