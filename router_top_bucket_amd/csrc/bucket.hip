@@ -15,6 +15,9 @@
 namespace moe {
 
 constexpr int BK_THREADS = 1024;
+// Dynamic LDS of the general bucket kernel: its masks and counts, plus, when
+// they fit, every slot's expert as an int16 (bucket_kernel, `cached`).
+constexpr int kBkMaxLds = 152 * 1024;
 // Dynamic LDS the fused top-k + bucket kernel may take: gfx950 gives a
 // workgroup 160 KB in all, and the kernel holds about 4 KB of static LDS.
 constexpr int kTbMaxLds = 152 * 1024;
@@ -27,15 +30,19 @@ __device__ __forceinline__ int slot_expert(const int32_t *ids, int t, int k, int
   return (e >= 0 && e < E) ? e : -1;
 }
 
+// cached: the counting pass also keeps each slot's expert in LDS (-1 for an
+// id outside [0, E)), so the placement rounds read no global memory; the
+// results are the same integers either way.
 __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(const int32_t *__restrict__ ids, int M, int k, int E,
                                                             int S, int32_t *__restrict__ offsets,
                                                             int32_t *__restrict__ perm, int32_t *__restrict__ active,
                                                             int32_t *__restrict__ n_active,
-                                                            int32_t *__restrict__ dev_error) {
+                                                            int32_t *__restrict__ dev_error, int cached) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int NE = E + S;
   unsigned long long *mask = (unsigned long long *)smem;  // [NE]
   int32_t *base = (int32_t *)(mask + NE);                 // [NE] counts, then running bases
+  int16_t *eid = (int16_t *)(base + NE);                  // [T] when cached
   __shared__ int32_t wave_sum[16][2];
   __shared__ int32_t err;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -48,6 +55,7 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(const int32_t *__res
   // ---- counts
   for (int t = tid; t < T; t += BK_THREADS) {
     const int e = slot_expert(ids, t, k, kps, E);
+    if (cached) eid[t] = (int16_t)e;
     if (e < 0 || e >= NE) err = 1;
     else atomicAdd(&base[e], 1);
   }
@@ -81,6 +89,7 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(const int32_t *__res
       offsets[e] = c_ex;
       if (c > 0) active[a_ex++] = e;
       base[e] = c_ex;
+      mask[e] = 0ull;
       c_ex += c;
     }
   }
@@ -89,15 +98,14 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(const int32_t *__res
     *n_active = a_tot;
   }
   __syncthreads();
-  // ---- stable placement, 64 rows at a time
+  // ---- stable placement, 64 rows at a time (the masks start at zero and
+  // each round clears them as it adds them to the bases)
   for (int m0 = 0; m0 < M; m0 += 64) {
-    for (int e = tid; e < NE; e += BK_THREADS) mask[e] = 0ull;
-    __syncthreads();
     const int mrows = (M - m0) < 64 ? (M - m0) : 64;
     const int tc = mrows * kps;
     for (int i = tid; i < tc; i += BK_THREADS) {
       const int t = m0 * kps + i;
-      const int e = slot_expert(ids, t, k, kps, E);
+      const int e = cached ? (int)eid[t] : slot_expert(ids, t, k, kps, E);
       if (e >= 0 && e < NE) {
         const unsigned long long bit = 1ull << (t / kps - m0);
         const unsigned long long old = atomicOr(&mask[e], bit);
@@ -107,7 +115,7 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(const int32_t *__res
     __syncthreads();
     for (int i = tid; i < tc; i += BK_THREADS) {
       const int t = m0 * kps + i;
-      const int e = slot_expert(ids, t, k, kps, E);
+      const int e = cached ? (int)eid[t] : slot_expert(ids, t, k, kps, E);
       if (e >= 0 && e < NE) {
         const unsigned long long bit = 1ull << (t / kps - m0);
         const int rank = base[e] + __popcll(mask[e] & (bit - 1ull));
@@ -115,7 +123,10 @@ __global__ __launch_bounds__(BK_THREADS) void bucket_kernel(const int32_t *__res
       }
     }
     __syncthreads();
-    for (int e = tid; e < NE; e += BK_THREADS) base[e] += __popcll(mask[e]);
+    for (int e = tid; e < NE; e += BK_THREADS) {
+      base[e] += __popcll(mask[e]);
+      mask[e] = 0ull;
+    }
     __syncthreads();
   }
   if (tid == 0) *dev_error = err;
@@ -285,9 +296,17 @@ int bucket_launch(const int32_t *ids, int M, int k, int E, int S, int32_t *offse
   if ((int64_t)M * (k + S) <= BK_THREADS && M <= 64)
     hipLaunchKernelGGL(bucket_small_kernel, dim3(1), dim3(BK_THREADS), smem, stream, ids, M, k, E, S, offsets, perm,
                        active, n_active, dev_error);
-  else
-    hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(BK_THREADS), smem, stream, ids, M, k, E, S, offsets, perm, active,
-                       n_active, dev_error);
+  else {
+    // the slots' experts as int16 in LDS where they fit (NE <= 4096 fits int16)
+    static const bool big_lds = hipFuncSetAttribute(reinterpret_cast<const void *>(&bucket_kernel),
+                                                    hipFuncAttributeMaxDynamicSharedMemorySize, kBkMaxLds) == hipSuccess;
+    if (!big_lds) (void)hipGetLastError();  // leave no error behind for the launch check
+    const size_t lim = big_lds ? (size_t)kBkMaxLds : (size_t)64 * 1024;
+    const size_t with_ids = smem + (size_t)M * (k + S) * sizeof(int16_t);
+    const int cached = with_ids <= lim ? 1 : 0;
+    hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(BK_THREADS), cached ? with_ids : smem, stream, ids, M, k, E, S,
+                       offsets, perm, active, n_active, dev_error, cached);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
