@@ -244,9 +244,11 @@ def _run_bucket(ids_np, E, S):
     return _host(offsets), _host(perm)[:T], _host(active), int(_host(na)[0]), int(_host(err)[0])
 
 
+# 4000 and 4100 rows at E + S = 898 sit on either side of the general
+# kernel's LDS limit for keeping every slot's expert on chip (152 KB)
 @pytest.mark.parametrize("M,E,k,S", [(1, 896, 16, 2), (3, 16, 2, 0), (16, 896, 16, 2), (64, 896, 16, 2),
                                      (65, 896, 16, 2), (270, 896, 16, 2), (1533, 896, 16, 2), (5, 4, 4, 1),
-                                     (200, 4000, 16, 96)])
+                                     (200, 4000, 16, 96), (4000, 896, 16, 2), (4100, 896, 16, 2)])
 def test_bucket_exact(M, E, k, S):
     g = synth.rng(3, M, E)
     ids = np.stack([g.permutation(E)[:k] for _ in range(M)]).astype(np.int32)
@@ -274,6 +276,31 @@ def test_bucket_flags_bad_ids_in_bounds():
     valid = np.array([[0, 5], [3, 1], [6, 2], [7, 8]], dtype=np.int32)
     off, perm, act, na, err = _run_bucket(valid, 16, 1)
     assert err == 0  # the flag is cleared by a clean call
+
+
+@pytest.mark.parametrize("M", [100, 26000])
+def test_bucket_general_kernel_flags_bad_ids(M):
+    """The general bucket kernel (more than 64 rows), with the slots' experts
+    kept in LDS (100 rows) and read from global memory (26,000 rows: 78,000
+    slots are past the LDS limit): an out-of-range id, a negative id and a
+    repeated id set the flag, and every write stays in bounds."""
+    E, k, S = 16, 2, 1
+    g = synth.rng(5, M, E)
+    ids = np.stack([g.permutation(E)[:k] for _ in range(M)]).astype(np.int32)
+    ids[M // 3, 0] = E + 3
+    ids[M // 2, 1] = -1
+    ids[M - 1, 1] = ids[M - 1, 0]
+    T = M * (k + S)
+    off, perm, act, na, err = _run_bucket(ids, E, S)
+    assert err == 1
+    assert 0 <= off[-1] <= T
+    written = perm[perm != -7]
+    assert ((written >= 0) & (written < T)).all()
+    ok = np.stack([g.permutation(E)[:k] for _ in range(M)]).astype(np.int32)
+    off, perm, act, na, err = _run_bucket(ok, E, S)
+    r_off, r_perm, r_act, r_na = oracle.bucket(ok, E, S)
+    assert err == 0 and np.array_equal(off, r_off) and np.array_equal(perm, r_perm)
+    assert na == r_na and np.array_equal(act[:na], r_act)
 
 
 ROUTE_SHAPES = [
