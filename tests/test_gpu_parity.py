@@ -215,6 +215,15 @@ def test_router_logits_rows_equal_single_rows(shape):
     for M in (17, 40, 64, 65):
         got = logits(xd[:M])
         assert np.array_equal(got.view(np.uint32), big[:M].view(np.uint32)), (shape.name, M)
+    # larger calls take other tile shapes (1 x 4, 2 x 2 and 2 x 4 router x x
+    # tiles per wave, by row count and x type): the same rows, the same bits
+    x8 = synth.rows_x(shape, 63, 800)
+    xd8 = _x_dev(shape, x8)
+    first = logits(xd8[:150])
+    for M in (300, 500, 800):
+        got = logits(xd8[:M])
+        assert np.array_equal(got[:150].view(np.uint32), first.view(np.uint32)), (shape.name, M)
+        assert_close(got[M - 40:], oracle.router_logits(x8[M - 40:M], wr), f"{shape.name} {M}-row logits, last rows")
 
 
 def test_route_zipf_prefill_logits_exact():
