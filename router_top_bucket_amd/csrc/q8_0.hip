@@ -89,6 +89,12 @@ __device__ __forceinline__ float q8_f16_hi(uint32_t v) { return (float)__builtin
 // LDS of one wave: the X fragments of one step (2 blocks x 4 lane groups x
 // 16*NMF columns x 16 B, then a 16-byte dummy slot for masked writes); after
 // the main loop the same bytes hold the wave's partial sums [RT][NMF][4][65].
+// Column c of fragment row b = 4 jb + g sits in 16-byte slot c ^ q8_swz(b)
+// of its 16-column group: the X split writes one column of all eight rows
+// per eight lanes, and rows 256 bytes apart would put those writes on the
+// same banks; a fragment read (16 consecutive columns of one row) stays a
+// permutation of 16 slots.
+__device__ __forceinline__ constexpr int q8_swz(int b) { return (b & 1) | ((b >> 1) << 2); }
 template <int RT, int NMF>
 struct Q8Lds {
   static constexpr int kCols = 16 * NMF;
@@ -145,10 +151,15 @@ __global__ __launch_bounds__(Q8_MAX_WAVES * 64) __attribute__((amdgpu_waves_per_
     // where this lane's split goes: block j, lane group g, column 3 xm + p
     const int xj = xk >> 5, xg8 = (xk & 31) >> 3, xe = xk & 7;
     const int xg = ((xg8 & 1) << 1) | (xg8 >> 1);
-    const uint32_t xdst = xm < M ? (uint32_t)(((xj * 4 + xg) * L::kCols + 2 * xm) * 16 + 2 * xe) : (uint32_t)L::kFrag;
-    const uint32_t xpstep = xm < M ? 16u : 0u;  // next part's column (dummy stays put)
-    // fragment reads: lane (r, q) reads column 16 mf + r of lane group q
-    const uint32_t frd = (uint32_t)((q * L::kCols + r) * 16);
+    // (x_0 in column 2 xm, x_1 in column 2 xm + 1; both < 16)
+    const int xb = xj * 4 + xg;
+    const uint32_t xdst = xm < M ? (uint32_t)((xb * L::kCols + ((2 * xm) ^ q8_swz(xb))) * 16 + 2 * xe) : (uint32_t)L::kFrag;
+    const uint32_t xdst_lo =
+        xm < M ? (uint32_t)((xb * L::kCols + ((2 * xm + 1) ^ q8_swz(xb))) * 16 + 2 * xe) : (uint32_t)L::kFrag;
+    // fragment reads: lane (r, q) reads column 16 mf + r of row 4 jb + q
+    uint32_t frd[2];
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) frd[jb] = (uint32_t)(((4 * jb + q) * L::kCols + (r ^ q8_swz(4 * jb + q))) * 16);
     // scale bpermute source addresses: output row 4q + i lives in lane 4q + i
     int baddr[4];
 #pragma unroll
@@ -245,12 +256,11 @@ __global__ __launch_bounds__(Q8_MAX_WAVES * 64) __attribute__((amdgpu_waves_per_
         const int slot = u % PF;
         // 1. split this step's X into the fragment area
         {
-          uint32_t d = xdst;
           if constexpr (EPL == 1) {
             uint32_t hp, lp;
             q8_split2(__uint_as_float(xr[slot][0]), hp, lp);
-            *(uint16_t *)(wl + d) = (uint16_t)(hp >> 16);
-            *(uint16_t *)(wl + d + xpstep) = (uint16_t)(lp >> 16);
+            *(uint16_t *)(wl + xdst) = (uint16_t)(hp >> 16);
+            *(uint16_t *)(wl + xdst_lo) = (uint16_t)(lp >> 16);
           } else {
             constexpr int NP = EPL / 2;  // packed pairs
             uint32_t hp[NP], lp[NP];
@@ -260,13 +270,13 @@ __global__ __launch_bounds__(Q8_MAX_WAVES * 64) __attribute__((amdgpu_waves_per_
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
               const uint32_t *src = p == 0 ? hp : lp;
+              const uint32_t d = p == 0 ? xdst : xdst_lo;
               if constexpr (EPL == 8)
                 *(u32x4 *)(wl + d) = u32x4{src[0], src[1], src[2], src[3]};
               else if constexpr (EPL == 4)
                 *(u32x2 *)(wl + d) = u32x2{src[0], src[1]};
               else
                 *(uint32_t *)(wl + d) = src[0];
-              d += xpstep;
             }
           }
         }
@@ -295,7 +305,7 @@ __global__ __launch_bounds__(Q8_MAX_WAVES * 64) __attribute__((amdgpu_waves_per_
           bf16x8 bfr[NMF];
 #pragma unroll
           for (int mf = 0; mf < NMF; ++mf)
-            bfr[mf] = bits_to_bf16x8(*(const u32x4 *)(wl + frd + (uint32_t)((jb * 4 * L::kCols + 16 * mf) * 16)));
+            bfr[mf] = bits_to_bf16x8(*(const u32x4 *)(wl + frd[jb] + (uint32_t)(16 * mf * 16)));
 #pragma unroll
           for (int t = 0; t < RT; ++t)
 #pragma unroll
